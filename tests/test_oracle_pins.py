@@ -1,0 +1,346 @@
+"""Pins for the CPU oracle: closed forms, invariants, brute force and a
+hand-worked example, chosen so that a plausible slip in the oracle (a dropped
+term, a wrong sign, a wrong index, a transposed operand, the wrong scale)
+fails at least one of them.  Nothing here compares the oracle with itself.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _haar(rng, D):
+    q, r = np.linalg.qr(rng.standard_normal((D, D)))
+    return q * np.where(np.diag(r) < 0, -1.0, 1.0)[None, :]
+
+
+def _rand_case(seed, S=40, D=8, d=3):
+    rng = np.random.default_rng(seed)
+    P = _haar(rng, D)
+    K = rng.standard_normal((S, D))
+    V = rng.standard_normal((S, D))
+    q = rng.standard_normal(D)
+    slab, rest, vv = oracle.append(K, V, P, d, "f64")
+    return q, P, K, V, slab, rest, vv
+
+
+# ------------------------------------------------------ hand-worked example --
+
+def _golden():
+    with open(os.path.join(GOLDEN, "worked_example_d4.json")) as fh:
+        return json.load(fh)
+
+
+def test_worked_example_rotation_and_scores():
+    f = _golden()
+    P = np.array(f["P_rows"], float)
+    q = np.array(f["q"], float)
+    slab = np.array(f["slab"], float)
+    assert np.array_equal(oracle.rotate(q, P), np.array(f["expected"]["q_rot"], float))
+    assert np.array_equal(oracle.low_rank_scores(q, P, slab), np.array(f["expected"]["scores"], float))
+
+
+@pytest.mark.parametrize("kname,k", [("k1", 1), ("k2", 2), ("k3", 3)])
+def test_worked_example_decode(kname, k):
+    f = _golden()
+    P = np.array(f["P_rows"], float)
+    q = np.array(f["q"], float)
+    slab, rest, V = (np.array(f[n], float) for n in ("slab", "rest", "V"))
+    out, idx, _ = oracle.decode_head(q, P, slab, rest, V, k)
+    exp = f["expected"][kname]
+    assert idx.tolist() == exp["idx"]
+    if kname == "k1":
+        assert np.array_equal(out, np.array(exp["out"], float))
+        return
+    z = np.array([math.exp(x) for x in exp["scaled_exact"]])
+    w = z / z.sum()
+    want = np.zeros(4)
+    for wi, j in zip(w, exp["idx"]):
+        want += wi * np.array(f["V"][j], float)
+    assert np.allclose(out, want, rtol=0, atol=1e-15)
+
+
+def test_worked_example_dense():
+    f = _golden()
+    P = np.array(f["P_rows"], float)
+    q = np.array(f["q"], float)
+    K = np.concatenate([np.array(f["slab"], float), np.array(f["rest"], float)], axis=1)
+    V = np.array(f["V"], float)
+    out = oracle.dense_attention(oracle.rotate(q, P), K, V)
+    z = np.array([math.exp(x) for x in f["expected"]["dense_scaled"]])
+    assert np.allclose(out, (z / z.sum()) @ V, rtol=0, atol=1e-12)
+
+
+# ------------------------------------------------------------------ scores --
+
+def test_full_rank_scores_invariant_under_orthogonal_P():
+    # with d = D the ranking score is q'.k' = q P P^T k^T = q.k
+    q, P, K, V, slab, rest, vv = _rand_case(1, d=8)
+    assert np.allclose(oracle.low_rank_scores(q, P, slab), K @ q, rtol=0, atol=1e-12)
+
+
+def test_identity_basis_scores_are_leading_dims():
+    rng = np.random.default_rng(2)
+    K = rng.standard_normal((30, 6))
+    q = rng.standard_normal(6)
+    slab, rest, _ = oracle.append(K, K, np.eye(6), 2, "f64")
+    assert np.array_equal(slab, K[:, :2]) and np.array_equal(rest, K[:, 2:])
+    want = [q[0] * K[j, 0] + q[1] * K[j, 1] for j in range(30)]
+    assert np.allclose(oracle.low_rank_scores(q, np.eye(6), slab), want, rtol=0, atol=1e-14)
+
+
+def test_scores_pure_python_brute_force():
+    # explicit double loops, transposition-sensitive (P not symmetric)
+    q, P, K, V, slab, rest, vv = _rand_case(3, S=12, D=5, d=2)
+    s = oracle.low_rank_scores(q, P, slab)
+    for j in range(12):
+        kj = [sum(K[j][m] * P[m][i] for m in range(5)) for i in range(5)]
+        qp = [sum(q[m] * P[m][i] for m in range(5)) for i in range(5)]
+        assert abs(s[j] - (qp[0] * kj[0] + qp[1] * kj[1])) < 1e-12
+
+
+# --------------------------------------------------------------- selection --
+
+def _rank_count_topk(s, k):
+    """Independent formulation: j is kept iff fewer than k tokens beat it,
+    where l beats j when s_l > s_j, or s_l == s_j and l < j."""
+    S = len(s)
+    keep = []
+    for j in range(S):
+        beats = sum(1 for l in range(S) if s[l] > s[j] or (s[l] == s[j] and l < j))
+        if beats < k:
+            keep.append(j)
+    return keep
+
+
+@pytest.mark.parametrize("kind", ["normal", "dup", "zeros", "sorted"])
+@pytest.mark.parametrize("n,k", [(1, 1), (7, 3), (64, 16), (100, 99), (130, 1), (130, 130), (50, 70)])
+def test_topk_matches_rank_counting(kind, n, k):
+    s = synth.score_vector(n * 31 + k, n, kind).astype(np.float64)
+    assert oracle.select_topk(s, k).tolist() == _rank_count_topk(s, min(k, n))
+
+
+def test_topk_brute_force_full_sort_tiny():
+    s = synth.score_vector(5, 256, "normal").astype(np.float64)
+    srt = sorted(range(256), key=lambda j: (-s[j], j))
+    assert oracle.select_topk(s, 64).tolist() == sorted(srt[:64])
+
+
+def test_topk_special_cases():
+    s = synth.score_vector(6, 50, "normal").astype(np.float64)
+    assert oracle.select_topk(s, 50).tolist() == list(range(50))
+    assert oracle.select_topk(s, 1).tolist() == [int(np.argmax(s))]
+    assert oracle.select_topk(np.zeros(20), 7).tolist() == list(range(7))
+    # -0.0 and +0.0 are equal: lower index wins
+    assert oracle.select_topk(np.array([-0.0, 0.0, -1.0, 0.0]), 2).tolist() == [0, 1]
+    # signed ranking, not by magnitude
+    assert oracle.select_topk(np.array([-5.0, 1.0, 0.5]), 1).tolist() == [1]
+
+
+def test_gap_and_band_rule():
+    s = np.array([5.0, 4.0, 3.0, 2.0])
+    assert oracle.topk_gap(s, 2) == pytest.approx(0.25)
+    s2 = np.array([5.0, 3.0, 3.0 * (1 - 1e-6), 1.0])
+    assert oracle.topk_gap(s2, 2) < 1e-4
+    assert oracle.valid_in_band(s2, 2, np.array([0, 1]))
+    assert oracle.valid_in_band(s2, 2, np.array([0, 2]))
+    assert not oracle.valid_in_band(s2, 2, np.array([1, 2]))
+    assert not oracle.valid_in_band(s2, 2, np.array([2, 0]))
+
+
+# --------------------------------------------------------------- attention --
+
+def test_full_budget_equals_dense_attention_on_original_keys():
+    # d = D, k = S: Loki is dense attention (orthogonal invariance)
+    q, P, K, V, slab, rest, vv = _rand_case(7, S=33, D=8, d=8)
+    out, idx, _ = oracle.decode_head(q, P, slab, rest, vv, 33)
+    assert idx.tolist() == list(range(33))
+    assert np.allclose(out, oracle.dense_attention(q, K, V), rtol=0, atol=1e-12)
+
+
+def test_all_tokens_kept_with_small_d_is_still_dense():
+    # k = S with d < D: the exact scores must use all D dims and 1/sqrt(D)
+    q, P, K, V, slab, rest, vv = _rand_case(8, S=25, D=8, d=2)
+    out, _, _ = oracle.decode_head(q, P, slab, rest, vv, 25)
+    e = K @ q / math.sqrt(8)
+    w = np.exp(e - e.max())
+    assert np.allclose(out, (w / w.sum()) @ V, rtol=0, atol=1e-12)
+
+
+def test_weights_sum_to_one_and_k1_returns_argmax_row():
+    q, P, K, V, slab, rest, vv = _rand_case(9, S=40, D=8, d=3)
+    idx = oracle.select_topk(oracle.low_rank_scores(q, P, slab), 10)
+    _, w = oracle.attend(q, P, slab, rest, vv, idx)
+    assert abs(w.sum() - 1.0) < 1e-15 and np.all(w > 0)
+    out, idx1, s = oracle.decode_head(q, P, slab, rest, vv, 1)
+    assert idx1.tolist() == [int(np.argmax(s))]
+    assert np.array_equal(out, V[idx1[0]])
+
+
+def test_constant_values_and_linearity_in_v():
+    q, P, K, V, slab, rest, vv = _rand_case(10, S=30, D=8, d=3)
+    c = np.arange(8, dtype=float) - 3.0
+    out, _, _ = oracle.decode_head(q, P, slab, rest, np.tile(c, (30, 1)), 9)
+    assert np.allclose(out, c, rtol=0, atol=1e-13)
+    o1, _, _ = oracle.decode_head(q, P, slab, rest, vv, 9)
+    o2, _, _ = oracle.decode_head(q, P, slab, rest, -2.5 * vv, 9)
+    assert np.allclose(o2, -2.5 * o1, rtol=0, atol=1e-13)
+
+
+def test_softmax_over_selected_tokens_only():
+    # two selected tokens whose exact scores differ by ln 3 after scaling;
+    # an unselected token with a huge exact score must get no weight
+    D = 4
+    P = np.eye(D)
+    q = np.array([1.0, 0.0, 1.0, 0.0])
+    a = 2.0 * math.log(3.0)  # scaled by 1/sqrt(4) -> ln 3
+    slab = np.array([[5.0, 0.0], [4.0, 0.0], [-9.0, 0.0]])
+    rest = np.array([[a, 0.0], [0.0, 0.0], [1000.0, 0.0]])
+    V = np.array([[1.0, 0, 0, 0], [0, 1.0, 0, 0], [0, 0, 1.0, 0]])
+    out, idx, _ = oracle.decode_head(q, P, slab, rest, V, 2)
+    assert idx.tolist() == [0, 1]
+    # e0 - e1 = (5 + a - 4) / 2 = 0.5 + ln 3 -> w0/w1 = 3 e^0.5
+    r = 3.0 * math.exp(0.5)
+    assert np.allclose(out, [r / (1 + r), 1 / (1 + r), 0, 0], rtol=0, atol=1e-15)
+
+
+def test_permutation_equivariance():
+    q, P, K, V, slab, rest, vv = _rand_case(11, S=50, D=8, d=3)
+    out, idx, s = oracle.decode_head(q, P, slab, rest, vv, 12)
+    perm = np.random.default_rng(0).permutation(50)
+    out2, idx2, _ = oracle.decode_head(q, P, slab[perm], rest[perm], vv[perm], 12)
+    inv = np.argsort(perm)
+    assert sorted(perm[idx2].tolist()) == idx.tolist()
+    assert np.allclose(out2, out, rtol=0, atol=1e-13)
+    assert inv.shape == (50,)
+
+
+def test_gqa_head_mapping_consecutive_groups():
+    rng = np.random.default_rng(12)
+    B, Hq, Hkv, S, D, d = 2, 6, 2, 20, 8, 3
+    P = np.stack([_haar(rng, D) for _ in range(Hkv)])
+    q = rng.standard_normal((B, Hq, D))
+    Kraw = rng.standard_normal((B, Hkv, S, D))
+    V = rng.standard_normal((B, Hkv, S, D))
+    slab = np.empty((B, Hkv, S, d)); rest = np.empty((B, Hkv, S, D - d))
+    for g in range(Hkv):
+        slab[:, g], rest[:, g], _ = oracle.append(Kraw[:, g], V[:, g], P[g], d, "f64")
+    out, idx, _ = oracle.decode(q, slab, rest, V, P, 5, "f64")
+    for b in range(B):
+        for h in range(Hq):
+            g = h // 3  # heads 0,1,2 -> KV 0; 3,4,5 -> KV 1
+            o, i, _ = oracle.decode_head(q[b, h], P[g], slab[b, g], rest[b, g], V[b, g], 5)
+            assert np.array_equal(i, idx[b, h]) and np.array_equal(o, out[b, h])
+    assert oracle.kv_head(2, 6, 2) == 0 and oracle.kv_head(3, 6, 2) == 1
+
+
+def test_decode_reads_only_first_S_positions():
+    q, P, K, V, slab, rest, vv = _rand_case(13, S=30, D=8, d=3)
+    big = lambda a: np.concatenate([a, 1e6 * np.ones((5, a.shape[1]))])[None, None]
+    out, idx, _ = oracle.decode(q[None, None], big(slab), big(rest), big(vv), P[None], 7, "f64", S=30)
+    o, i, _ = oracle.decode_head(q, P, slab, rest, vv, 7)
+    assert np.array_equal(out[0, 0], o) and np.array_equal(idx[0, 0], i)
+
+
+# ------------------------------------------------------------- calibration --
+
+def test_calibration_orthogonal_descending_and_spectrum():
+    w = synth.WORKLOADS["l2_7b"]
+    Q = synth.head_basis(w, 0)
+    keys = synth.calib_keys(w, 0, Q)
+    P, ev = oracle.calibrate(keys)
+    assert np.allclose(P.T @ P, np.eye(w.D), rtol=0, atol=1e-12)
+    assert np.all(np.diff(ev) <= 0)
+    sig2 = synth.spectrum(w) ** 2
+    # sample eigenvalues within 6 standard errors sigma^2 sqrt(2/n) of truth
+    # for the well-separated leading ones
+    lead = 8
+    assert np.all(np.abs(ev[:lead] - sig2[:lead]) < 6 * sig2[:lead] * math.sqrt(2 / w.calib_n))
+    # the leading-d columns capture (nearly) the true top-d key variance:
+    # sum_c P_c^T C P_c for C = Q diag(sigma^2) Q^T against sum_{i<d} sigma_i^2
+    d = w.d
+    C = (Q * sig2[None, :]) @ Q.T
+    captured = np.trace(P[:, :d].T @ C @ P[:, :d])
+    assert 0.999 < captured / sig2[:d].sum() <= 1.0 + 1e-12
+
+
+def test_calibration_exact_low_rank_subspace_and_signs():
+    rng = np.random.default_rng(14)
+    D, r, n = 10, 3, 500
+    Q = _haar(rng, D)
+    z = rng.standard_normal((n, r)) * np.array([3.0, 2.0, 1.0])
+    X = z @ Q[:, :r].T + np.arange(D) * 0.1  # mean offset must not matter
+    P, ev = oracle.calibrate(X)
+    assert np.allclose(P[:, :r] @ P[:, :r].T, Q[:, :r] @ Q[:, :r].T, atol=1e-10)
+    assert np.all(np.abs(ev[r:]) < 1e-10)
+    for c in range(D):
+        i = int(np.argmax(np.abs(P[:, c])))
+        assert P[i, c] > 0
+
+
+def test_calibration_known_covariance_closed_form():
+    # keys +-a e1, +-b e2 exactly (zero mean): covariance diag(a^2, b^2, 0) * n/(n-1)
+    a, b = 3.0, 2.0
+    X = np.array([[a, 0, 0], [-a, 0, 0], [0, b, 0], [0, -b, 0]])
+    P, ev = oracle.calibrate(X)
+    assert np.allclose(ev, [2 * a * a / 3, 2 * b * b / 3, 0.0], atol=1e-12)
+    assert np.allclose(np.abs(P), np.eye(3), atol=1e-12)
+    assert np.allclose(P, np.eye(3), atol=1e-12)  # sign convention
+
+
+# ------------------------------------------------------------------ append --
+
+def test_append_rotation_is_invertible_and_split():
+    rng = np.random.default_rng(15)
+    P = _haar(rng, 8)
+    K = rng.standard_normal((5, 8))
+    slab, rest, v = oracle.append(K, -K, P, 3, "f64")
+    assert np.allclose(np.concatenate([slab, rest], axis=1) @ P.T, K, atol=1e-13)
+    assert np.array_equal(v, -K)
+
+
+def test_bf16_rounding_exhaustive_roundtrip():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    vals = oracle.bf16_to_f64(bits)
+    fin = np.isfinite(vals)
+    back = oracle.f64_to_bf16(vals[fin])
+    same = back == bits[fin]
+    # -0.0 maps to itself, every finite pattern round-trips
+    assert same.all()
+
+
+def test_bf16_rounding_ties_and_halfway():
+    one = 1.0
+    ulp = 2.0 ** -7
+    x = np.array([one + ulp / 2, one + 3 * ulp / 2, one + ulp / 2 + 2.0 ** -40,
+                  -(one + ulp / 2), 2.0 ** -130, 3.0 * 2.0 ** -134, 2.0 ** 200])
+    got = oracle.bf16_to_f64(oracle.f64_to_bf16(x))
+    want = [1.0, 1.0 + 2 * ulp, 1.0 + ulp, -1.0, 2.0 ** -130, 4.0 * 2.0 ** -134, np.inf]
+    assert got.tolist() == want
+
+
+def test_bf16_rounding_matches_torch_for_float32_values():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(16)
+    x = (rng.standard_normal(200000) * np.exp(rng.uniform(-20, 20, 200000))).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(oracle.f64_to_bf16(x.astype(np.float64)), ref)
+
+
+def test_append_bf16_within_half_ulp():
+    rng = np.random.default_rng(17)
+    P = _haar(rng, 16)
+    K = rng.standard_normal((64, 16))
+    slab, rest, _ = oracle.append(K, K, P, 4, "bf16")
+    exact = K @ P
+    got = np.concatenate([oracle.bf16_to_f64(slab), oracle.bf16_to_f64(rest)], axis=1)
+    _, e = np.frexp(exact)
+    assert np.all(np.abs(got - exact) <= np.ldexp(1.0, e - 9) * (1 + 1e-12))
