@@ -1,0 +1,321 @@
+"""Benchmark of Loki decode attention on one MI355X.
+
+Workload: the Llama2-13B-shaped run (B=16, 40 query = 40 KV heads, D=128,
+bf16 cache, k_f = d_f = 0.25 -> d = 32) in steady state at S = 3584 cached
+tokens (prompt 3072 + 512 generated, the longest cache of the run).  One
+step = append the step's new key/value of every sequence at position S-1
+(rotate into the PCA basis, split, store) + one Loki decode over all S
+tokens (k = 896).  Several copies of the cache ("layers") are cycled so that
+a step never finds the previous step's bytes in the 256 MB last-level cache.
+
+Prints one JSON line: head-queries/s of the whole step, per-kernel HBM
+roofline of the decode kernel (HIP events on the launch stream), the
+same-GPU dense baseline, the pages' 3072 + 512 generation run (decode time
+summed with append excluded, as the pages time it) and the CPU oracle on a
+bounded sample.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "Loki decode attention: head-queries/s + achieved HBM GB/s (13B shape, S=3584)"
+PEAK_HBM_GBS = 8000.0
+KERNEL_SOURCES = ["device.hpp", "select.hpp", "attend.hpp", "decode_kernels.hip"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "sparse_attention_decode_loki_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(w, S, k) -> dict:
+    """Bytes Loki must move per decode: the d-wide key slab of every cached
+    token once per KV head, plus k full key rows and k value rows per query
+    head."""
+    e = w.esize
+    slab = w.B * w.Hkv * S * w.d * e
+    rows = w.B * w.Hq * k * 2 * w.D * e
+    dense = w.B * w.Hkv * S * 2 * w.D * e
+    return {"slab": slab, "rows": rows, "total": slab + rows, "dense": dense}
+
+
+def measured_traffic(kernel_hash: str, workload: str):
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current kernel source; else None."""
+    p = os.path.join(ROOT, "profiles", f"traffic_fused_decode_{workload}.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as fh:
+        t = json.load(fh)
+    if t.get("kernel_source_hash") != kernel_hash:
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="l2_13b_run")
+    ap.add_argument("--layers", type=int, default=4)
+    ap.add_argument("--path", type=int, default=0, help="0 auto, 1 fused, 2 split")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-run", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this implementation runs on a single GPU; --gpus {args.gpus} is not "
+              "supported (the decode shards by sequence or head with no communication, but only "
+              "the one-GPU slice is built).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import sparse_attention_decode_loki_amd as loki
+    import synth
+
+    loki.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = synth.WORKLOADS[args.config]
+    S = w.S
+    k = w.k
+    t_setup = time.time()
+
+    def log(msg):
+        print(f"[bench {time.time() - t_setup:6.1f}s] {msg}", file=sys.stderr, flush=True)
+
+    # ---- basis (library calibration, host) and prefill through the GPU append
+    Qs = synth.bases(w)
+    P = np.stack([loki.calibrate(synth.calib_keys(w, g, Qs[g]).astype(np.float32))[0]
+                  for g in range(w.Hkv)])
+    Pd = torch.from_numpy(P).to(dev)
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+
+    def up(a):
+        if w.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    prefill = w.prefill if w.prefill else S - 1
+    K_raw, V_raw = synth.raw_cache(w, S - 1)
+    log(f"generated raw cache {K_raw.shape}")
+    base = loki.KVCache(w.B, w.Hkv, S, w.D, w.d, tdt, dev)
+    loki.append(base, up(K_raw), up(V_raw), Pd, pos=0)
+    R = 8
+    new_k, new_v, qs = [], [], []
+    for r in range(R):
+        kn, vn = synth.new_tokens(w, r, Qs)
+        new_k.append(up(kn))
+        new_v.append(up(vn))
+        qs.append(up(synth.queries(w, step=r)))
+    loki.append(base, new_k[0], new_v[0], Pd, pos=S - 1)
+    caches = [base]
+    for _ in range(args.layers - 1):
+        c = loki.KVCache(w.B, w.Hkv, S, w.D, w.d, tdt, dev)
+        c.k_slab.copy_(base.k_slab)
+        if c.k_rest is not None:
+            c.k_rest.copy_(base.k_rest)
+        c.v.copy_(base.v)
+        c.length = S
+        caches.append(c)
+    torch.cuda.synchronize()
+    cache_bytes = sum(t.numel() * t.element_size() for t in (base.k_slab, base.k_rest, base.v)
+                      if t is not None)
+    log(f"caches ready: {args.layers} x {cache_bytes / 1e9:.2f} GB")
+
+    out = torch.empty((w.B, w.Hq, w.D), dtype=torch.float32, device=dev)
+    idx = torch.empty((w.B, w.Hq, k), dtype=torch.int32, device=dev)
+    ws = loki.alloc_workspace(w.B, w.Hq, w.D, S, k, dev)
+
+    def step(i, ev=None):
+        c = caches[i % len(caches)]
+        loki.append(c, new_k[i % R], new_v[i % R], Pd, pos=S - 1)
+        if ev is not None:
+            ev[0].record()
+        loki.decode(qs[i % R], c, Pd, k, S=S, out=out, idx=idx, workspace=ws, path=args.path)
+        if ev is not None:
+            ev[1].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    dec_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    dec_avg_ms = float(dec_ms.mean())
+    log(f"timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step, decode {dec_avg_ms * 1e3:.1f} us")
+
+    hq = w.B * w.Hq
+    by = algorithmic_bytes(w, S, k)
+    achieved = by["total"] / (dec_avg_ms * 1e-3) / 1e9
+    khash = kernel_source_hash()
+    path_name = {1: "fused", 2: "split"}[loki.decode_path(w.B, w.Hq, w.Hkv, w.D, w.d, S, k, args.path)]
+    traffic = measured_traffic(khash, args.config) if "fused" in path_name else None
+
+    result = {
+        "metric": METRIC,
+        "value": hq / (ms_per_step * 1e-3),
+        "unit": "head-queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic: seeded keys with a decaying PCA spectrum, N(0,1) values and queries",
+        "config": {"workload": f"{w.name} steady state at S={S}", "B": w.B, "Hq": w.Hq,
+                   "Hkv": w.Hkv, "D": w.D, "d": w.d, "S": S, "k": k, "cache_dtype": w.dtype,
+                   "step": "append 1 token/sequence + decode", "path": path_name,
+                   "layers_cycled": args.layers},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
+                     "kernel": "loki fused decode" if "fused" in path_name else "loki decode (split kernels)",
+                     "algorithmic_bytes_per_launch": by["total"],
+                     "avg_launch_ms": dec_avg_ms, "kernel_source_hash": khash},
+        "decode_only": {"head_queries_per_s": hq / (dec_avg_ms * 1e-3), "avg_ms": dec_avg_ms,
+                        "p10_ms": float(np.percentile(dec_ms, 10)),
+                        "p90_ms": float(np.percentile(dec_ms, 90))},
+    }
+
+    # ---- same-GPU dense baseline on the same caches
+    if not args.no_dense:
+        dws = loki.alloc_workspace(w.B, w.Hq, w.D, S, 1, dev)
+        for i in range(args.warmup):
+            loki.dense_decode(qs[i % R], caches[i % len(caches)], Pd, S=S, out=out, workspace=dws)
+        dev_evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(args.steps)]
+        for i in range(args.steps):
+            dev_evs[i][0].record()
+            loki.dense_decode(qs[i % R], caches[i % len(caches)], Pd, S=S, out=out, workspace=dws)
+            dev_evs[i][1].record()
+        torch.cuda.synchronize()
+        dms = float(np.mean([a.elapsed_time(b) for a, b in dev_evs]))
+        result["dense_baseline"] = {
+            "avg_ms": dms, "head_queries_per_s": hq / (dms * 1e-3),
+            "achieved_GBs": by["dense"] / (dms * 1e-3) / 1e9,
+            "loki_speedup": dms / dec_avg_ms}
+        log(f"dense {dms * 1e3:.1f} us, loki speedup {dms / dec_avg_ms:.2f}x")
+
+    # ---- the pages' run: prompt 3072, then 512 x (append 1, decode)
+    if not args.no_run and w.prefill and w.steps:
+        run_cache = caches[0]
+        nk = []
+        for st in range(w.steps):
+            kn, vn = synth.new_tokens(w, 1000 + st, Qs)
+            nk.append((up(kn), up(vn)))
+        idx_flat = torch.empty(hq * k, dtype=torch.int32, device=dev)
+        a_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for _ in range(w.steps)]
+        d_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for _ in range(w.steps)]
+        f_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for _ in range(w.steps)]
+        torch.cuda.synchronize()
+        for st in range(w.steps):
+            Sst = w.prefill + st + 1
+            kst = w.k_at(Sst)
+            a_ev[st][0].record()
+            loki.append(run_cache, nk[st][0], nk[st][1], Pd, pos=Sst - 1)
+            a_ev[st][1].record()
+            d_ev[st][0].record()
+            loki.decode(qs[st % R], run_cache, Pd, kst, S=Sst, out=out,
+                        idx=idx_flat[:hq * kst].view(w.B, w.Hq, kst), workspace=ws, path=args.path)
+            d_ev[st][1].record()
+            if not args.no_dense:
+                f_ev[st][0].record()
+                loki.dense_decode(qs[st % R], run_cache, Pd, S=Sst, out=out, workspace=dws)
+                f_ev[st][1].record()
+        torch.cuda.synchronize()
+        ssum = lambda evl: float(sum(a.elapsed_time(b) for a, b in evl))
+        run = {"prompt": w.prefill, "generated": w.steps,
+               "decode_ms_total": ssum(d_ev), "append_ms_total": ssum(a_ev)}
+        if not args.no_dense:
+            run["dense_ms_total"] = ssum(f_ev)
+            run["loki_speedup_vs_dense"] = run["dense_ms_total"] / run["decode_ms_total"]
+        result["generation_run"] = run
+        log(f"run: decode {run['decode_ms_total']:.2f} ms, append {run['append_ms_total']:.2f} ms")
+
+    # ---- CPU oracle on a bounded sample (rank 0, one GPU)
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(w, S, k, K_raw, V_raw, log)
+
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(w, S, k, K_raw, V_raw, log):
+    """The CPU oracle, as it stands, decoding a bounded sample of the same
+    workload: every query head of the first `nb` sequences at S tokens.  The
+    oracle gets its own inputs (its own calibration and float64 append of the
+    same raw keys); BLAS is held to one thread."""
+    import oracle
+    import synth
+    from threadpoolctl import threadpool_limits
+
+    nb = 4
+    Qs = synth.bases(w)
+    P = np.stack([oracle.calibrate(synth.calib_keys(w, g, Qs[g]))[0] for g in range(w.Hkv)])
+    P32 = P.astype(np.float32)
+    kn, vn = synth.new_tokens(w, 0, Qs)
+    st = np.uint16 if w.dtype == "bf16" else np.float32
+    slab = np.empty((nb, w.Hkv, S, w.d), st)
+    rest = np.empty((nb, w.Hkv, S, w.D - w.d), st)
+    vv = np.empty((nb, w.Hkv, S, w.D), st)
+    for g in range(w.Hkv):
+        Kg = np.concatenate([K_raw[:nb, g], kn[:nb, g]], axis=1)
+        Vg = np.concatenate([V_raw[:nb, g], vn[:nb, g]], axis=1)
+        slab[:, g], rest[:, g], vv[:, g] = oracle.append(oracle.to_f64(Kg, w.dtype),
+                                                         oracle.to_f64(Vg, w.dtype),
+                                                         P32[g].astype(np.float64), w.d, w.dtype)
+    q = synth.queries(w)[:nb]
+    pairs = [(b, h) for b in range(nb) for h in range(w.Hq)]
+    reps, elapsed = 0, 0.0
+    with threadpool_limits(limits=1):
+        while reps < 1 or (elapsed < 10.0 and reps < 5):
+            t = time.perf_counter()
+            oracle.decode(q, slab, rest, vv, P32, k, w.dtype, S=S, heads=pairs)
+            elapsed += time.perf_counter() - t
+            reps += 1
+    n = reps * len(pairs)
+    log(f"cpu oracle: {n} head-queries in {elapsed:.1f}s")
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": n / elapsed, "unit": "head-queries/s", "cores": 1, "kind": "oracle",
+            "sample": f"{len(pairs)} head-queries (all {w.Hq} heads of {nb} sequences) at S={S}, "
+                      f"k={k}, x{reps} repetitions, float64 numpy oracle, 1 BLAS thread",
+            "host_cpu": cpu, "host_nproc": os.cpu_count()}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,180 @@
+/*
+ * loki.h -- C ABI of libloki.so: Loki decode-step sparse attention on AMD
+ * MI355X (gfx950).
+ *
+ * The method (web pages titled "Loki: Low-rank Keys for Efficient Sparse
+ * Attention": the AI-extracted summary, sections "Approach" and the summary
+ * line, and the arXiv "Abstract"): keys live in the cache already projected
+ * onto a PCA basis P calibrated offline; the decode query is projected by the
+ * same P; every cached token is ranked by a score computed from only the
+ * leading d principal dimensions; the k best tokens are kept and exact
+ * softmax attention runs over them; nothing is ever evicted from the cache.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Ownership: the caller allocates and owns every buffer.  The library keeps no
+ *   state between calls, allocates no device memory and is thread-safe.
+ * Streams: `stream` is a hipStream_t passed as void* (NULL: the default
+ *   stream).  All device work is enqueued asynchronously on it; no entry point
+ *   synchronises.  Device pointers must stay valid until that work finishes.
+ * Errors: every call returns a loki_status.  Arguments are checked on the
+ *   host before anything is launched; a rejected call has no side effects.
+ *   LOKI_EDEVICE means a HIP launch reported an error (the outputs are then
+ *   undefined).  Nothing is thrown across the ABI.
+ * Element types: `dtype` is LOKI_F32 or LOKI_BF16 (bf16 = the upper 16 bits of
+ *   an IEEE float32) and applies to q, k_new, v_new and the three cache
+ *   tensors.  P, out and scores are always float32; idx is int32.
+ * Shapes (all tensors dense, row-major, last index fastest):
+ *   q        [B, Hq, D]              decode queries (unrotated)
+ *   P        [Hkv, D, D]  float32    P[g][m][c]: component m of principal
+ *                                    axis c of KV head g; columns orthonormal,
+ *                                    variance descending.  The rotated
+ *                                    vector is x' = x . P, i.e.
+ *                                    x'[c] = sum_m x[m] * P[g][m][c].
+ *   k_slab   [B, Hkv, S_max, d]      rotated keys, dimensions 0..d-1
+ *   k_rest   [B, Hkv, S_max, D-d]    rotated keys, dimensions d..D-1
+ *                                    (may be NULL when d == D)
+ *   v        [B, Hkv, S_max, D]      values (not rotated)
+ *   out      [B, Hq, D]   float32
+ *   idx      [B, Hq, k_eff] int32    k_eff = min(k, S); ascending token ids
+ * Query head h reads KV head h / (Hq / Hkv) (consecutive grouping).
+ * Supported: D in {64, 128}; 1 <= d <= D with d * sizeof(element) a multiple
+ *   of 16 bytes; Hq a multiple of Hkv; 1 <= S <= S_max; k >= 1 (k > S keeps
+ *   all S tokens).  Device pointers must be 16-byte aligned (idx: 4-byte).
+ *   B == 0 is a no-op that returns LOKI_OK.  Inputs must be finite.
+ */
+#ifndef LOKI_H
+#define LOKI_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LOKI_OK = 0,
+  LOKI_EINVAL = -1,       /* bad argument: null pointer, bad size, misalignment */
+  LOKI_EWORKSPACE = -2,   /* workspace missing or smaller than required        */
+  LOKI_EDEVICE = -3,      /* a HIP launch failed                               */
+  LOKI_EUNSUPPORTED = -4  /* valid but unsupported shape / dtype               */
+} loki_status;
+
+typedef enum { LOKI_F32 = 0, LOKI_BF16 = 1 } loki_dtype;
+
+/* Execution path of loki_decode_ex.  AUTO picks by shape.  FUSED runs one
+ * kernel per (sequence, query head) that scores, selects and attends with
+ * the scores held in LDS (requires (D + S + min(k, S)) * 4 bytes <= 56 KiB).
+ * SPLIT runs separate rotation, score, selection and attention kernels
+ * through the workspace. */
+typedef enum { LOKI_PATH_AUTO = 0, LOKI_PATH_FUSED = 1, LOKI_PATH_SPLIT = 2 } loki_path;
+
+/* Human-readable name of a status code.  Never NULL. */
+const char* loki_status_string(int status);
+
+/* ABI revision of this header (incremented on any signature change). */
+int loki_abi_version(void);
+
+/* Offline PCA of sample keys (host only, no device work).  The pages state
+ * that the basis is calibrated offline (summary line; "Approach": keys and
+ * queries are PCA-projected).
+ *   keys        host [n, D] float32, n >= 2
+ *   P_out       host [D, D] float32: eigenvectors of the centred sample
+ *               covariance (divisor n-1) as columns, eigenvalues descending,
+ *               each column's sign chosen so that its largest-magnitude entry
+ *               (lowest index among equal magnitudes) is positive
+ *   eigvals_out host [D] float64 or NULL
+ * Accumulates in float64; cyclic Jacobi eigensolver.  Any D >= 1. */
+int loki_calibrate(const float* keys, int64_t n, int32_t D, float* P_out, double* eigvals_out);
+
+/* Append T tokens per (sequence, KV head) at cache positions pos..pos+T-1:
+ * each key is rotated into the PCA basis (x' = x . P[g], accumulated in
+ * float64, rounded once to the cache dtype, ties to even), its leading d
+ * dimensions stored in k_slab and the rest in k_rest; values are copied
+ * unchanged ("Approach": queries and keys are PCA-projected; cache entries
+ * are never deleted).
+ *   k_new, v_new  device [B, Hkv, T, D] dtype
+ *   requires 0 <= pos, pos + T <= S_max; T == 0 is a no-op. */
+int loki_kv_append(const void* k_new, const void* v_new, const float* P,
+                   void* k_slab, void* k_rest, void* v,
+                   int32_t B, int32_t Hkv, int32_t D, int32_t d, int32_t S_max,
+                   int32_t pos, int32_t T, int32_t dtype, void* stream);
+
+/* Bytes of device workspace that every decode-family entry point below needs
+ * for these sizes (any S <= S_max, any k <= k_max).  Always a multiple of 256. */
+size_t loki_decode_workspace_size(int32_t B, int32_t Hq, int32_t D, int32_t S_max, int32_t k_max);
+
+/* One Loki decode step ("Approach"; "Abstract": ranking and selection by
+ * attention scores computed in the low-dimensional space; summary line:
+ * exact attention over the selected keys):
+ *   q' = q . P[g]
+ *   s_j = sum_{i<d} q'_i * k_slab[j, i]                 for j < S
+ *   I   = the k_eff tokens with the largest s_j, equal scores to the lower j,
+ *         written to idx in ascending order
+ *   e_j = (q' . [k_slab[j] | k_rest[j]]) / sqrt(D)      for j in I
+ *   out = sum_{j in I} softmax_I(e)_j * v[j]
+ * Ranking scores are float32 sums of the stored keys times q' (float32);
+ * accumulation is float32 throughout.  workspace: device, 16-byte aligned,
+ * >= loki_decode_workspace_size(B, Hq, D, S_max, k) bytes; the fused path
+ * does not touch it (loki_decode_ex with LOKI_PATH_FUSED accepts NULL). */
+int loki_decode(const void* q, const void* k_slab, const void* k_rest, const void* v,
+                const float* P, int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t d,
+                int32_t S, int32_t S_max, int32_t k, int32_t dtype,
+                float* out, int32_t* idx, void* workspace, size_t workspace_bytes,
+                void* stream);
+
+/* loki_decode with an explicit execution path (loki_path).  FUSED returns
+ * LOKI_EUNSUPPORTED when its LDS limit is exceeded.  Both paths compute the
+ * same function; AUTO never needs workspace beyond the size above. */
+int loki_decode_ex(const void* q, const void* k_slab, const void* k_rest, const void* v,
+                   const float* P, int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t d,
+                   int32_t S, int32_t S_max, int32_t k, int32_t dtype,
+                   float* out, int32_t* idx, void* workspace, size_t workspace_bytes,
+                   int32_t path, void* stream);
+
+/* The path loki_decode_ex would take for these sizes with `path` (AUTO,
+ * FUSED or SPLIT): LOKI_PATH_FUSED or LOKI_PATH_SPLIT, or a negative status
+ * for invalid sizes or a FUSED request that does not fit.  Host only. */
+int loki_decode_path(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t d, int32_t S,
+                     int32_t k, int32_t path);
+
+/* The ranking pass alone: scores [B, Hq, S] float32 (device) receives s_j as
+ * defined for loki_decode.  Same workspace rule. */
+int loki_scores(const void* q, const void* k_slab, const float* P,
+                int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t d,
+                int32_t S, int32_t S_max, int32_t dtype, float* scores,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/* The selection alone: for each of `rows` score rows (device float32, row r
+ * at scores + r * ld, S entries), writes the min(k, S) indices of the largest
+ * scores, equal scores to the lower index, ascending, to idx + r * min(k, S).
+ * -0.0 ranks equal to +0.0.  Requires ld >= S, 16-byte aligned scores and ld
+ * a multiple of 4. */
+int loki_topk(const float* scores, int32_t rows, int32_t S, int32_t ld, int32_t k,
+              int32_t* idx, void* stream);
+
+/* Exact attention over caller-chosen tokens: idx [B, Hq, k] int32 (device),
+ * each row strictly ascending with entries in [0, S); out as loki_decode with
+ * I = that row.  Same workspace rule (with k_max >= k). */
+int loki_attend_indices(const void* q, const void* k_slab, const void* k_rest, const void* v,
+                        const float* P, int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                        int32_t d, int32_t S, int32_t S_max, const int32_t* idx, int32_t k,
+                        int32_t dtype, float* out, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
+/* Dense ("vanilla") decode attention over all S tokens of the same rotated
+ * cache, the baseline the pages compare Loki with ("Key results"):
+ * out = softmax(q' . K'^T / sqrt(D)) . V with K' = [k_slab | k_rest].  Reads
+ * each KV head's keys and values once for all its query heads.  Same
+ * workspace rule. */
+int loki_dense_decode(const void* q, const void* k_slab, const void* k_rest, const void* v,
+                      const float* P, int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t d,
+                      int32_t S, int32_t S_max, int32_t dtype, float* out,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LOKI_H */

@@ -1,0 +1,276 @@
+"""Python binding of libloki.so (Loki decode-step sparse attention, gfx950).
+
+Argument marshalling only: every computation runs in the HIP kernels of
+libloki.so (or, for calibrate, its host C++ code).  torch supplies device
+memory and the current stream.  Importing this package does not load the
+library; the first call does, and raises if libloki.so has not been built.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libloki.so")
+
+LOKI_OK, LOKI_EINVAL, LOKI_EWORKSPACE, LOKI_EDEVICE, LOKI_EUNSUPPORTED = 0, -1, -2, -3, -4
+LOKI_F32, LOKI_BF16 = 0, 1
+PATH_AUTO, PATH_FUSED, PATH_SPLIT = 0, 1, 2
+
+# name -> (restype, argtypes); mirrors include/loki.h
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+_SIGS = {
+    "loki_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "loki_abi_version": (ctypes.c_int, []),
+    "loki_calibrate": (ctypes.c_int, [_P, ctypes.c_int64, _I, _P, _P]),
+    "loki_kv_append": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P]),
+    "loki_decode_workspace_size": (ctypes.c_size_t, [_I, _I, _I, _I, _I]),
+    "loki_decode": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I,
+                                   _P, _P, _P, ctypes.c_size_t, _P]),
+    "loki_decode_ex": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I,
+                                      _P, _P, _P, ctypes.c_size_t, _I, _P]),
+    "loki_decode_path": (ctypes.c_int, [_I, _I, _I, _I, _I, _I, _I, _I]),
+    "loki_scores": (ctypes.c_int, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P,
+                                   ctypes.c_size_t, _P]),
+    "loki_topk": (ctypes.c_int, [_P, _I, _I, _I, _I, _P, _P]),
+    "loki_attend_indices": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _I,
+                                           _I, _P, _P, ctypes.c_size_t, _P]),
+    "loki_dense_decode": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P,
+                                         _P, ctypes.c_size_t, _P]),
+}
+
+_lib = None
+
+
+class LokiError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} ({status})")
+
+
+def load(path: str | None = None):
+    """Load libloki.so (once).  Raises FileNotFoundError if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise FileNotFoundError(f"{p} not built; run python -m sparse_attention_decode_loki_amd.build_lib")
+    lib = ctypes.CDLL(p)
+    for name, (res, args) in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def exported_symbols() -> list[str]:
+    return list(_SIGS)
+
+
+def status_string(status: int) -> str:
+    return load().loki_status_string(int(status)).decode()
+
+
+def _check(st: int, where: str):
+    if st != LOKI_OK:
+        raise LokiError(st, where)
+
+
+# ------------------------------------------------------------ torch glue --
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return LOKI_F32
+    if t.dtype == torch.bfloat16:
+        return LOKI_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _need(t, name, dtype=None, cuda=True):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if cuda and not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}")
+
+
+class KVCache:
+    """Device buffers of a Loki key/value cache with capacity S_max:
+    k_slab [B, Hkv, S_max, d], k_rest [B, Hkv, S_max, D-d] (None if d == D),
+    v [B, Hkv, S_max, D]; `length` counts the tokens appended so far."""
+
+    def __init__(self, B, Hkv, S_max, D, d, dtype, device="cuda"):
+        torch = _torch()
+        self.B, self.Hkv, self.S_max, self.D, self.d = B, Hkv, S_max, D, d
+        self.dtype = dtype
+        self.k_slab = torch.zeros((B, Hkv, S_max, d), dtype=dtype, device=device)
+        self.k_rest = (torch.zeros((B, Hkv, S_max, D - d), dtype=dtype, device=device)
+                       if d < D else None)
+        self.v = torch.zeros((B, Hkv, S_max, D), dtype=dtype, device=device)
+        self.length = 0
+
+
+def calibrate(keys: np.ndarray):
+    """PCA basis of sample keys (host).  keys [n, D] -> (P [D, D] float32,
+    eigvals [D] float64), columns = principal axes, variance descending."""
+    lib = load()
+    k = np.ascontiguousarray(keys, dtype=np.float32)
+    n, D = k.shape
+    P = np.empty((D, D), dtype=np.float32)
+    ev = np.empty(D, dtype=np.float64)
+    _check(lib.loki_calibrate(k.ctypes.data, n, D, P.ctypes.data, ev.ctypes.data), "loki_calibrate")
+    return P, ev
+
+
+def append(cache: KVCache, k_new, v_new, P, pos: int | None = None):
+    """Rotate and store k_new/v_new [B, Hkv, T, D] at positions pos..pos+T-1
+    (default: the cache's current length, which then advances)."""
+    lib = load()
+    _need(k_new, "k_new", cache.dtype)
+    _need(v_new, "v_new", cache.dtype)
+    _need(P, "P", _torch().float32)
+    B, Hkv, T, D = k_new.shape
+    at = cache.length if pos is None else pos
+    st = lib.loki_kv_append(_ptr(k_new), _ptr(v_new), _ptr(P), _ptr(cache.k_slab),
+                            _ptr(cache.k_rest), _ptr(cache.v), B, Hkv, D, cache.d, cache.S_max,
+                            at, T, _dtype_code(k_new), _stream(k_new))
+    _check(st, "loki_kv_append")
+    if pos is None or at + T > cache.length:
+        cache.length = max(cache.length, at + T)
+
+
+def workspace_size(B, Hq, D, S_max, k_max) -> int:
+    return int(load().loki_decode_workspace_size(B, Hq, D, S_max, k_max))
+
+
+def alloc_workspace(B, Hq, D, S_max, k_max, device="cuda"):
+    torch = _torch()
+    n = max(workspace_size(B, Hq, D, S_max, k_max), 256)
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def decode(q, cache: KVCache, P, k: int, S: int | None = None, out=None, idx=None,
+           workspace=None, path: int = PATH_AUTO):
+    """One Loki decode step.  q [B, Hq, D] -> (out [B, Hq, D] float32,
+    idx [B, Hq, min(k, S)] int32 ascending)."""
+    torch = _torch()
+    lib = load()
+    _need(q, "q", cache.dtype)
+    _need(P, "P", torch.float32)
+    B, Hq, D = q.shape
+    S = cache.length if S is None else S
+    kk = min(k, S)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    if idx is None:
+        idx = torch.empty((B, Hq, kk), dtype=torch.int32, device=q.device)
+    if workspace is None and path != PATH_FUSED:
+        workspace = alloc_workspace(B, Hq, D, cache.S_max, kk, q.device)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.loki_decode_ex(_ptr(q), _ptr(cache.k_slab), _ptr(cache.k_rest), _ptr(cache.v), _ptr(P),
+                            B, Hq, cache.Hkv, D, cache.d, S, cache.S_max, k, _dtype_code(q),
+                            _ptr(out), _ptr(idx), _ptr(workspace), wsb, path, _stream(q))
+    _check(st, "loki_decode")
+    return out, idx
+
+
+def decode_path(B, Hq, Hkv, D, d, S, k, path=PATH_AUTO) -> int:
+    """The path (PATH_FUSED or PATH_SPLIT) loki_decode_ex takes for these sizes."""
+    st = load().loki_decode_path(B, Hq, Hkv, D, d, S, k, path)
+    if st < 0:
+        raise LokiError(st, "loki_decode_path")
+    return st
+
+
+def scores(q, cache: KVCache, P, S: int | None = None, out=None, workspace=None):
+    """Ranking scores [B, Hq, S] float32 (the low-rank pass alone)."""
+    torch = _torch()
+    lib = load()
+    B, Hq, D = q.shape
+    S = cache.length if S is None else S
+    if out is None:
+        out = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = alloc_workspace(B, Hq, D, cache.S_max, 1, q.device)
+    st = lib.loki_scores(_ptr(q), _ptr(cache.k_slab), _ptr(P), B, Hq, cache.Hkv, D, cache.d, S,
+                         cache.S_max, _dtype_code(q), _ptr(out), _ptr(workspace),
+                         workspace.numel(), _stream(q))
+    _check(st, "loki_scores")
+    return out
+
+
+def topk(scores_2d, k: int, S: int | None = None, idx=None):
+    """Top-k of each row of a float32 device matrix [rows, ld]; ascending ids."""
+    torch = _torch()
+    lib = load()
+    _need(scores_2d, "scores", torch.float32)
+    rows, ld = scores_2d.shape
+    S = ld if S is None else S
+    kk = min(k, S)
+    if idx is None:
+        idx = torch.empty((rows, kk), dtype=torch.int32, device=scores_2d.device)
+    st = lib.loki_topk(_ptr(scores_2d), rows, S, ld, k, _ptr(idx), _stream(scores_2d))
+    _check(st, "loki_topk")
+    return idx
+
+
+def attend_indices(q, cache: KVCache, P, idx, S: int | None = None, out=None, workspace=None):
+    """Exact attention over given ascending index rows idx [B, Hq, k] int32."""
+    torch = _torch()
+    lib = load()
+    _need(idx, "idx", torch.int32)
+    B, Hq, D = q.shape
+    k = idx.shape[-1]
+    S = cache.length if S is None else S
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = alloc_workspace(B, Hq, D, cache.S_max, k, q.device)
+    st = lib.loki_attend_indices(_ptr(q), _ptr(cache.k_slab), _ptr(cache.k_rest), _ptr(cache.v),
+                                 _ptr(P), B, Hq, cache.Hkv, D, cache.d, S, cache.S_max, _ptr(idx),
+                                 k, _dtype_code(q), _ptr(out), _ptr(workspace), workspace.numel(),
+                                 _stream(q))
+    _check(st, "loki_attend_indices")
+    return out
+
+
+def dense_decode(q, cache: KVCache, P, S: int | None = None, out=None, workspace=None):
+    """Dense attention over all S tokens of the same rotated cache."""
+    torch = _torch()
+    lib = load()
+    B, Hq, D = q.shape
+    S = cache.length if S is None else S
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = alloc_workspace(B, Hq, D, cache.S_max, 1, q.device)
+    st = lib.loki_dense_decode(_ptr(q), _ptr(cache.k_slab), _ptr(cache.k_rest), _ptr(cache.v),
+                               _ptr(P), B, Hq, cache.Hkv, D, cache.d, S, cache.S_max,
+                               _dtype_code(q), _ptr(out), _ptr(workspace), workspace.numel(),
+                               _stream(q))
+    _check(st, "loki_dense_decode")
+    return out

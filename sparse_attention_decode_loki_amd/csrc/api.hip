@@ -1,0 +1,299 @@
+// C ABI of libloki.so: argument checks on the host, workspace layout and
+// path choice, then kernel launches on the caller's stream.
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "../../include/loki.h"
+#include "launch.hpp"
+
+using loki::DecodeArgs;
+
+namespace {
+
+constexpr int kAbiVersion = 1;
+constexpr int kTargetWorkgroups = 1024;  // about four per compute unit
+constexpr int kAttendStageTok = 2048;    // must match the attend kernel's LDS stage
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+int cdiv(int64_t a, int64_t b) { return static_cast<int>((a + b - 1) / b); }
+int esize(int dtype) { return dtype == LOKI_F32 ? 4 : 2; }
+
+int sparse_nsplit(int rows, int kk) {
+  int n = std::min(cdiv(kTargetWorkgroups, rows), cdiv(kk, 64));
+  n = std::max(n, cdiv(kk, kAttendStageTok));
+  return std::max(n, 1);
+}
+
+int heads_per_dense_block(int G) { return G >= 4 ? 4 : (G >= 2 ? 2 : 1); }
+
+int dense_nsplit(int B, int Hq, int Hkv, int S) {
+  const int G = Hq / Hkv;
+  const int rows = B * Hkv * cdiv(G, heads_per_dense_block(G));
+  return std::max(1, std::min(cdiv(kTargetWorkgroups, rows), cdiv(S, 256)));
+}
+
+struct Layout {
+  size_t qrot, scores, part, total;
+};
+
+Layout layout(int B, int Hq, int D, int S_max, int nsplit) {
+  Layout L;
+  const size_t rows = static_cast<size_t>(B) * Hq;
+  L.qrot = 0;
+  L.scores = align256(rows * D * sizeof(float));
+  L.part = L.scores + align256(rows * static_cast<size_t>(S_max) * sizeof(float));
+  L.total = L.part + align256(rows * static_cast<size_t>(nsplit) * (D + 2) * sizeof(float));
+  return L;
+}
+
+int max_nsplit(int B, int Hq, int S_max, int k_max) {
+  const int kk = std::max(1, std::min(k_max, S_max));
+  // dense_nsplit over any Hkv dividing Hq: its row count is at least B
+  const int dense_max = std::max(1, std::min(cdiv(kTargetWorkgroups, B), cdiv(S_max, 256)));
+  return std::max(sparse_nsplit(B * Hq, kk), dense_max);
+}
+
+size_t workspace_bytes(int B, int Hq, int D, int S_max, int k_max) {
+  return layout(B, Hq, D, S_max, max_nsplit(B, Hq, S_max, k_max)).total;
+}
+
+// Shape checks shared by the decode family.  Returns LOKI_OK or an error.
+int check_shape(int B, int Hq, int Hkv, int D, int d, int S, int S_max, int dtype) {
+  if (dtype != LOKI_F32 && dtype != LOKI_BF16) return LOKI_EINVAL;
+  if (B < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return LOKI_EINVAL;
+  if (D < 1 || d < 1 || d > D) return LOKI_EINVAL;
+  if (S < 1 || S_max < S) return LOKI_EINVAL;
+  if (D != 64 && D != 128) return LOKI_EUNSUPPORTED;
+  if ((d * esize(dtype)) % 16 != 0) return LOKI_EUNSUPPORTED;
+  if (static_cast<int64_t>(B) * Hq > (1 << 30) || Hkv > 65535) return LOKI_EUNSUPPORTED;
+  if (S > 65535 * 1024) return LOKI_EUNSUPPORTED;  // score grid.y limit
+  return LOKI_OK;
+}
+
+int check_cache_ptrs(const void* k_slab, const void* k_rest, const void* v, const float* P, int D,
+                     int d) {
+  if (!k_slab || !v || !P) return LOKI_EINVAL;
+  if (d < D && !k_rest) return LOKI_EINVAL;
+  if (!aligned16(k_slab) || !aligned16(v) || !aligned16(P)) return LOKI_EINVAL;
+  if (k_rest && !aligned16(k_rest)) return LOKI_EINVAL;
+  return LOKI_OK;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? LOKI_OK : LOKI_EDEVICE; }
+
+DecodeArgs make_args(const void* q, const void* k_slab, const void* k_rest, const void* v,
+                     const float* P, int B, int Hq, int Hkv, int D, int d, int S, int S_max,
+                     int dtype, float* out, int32_t* idx, void* stream) {
+  DecodeArgs a;
+  a.q = q;
+  a.k_slab = k_slab;
+  a.k_rest = d < D ? k_rest : nullptr;
+  a.v = v;
+  a.P = P;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.D = D;
+  a.d = d;
+  a.S = S;
+  a.S_max = S_max;
+  a.dtype = dtype;
+  a.out = out;
+  a.idx = idx;
+  a.stream = static_cast<hipStream_t>(stream);
+  return a;
+}
+
+bool fused_fits(int D, int S, int kk) {
+  return loki::fused_lds_bytes(D, S, kk) <= loki::kFusedLdsMax;
+}
+
+// The fused kernel reads the key slab once per query head, so it is chosen
+// for one query head per KV head, when there are enough (sequence, head)
+// pairs to give every compute unit work, and when its LDS fits.
+bool auto_fused(int B, int Hq, int Hkv, int D, int S, int kk) {
+  return Hq == Hkv && static_cast<int64_t>(B) * Hq >= 256 && fused_fits(D, S, kk);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* loki_status_string(int status) {
+  switch (status) {
+    case LOKI_OK: return "LOKI_OK";
+    case LOKI_EINVAL: return "LOKI_EINVAL: invalid argument";
+    case LOKI_EWORKSPACE: return "LOKI_EWORKSPACE: workspace missing or too small";
+    case LOKI_EDEVICE: return "LOKI_EDEVICE: HIP launch failed";
+    case LOKI_EUNSUPPORTED: return "LOKI_EUNSUPPORTED: unsupported shape or dtype";
+    default: return "LOKI: unknown status";
+  }
+}
+
+int loki_abi_version(void) { return kAbiVersion; }
+
+int loki_kv_append(const void* k_new, const void* v_new, const float* P, void* k_slab,
+                   void* k_rest, void* v, int32_t B, int32_t Hkv, int32_t D, int32_t d,
+                   int32_t S_max, int32_t pos, int32_t T, int32_t dtype, void* stream) {
+  if (dtype != LOKI_F32 && dtype != LOKI_BF16) return LOKI_EINVAL;
+  if (B < 0 || Hkv < 1 || D < 1 || d < 1 || d > D || S_max < 1 || pos < 0 || T < 0)
+    return LOKI_EINVAL;
+  if (static_cast<int64_t>(pos) + T > S_max) return LOKI_EINVAL;
+  if (D != 64 && D != 128) return LOKI_EUNSUPPORTED;
+  if ((d * esize(dtype)) % 16 != 0) return LOKI_EUNSUPPORTED;
+  if (B == 0 || T == 0) return LOKI_OK;
+  if (!k_new || !v_new) return LOKI_EINVAL;
+  int st = check_cache_ptrs(k_slab, k_rest, v, P, D, d);
+  if (st != LOKI_OK) return st;
+  if (T > 65535 * 32) return LOKI_EUNSUPPORTED;  // grid.y limit
+  return status_of(loki::launch_append(k_new, v_new, P, k_slab, d < D ? k_rest : nullptr, v, B,
+                                       Hkv, D, d, S_max, pos, T, dtype,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+size_t loki_decode_workspace_size(int32_t B, int32_t Hq, int32_t D, int32_t S_max, int32_t k_max) {
+  if (B <= 0 || Hq <= 0 || D <= 0 || S_max <= 0) return 0;
+  return workspace_bytes(B, Hq, D, S_max, k_max < 1 ? 1 : k_max);
+}
+
+int loki_decode_path(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t d, int32_t S,
+                     int32_t k, int32_t path) {
+  int st = check_shape(B < 1 ? 1 : B, Hq, Hkv, D, d, S, S, LOKI_BF16);
+  if (st != LOKI_OK) return st;
+  if (k < 1) return LOKI_EINVAL;
+  const int kk = std::min(k, S);
+  if (path == LOKI_PATH_SPLIT) return LOKI_PATH_SPLIT;
+  if (path == LOKI_PATH_FUSED) return fused_fits(D, S, kk) ? LOKI_PATH_FUSED : LOKI_EUNSUPPORTED;
+  if (path != LOKI_PATH_AUTO) return LOKI_EINVAL;
+  return auto_fused(B, Hq, Hkv, D, S, kk) ? LOKI_PATH_FUSED : LOKI_PATH_SPLIT;
+}
+
+int loki_decode_ex(const void* q, const void* k_slab, const void* k_rest, const void* v,
+                   const float* P, int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t d,
+                   int32_t S, int32_t S_max, int32_t k, int32_t dtype, float* out, int32_t* idx,
+                   void* workspace, size_t ws_bytes, int32_t path, void* stream) {
+  int st = check_shape(B, Hq, Hkv, D, d, S, S_max, dtype);
+  if (st != LOKI_OK) return st;
+  if (k < 1) return LOKI_EINVAL;
+  if (path != LOKI_PATH_AUTO && path != LOKI_PATH_FUSED && path != LOKI_PATH_SPLIT)
+    return LOKI_EINVAL;
+  if (B == 0) return LOKI_OK;
+  if (!q || !out || !idx) return LOKI_EINVAL;
+  st = check_cache_ptrs(k_slab, k_rest, v, P, D, d);
+  if (st != LOKI_OK) return st;
+  if (!aligned16(out) || (reinterpret_cast<uintptr_t>(idx) & 3u)) return LOKI_EINVAL;
+  const int kk = std::min(k, S);
+  const bool fused = path == LOKI_PATH_FUSED ||
+                     (path == LOKI_PATH_AUTO && auto_fused(B, Hq, Hkv, D, S, kk));
+  DecodeArgs a = make_args(q, k_slab, k_rest, v, P, B, Hq, Hkv, D, d, S, S_max, dtype, out, idx,
+                           stream);
+  if (fused) {
+    if (!fused_fits(D, S, kk)) return LOKI_EUNSUPPORTED;
+    return status_of(loki::launch_fused(a, kk));
+  }
+  const int rows = B * Hq;
+  const int nsplit = sparse_nsplit(rows, kk);
+  const Layout L = layout(B, Hq, D, S_max, nsplit);
+  if (!workspace || ws_bytes < L.total || !aligned16(workspace)) return LOKI_EWORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  float* qrot = reinterpret_cast<float*>(ws + L.qrot);
+  float* scores = reinterpret_cast<float*>(ws + L.scores);
+  float* part = reinterpret_cast<float*>(ws + L.part);
+  hipError_t e = loki::launch_rotate(a, qrot);
+  if (e == hipSuccess) e = loki::launch_scores(a, qrot, scores);
+  if (e == hipSuccess) e = loki::launch_topk(scores, rows, S, S, kk, idx, a.stream);
+  if (e == hipSuccess) e = loki::launch_attend(a, qrot, scores, idx, kk, part, nsplit, true);
+  return status_of(e);
+}
+
+int loki_decode(const void* q, const void* k_slab, const void* k_rest, const void* v,
+                const float* P, int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t d,
+                int32_t S, int32_t S_max, int32_t k, int32_t dtype, float* out, int32_t* idx,
+                void* workspace, size_t ws_bytes, void* stream) {
+  return loki_decode_ex(q, k_slab, k_rest, v, P, B, Hq, Hkv, D, d, S, S_max, k, dtype, out, idx,
+                        workspace, ws_bytes, LOKI_PATH_AUTO, stream);
+}
+
+int loki_scores(const void* q, const void* k_slab, const float* P, int32_t B, int32_t Hq,
+                int32_t Hkv, int32_t D, int32_t d, int32_t S, int32_t S_max, int32_t dtype,
+                float* scores, void* workspace, size_t ws_bytes, void* stream) {
+  int st = check_shape(B, Hq, Hkv, D, d, S, S_max, dtype);
+  if (st != LOKI_OK) return st;
+  if (B == 0) return LOKI_OK;
+  if (!q || !k_slab || !P || !scores) return LOKI_EINVAL;
+  if (!aligned16(k_slab) || !aligned16(P) || !aligned16(scores)) return LOKI_EINVAL;
+  const Layout L = layout(B, Hq, D, S_max, 1);
+  if (!workspace || ws_bytes < L.scores || !aligned16(workspace)) return LOKI_EWORKSPACE;
+  DecodeArgs a = make_args(q, k_slab, nullptr, k_slab, P, B, Hq, Hkv, D, d, S, S_max, dtype,
+                           nullptr, nullptr, stream);
+  float* qrot = static_cast<float*>(workspace);
+  hipError_t e = loki::launch_rotate(a, qrot);
+  if (e == hipSuccess) e = loki::launch_scores(a, qrot, scores);
+  return status_of(e);
+}
+
+int loki_topk(const float* scores, int32_t rows, int32_t S, int32_t ld, int32_t k, int32_t* idx,
+              void* stream) {
+  if (rows < 0 || S < 1 || ld < S || k < 1) return LOKI_EINVAL;
+  if (rows == 0) return LOKI_OK;
+  if (!scores || !idx || !aligned16(scores) || (ld % 4) != 0) return LOKI_EINVAL;
+  if (reinterpret_cast<uintptr_t>(idx) & 3u) return LOKI_EINVAL;
+  return status_of(loki::launch_topk(scores, rows, S, ld, std::min(k, S), idx,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+int loki_attend_indices(const void* q, const void* k_slab, const void* k_rest, const void* v,
+                        const float* P, int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t d,
+                        int32_t S, int32_t S_max, const int32_t* idx, int32_t k, int32_t dtype,
+                        float* out, void* workspace, size_t ws_bytes, void* stream) {
+  int st = check_shape(B, Hq, Hkv, D, d, S, S_max, dtype);
+  if (st != LOKI_OK) return st;
+  if (k < 1 || k > S) return LOKI_EINVAL;
+  if (B == 0) return LOKI_OK;
+  if (!q || !out || !idx) return LOKI_EINVAL;
+  st = check_cache_ptrs(k_slab, k_rest, v, P, D, d);
+  if (st != LOKI_OK) return st;
+  if (!aligned16(out) || (reinterpret_cast<uintptr_t>(idx) & 3u)) return LOKI_EINVAL;
+  const int rows = B * Hq;
+  const int nsplit = sparse_nsplit(rows, k);
+  const Layout L = layout(B, Hq, D, S_max, nsplit);
+  if (!workspace || ws_bytes < L.total || !aligned16(workspace)) return LOKI_EWORKSPACE;
+  DecodeArgs a = make_args(q, k_slab, k_rest, v, P, B, Hq, Hkv, D, d, S, S_max, dtype, out,
+                           const_cast<int32_t*>(idx), stream);
+  char* ws = static_cast<char*>(workspace);
+  float* qrot = reinterpret_cast<float*>(ws + L.qrot);
+  float* scores = reinterpret_cast<float*>(ws + L.scores);
+  float* part = reinterpret_cast<float*>(ws + L.part);
+  hipError_t e = loki::launch_rotate(a, qrot);
+  if (e == hipSuccess) e = loki::launch_scores(a, qrot, scores);
+  if (e == hipSuccess) e = loki::launch_attend(a, qrot, scores, idx, k, part, nsplit, true);
+  return status_of(e);
+}
+
+int loki_dense_decode(const void* q, const void* k_slab, const void* k_rest, const void* v,
+                      const float* P, int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t d,
+                      int32_t S, int32_t S_max, int32_t dtype, float* out, void* workspace,
+                      size_t ws_bytes, void* stream) {
+  int st = check_shape(B, Hq, Hkv, D, d, S, S_max, dtype);
+  if (st != LOKI_OK) return st;
+  if (B == 0) return LOKI_OK;
+  if (!q || !out) return LOKI_EINVAL;
+  st = check_cache_ptrs(k_slab, k_rest, v, P, D, d);
+  if (st != LOKI_OK) return st;
+  if (!aligned16(out)) return LOKI_EINVAL;
+  const int nsplit = dense_nsplit(B, Hq, Hkv, S);
+  const Layout L = layout(B, Hq, D, S_max, nsplit);
+  if (!workspace || ws_bytes < L.total || !aligned16(workspace)) return LOKI_EWORKSPACE;
+  DecodeArgs a = make_args(q, k_slab, k_rest, v, P, B, Hq, Hkv, D, d, S, S_max, dtype, out,
+                           nullptr, stream);
+  char* ws = static_cast<char*>(workspace);
+  float* qrot = reinterpret_cast<float*>(ws + L.qrot);
+  float* part = reinterpret_cast<float*>(ws + L.part);
+  hipError_t e = loki::launch_rotate(a, qrot);
+  if (e == hipSuccess) e = loki::launch_attend(a, qrot, nullptr, nullptr, S, part, nsplit, false);
+  return status_of(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,45 @@
+// Internal interface between the C ABI (api.hip) and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include <cmath>
+
+namespace loki {
+
+constexpr int kF32 = 0;
+constexpr int kBF16 = 1;
+constexpr size_t kTopkLdsMax = 48 * 1024;    // scores staged in LDS up to this size
+constexpr size_t kFusedLdsMax = 56 * 1024;   // fused path: q' + scores + kept ids (dynamic LDS)
+
+struct DecodeArgs {
+  const void* q;
+  const void* k_slab;
+  const void* k_rest;
+  const void* v;
+  const float* P;
+  int B, Hq, Hkv, D, d, S, S_max;
+  int dtype;
+  float* out;
+  int* idx;
+  hipStream_t stream;
+};
+
+hipError_t launch_rotate(const DecodeArgs& a, float* qrot);
+hipError_t launch_scores(const DecodeArgs& a, const float* qrot, float* scores);
+hipError_t launch_topk(const float* scores, int rows, int S, int64_t ld, int k, int* idx,
+                       hipStream_t stream);
+// sparse: attention over idx (k_eff = kk per row, scores from `scores`);
+// dense: over all S tokens.  nsplit > 1 writes `part` and combines into out.
+hipError_t launch_attend(const DecodeArgs& a, const float* qrot, const float* scores,
+                         const int* idx, int kk, float* part, int nsplit, bool sparse);
+size_t fused_lds_bytes(int D, int S, int kk);
+hipError_t launch_fused(const DecodeArgs& a, int kk);
+
+hipError_t launch_append(const void* k_new, const void* v_new, const float* P, void* k_slab,
+                         void* k_rest, void* v, int B, int Hkv, int D, int d, int S_max, int pos,
+                         int T, int dtype, hipStream_t stream);
+
+}  // namespace loki

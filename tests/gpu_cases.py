@@ -1,0 +1,171 @@
+"""Builders shared by the GPU parity tests.
+
+Every input comes from the seeded generators (synth) and the oracle: the
+PCA basis is the oracle's calibration of the generator's calibration keys,
+and the rotated cache is the oracle's float64 append of the generator's raw
+keys, rounded to the cache dtype.  The GPU library only ever receives these
+bytes; nothing produced by the GPU feeds the oracle.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import numpy as np
+
+import oracle
+import synth
+
+# a finite value far outside the data: any read past the S valid tokens
+# would dominate a score or a softmax and fail the comparison
+_POISON = 3.0e4
+
+
+@dataclass
+class Case:
+    w: synth.Workload
+    S: int
+    S_max: int
+    P: np.ndarray          # [Hkv, D, D] float32
+    q: np.ndarray          # [B, Hq, D] storage
+    K: np.ndarray          # raw keys [B, Hkv, S, D] storage
+    V: np.ndarray          # raw values [B, Hkv, S, D] storage
+    slab: np.ndarray       # [B, Hkv, S_max, d] storage
+    rest: np.ndarray       # [B, Hkv, S_max, D-d] storage (width 0 when d == D)
+    v: np.ndarray          # [B, Hkv, S_max, D] storage
+
+    @property
+    def k(self):
+        return self.w.k_at(self.S)
+
+
+def storage_dtype(dtype: str):
+    return np.uint16 if dtype == "bf16" else np.float32
+
+
+def basis(w: synth.Workload) -> np.ndarray:
+    P = np.empty((w.Hkv, w.D, w.D), np.float32)
+    for g in range(w.Hkv):
+        Pg, _ = oracle.calibrate(synth.calib_keys(w, g))
+        P[g] = Pg.astype(np.float32)
+    return P
+
+
+def make_case(w: synth.Workload, S: int | None = None, S_max: int | None = None) -> Case:
+    S = w.S if S is None else S
+    S_max = S if S_max is None else S_max
+    P = basis(w)
+    K, V = synth.raw_cache(w, S)
+    st = storage_dtype(w.dtype)
+    poison = oracle.from_f64(np.array(_POISON), w.dtype)
+    slab = np.full((w.B, w.Hkv, S_max, w.d), poison, st)
+    rest = np.full((w.B, w.Hkv, S_max, w.D - w.d), poison, st)
+    vv = np.full((w.B, w.Hkv, S_max, w.D), poison, st)
+    for g in range(w.Hkv):
+        s_, r_, v_ = oracle.append(oracle.to_f64(K[:, g], w.dtype), oracle.to_f64(V[:, g], w.dtype),
+                                   P[g].astype(np.float64), w.d, w.dtype)
+        slab[:, g, :S], rest[:, g, :S], vv[:, g, :S] = s_, r_, v_
+    return Case(w, S, S_max, P, synth.queries(w), K, V, slab, rest, vv)
+
+
+# ------------------------------------------------------------- torch glue --
+
+def to_dev(a: np.ndarray, dtype: str):
+    import torch
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def to_host(t, dtype: str) -> np.ndarray:
+    import torch
+    if dtype == "bf16":
+        return t.detach().view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.detach().cpu().numpy()
+
+
+def device_cache(loki, c: Case):
+    import torch
+    w = c.w
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    cache = loki.KVCache(w.B, w.Hkv, c.S_max, w.D, w.d, tdt)
+    cache.k_slab.copy_(to_dev(c.slab, w.dtype))
+    if w.d < w.D:
+        cache.k_rest.copy_(to_dev(c.rest, w.dtype))
+    cache.v.copy_(to_dev(c.v, w.dtype))
+    cache.length = c.S
+    return cache
+
+
+# ------------------------------------------------------------- comparison --
+
+def out_error(dtype: str, got: np.ndarray, ref: np.ndarray) -> float:
+    """fp32 caches: max-abs error; bf16 caches: relative L2 error."""
+    got = np.asarray(got, np.float64)
+    if dtype == "f32":
+        return float(np.max(np.abs(got - ref)))
+    return float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30))
+
+
+TOL = {"f32": 1e-5, "bf16": 2e-3}
+
+
+def check_decode(dtype, k, out, idx, ref_out, ref_idx, ref_s, pairs, max_swaps=None):
+    """Index sets: equal to the oracle's whenever the relative gap at the k-th
+    place exceeds 1e-4; otherwise a valid choice inside the tie band.
+    Outputs: compared with the oracle wherever the sets agree.
+    Returns (n_band, n_swapped, worst_output_error)."""
+    n_band = n_swap = 0
+    worst = 0.0
+    for b, h in pairs:
+        s = ref_s[b, h]
+        kk = min(k, s.shape[0])
+        gi = idx[b, h].astype(np.int64)
+        assert gi.shape == (kk,)
+        gap = oracle.topk_gap(s, kk)
+        if gap > 1e-4:
+            assert np.array_equal(gi, ref_idx[b, h]), f"idx mismatch at (b={b}, h={h}), gap {gap:.3g}"
+        else:
+            n_band += 1
+            assert oracle.valid_in_band(s, kk, gi), f"invalid near-tie set at (b={b}, h={h})"
+        if np.array_equal(gi, ref_idx[b, h]):
+            e = out_error(dtype, out[b, h], ref_out[b, h])
+            worst = max(worst, e)
+            assert e <= TOL[dtype], f"output error {e:.3g} at (b={b}, h={h})"
+        else:
+            n_swap += 1
+    limit = max(1, len(pairs) // 100) if max_swaps is None else max_swaps
+    assert n_swap <= limit, f"{n_swap} near-tie swaps in {len(pairs)} head-queries"
+    return n_band, n_swap, worst
+
+
+def all_pairs(w):
+    return [(b, h) for b in range(w.B) for h in range(w.Hq)]
+
+
+def sample_pairs(w, n=16, seed=0):
+    rng = np.random.default_rng(seed)
+    allp = all_pairs(w)
+    pick = rng.choice(len(allp), size=min(n, len(allp)), replace=False)
+    return sorted(allp[i] for i in pick)
+
+
+def ulp_diff_bf16(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """|a - b| in units of bf16 steps for same-sign finite bf16 patterns
+    (ordered integer distance of the bit patterns)."""
+    def ordered(x):
+        x = x.astype(np.int32)
+        return np.where(x & 0x8000, 0x8000 - (x & 0x7FFF), 0x8000 + x)
+    return np.abs(ordered(a) - ordered(b))
+
+
+def ulp_diff_f32(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    def ordered(x):
+        x = x.view(np.int32).astype(np.int64)
+        return np.where(x < 0, -(x & 0x7FFFFFFF), x)
+    return np.abs(ordered(np.ascontiguousarray(a)) - ordered(np.ascontiguousarray(b)))
+
+
+def scale(D):
+    return 1.0 / math.sqrt(D)

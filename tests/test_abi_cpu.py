@@ -1,0 +1,161 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/loki.h declares, rejects bad arguments on the host before launching
+anything, and its host-only PCA calibration matches the oracle."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "loki.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(loki_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    import sparse_attention_decode_loki_amd as loki
+    if not os.path.exists(loki.LIB_PATH):
+        pytest.fail("libloki.so not built: run python -m sparse_attention_decode_loki_amd.build_lib")
+    loki.load()
+    return loki
+
+
+def test_header_declarations_exported(L):
+    names = _declared()
+    assert len(names) >= 11
+    out = subprocess.run(["nm", "-D", "--defined-only", L.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (loki_[a-z_]+)", out))
+    assert set(names) <= exported, set(names) - exported
+    assert set(names) == set(L.exported_symbols())
+
+
+def test_version_and_status_strings(L):
+    lib = L.load()
+    assert lib.loki_abi_version() == 1
+    for st in (0, -1, -2, -3, -4, 7):
+        assert lib.loki_status_string(st)
+    assert L.status_string(-2).startswith("LOKI_EWORKSPACE")
+
+
+FAKE = ctypes.c_void_p(0x100000)       # never dereferenced on rejected calls
+FAKE_MIS = ctypes.c_void_p(0x100004)   # misaligned
+
+
+def _decode(lib, **kw):
+    a = dict(q=FAKE, ks=FAKE, kr=FAKE, v=FAKE, P=FAKE, B=2, Hq=4, Hkv=2, D=128, d=32, S=100,
+             S_max=128, k=25, dt=1, out=FAKE, idx=FAKE, ws=FAKE, wsb=1 << 40, path=2)
+    a.update(kw)
+    return lib.loki_decode_ex(a["q"], a["ks"], a["kr"], a["v"], a["P"], a["B"], a["Hq"], a["Hkv"],
+                              a["D"], a["d"], a["S"], a["S_max"], a["k"], a["dt"], a["out"],
+                              a["idx"], a["ws"], a["wsb"], a["path"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(d=0), -1), (dict(d=129), -1), (dict(k=0), -1), (dict(S=0), -1), (dict(S=200), -1),
+    (dict(Hq=3), -1), (dict(Hkv=0), -1), (dict(dt=7), -1), (dict(B=-1), -1), (dict(path=9), -1),
+    (dict(q=None), -1), (dict(ks=None), -1), (dict(kr=None), -1), (dict(v=None), -1),
+    (dict(P=None), -1), (dict(out=None), -1), (dict(idx=None), -1),
+    (dict(ks=FAKE_MIS), -1), (dict(v=FAKE_MIS), -1), (dict(out=FAKE_MIS), -1),
+    (dict(D=96, d=32), -4), (dict(d=20), -4), (dict(dt=0, d=18), -4),
+    (dict(ws=None), -2), (dict(wsb=1024), -2), (dict(ws=FAKE_MIS), -2),
+])
+def test_decode_rejects_bad_arguments(L, kw, want):
+    assert _decode(L.load(), **kw) == want
+
+
+def test_decode_fused_rejects_when_lds_too_small(L):
+    # q' + scores + kept ids over 56 KiB cannot take the fused path
+    assert _decode(L.load(), path=1, S=20000, S_max=20000, k=5000) == -4
+    lib = L.load()
+    assert lib.loki_decode_path(1, 4, 4, 128, 32, 20000, 5000, 1) == -4
+    assert lib.loki_decode_path(16, 40, 40, 128, 32, 3584, 896, 0) == 1   # auto -> fused
+    assert lib.loki_decode_path(8, 32, 8, 128, 32, 8192, 2048, 0) == 2    # GQA -> split
+    assert lib.loki_decode_path(1, 32, 32, 128, 32, 4096, 1024, 0) == 2   # few heads -> split
+    assert lib.loki_decode_path(1, 4, 4, 128, 32, 100, 25, 2) == 2
+    assert lib.loki_decode_path(1, 4, 4, 128, 32, 100, 25, 1) == 1
+    assert lib.loki_decode_path(1, 4, 4, 128, 33, 100, 25, 0) == -4
+
+
+def test_empty_batch_is_a_noop(L):
+    lib = L.load()
+    assert _decode(lib, B=0) == 0
+    assert lib.loki_kv_append(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 2, 128, 32, 64, 0, 4, 1, None) == 0
+    assert lib.loki_kv_append(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 2, 128, 32, 64, 0, 0, 1, None) == 0
+    assert lib.loki_topk(FAKE, 0, 10, 12, 3, FAKE, None) == 0
+
+
+def test_append_rejects_bad_arguments(L):
+    lib = L.load()
+    ap = lambda **kw: lib.loki_kv_append(
+        kw.get("k", FAKE), kw.get("v", FAKE), FAKE, kw.get("ks", FAKE), kw.get("kr", FAKE), FAKE,
+        2, 2, kw.get("D", 128), kw.get("d", 32), kw.get("S_max", 64), kw.get("pos", 0),
+        kw.get("T", 4), kw.get("dt", 1), None)
+    assert ap(pos=62) == -1          # pos + T > S_max
+    assert ap(pos=-1) == -1
+    assert ap(T=-1) == -1
+    assert ap(d=0) == -1
+    assert ap(k=None) == -1
+    assert ap(kr=None) == -1
+    assert ap(ks=FAKE_MIS) == -1
+    assert ap(D=96) == -4
+    assert ap(d=4) == -4
+    assert ap(dt=3) == -1
+
+
+def test_topk_and_scores_reject_bad_arguments(L):
+    lib = L.load()
+    assert lib.loki_topk(FAKE, 3, 10, 9, 3, FAKE, None) == -1      # ld < S
+    assert lib.loki_topk(FAKE, 3, 10, 12, 0, FAKE, None) == -1
+    assert lib.loki_topk(FAKE_MIS, 3, 10, 12, 3, FAKE, None) == -1
+    assert lib.loki_topk(FAKE, 3, 10, 10, 3, FAKE, None) == -1     # ld not a multiple of 4
+    assert lib.loki_scores(FAKE, FAKE, FAKE, 1, 2, 2, 128, 32, 10, 10, 1, FAKE, None, 0, None) == -2
+    assert lib.loki_attend_indices(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, 2, 128, 32, 10, 10, FAKE,
+                                   11, 1, FAKE, FAKE, 1 << 30, None) == -1   # k > S
+    assert lib.loki_dense_decode(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, 2, 128, 32, 10, 10, 1, FAKE,
+                                 FAKE, 16, None) == -2
+
+
+def test_workspace_size_properties(L):
+    lib = L.load()
+    ws = lambda *a: lib.loki_decode_workspace_size(*a)
+    assert ws(0, 4, 128, 100, 10) == 0
+    for args in [(16, 40, 128, 3584, 896), (1, 32, 128, 4096, 1024), (4, 32, 128, 32768, 4096),
+                 (1, 1, 64, 256, 64)]:
+        n = ws(*args)
+        assert n % 256 == 0 and n > 0
+        B, Hq, D, S_max, k = args
+        assert n >= B * Hq * (D + S_max) * 4
+        assert ws(B, Hq, D, S_max, k + 100) >= n
+
+
+def test_calibrate_matches_oracle(L):
+    w = synth.WORKLOADS["l2_7b"]
+    keys = synth.calib_keys(w, 3).astype(np.float32)
+    P, ev = L.calibrate(keys)
+    Po, evo = oracle.calibrate(keys.astype(np.float64))
+    assert np.allclose(ev, evo, rtol=1e-9, atol=1e-12)
+    assert np.max(np.abs(P.astype(np.float64) - Po)) < 1e-6
+    assert np.allclose(P.T.astype(np.float64) @ P, np.eye(w.D), atol=1e-5)
+
+
+def test_calibrate_small_and_degenerate(L):
+    X = np.array([[3, 0, 0], [-3, 0, 0], [0, 2, 0], [0, -2, 0]], dtype=np.float32)
+    P, ev = L.calibrate(X)
+    assert np.allclose(ev, [6.0, 8.0 / 3.0, 0.0], atol=1e-12)
+    assert np.allclose(P, np.eye(3), atol=1e-7)
+    lib = L.load()
+    P1 = np.zeros(1, np.float32)
+    assert lib.loki_calibrate(np.ones(1, np.float32).ctypes.data, 1, 1, P1.ctypes.data, None) == -1
+    assert lib.loki_calibrate(None, 5, 1, P1.ctypes.data, None) == -1
