@@ -77,6 +77,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-run", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="first run a plain device copy of this size (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this implementation runs on a single GPU; --gpus {args.gpus} is not "
@@ -92,6 +94,16 @@ def main():
     loki.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_probe_mib:
+        # a plain copy kernel of known size: its FETCH_SIZE / WRITE_SIZE
+        # counters calibrate the byte counts read for the decode kernel
+        n = args.copy_probe_mib << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     w = synth.WORKLOADS[args.config]
     S = w.S
     k = w.k
@@ -142,13 +154,20 @@ def main():
     out = torch.empty((w.B, w.Hq, w.D), dtype=torch.float32, device=dev)
     idx = torch.empty((w.B, w.Hq, k), dtype=torch.int32, device=dev)
     ws = loki.alloc_workspace(w.B, w.Hq, w.D, S, k, dev)
+    # every (layer, token) combination marshalled once, so the timed loop is
+    # one C call per kernel launch
+    L = len(caches)
+    n_plans = L * R // np.gcd(L, R)
+    app_plans = [loki.AppendPlan(caches[i % L], new_k[i % R], new_v[i % R], Pd, S - 1)
+                 for i in range(n_plans)]
+    dec_plans = [loki.DecodePlan(qs[i % R], caches[i % L], Pd, k, S=S, out=out, idx=idx,
+                                 workspace=ws, path=args.path) for i in range(n_plans)]
 
     def step(i, ev=None):
-        c = caches[i % len(caches)]
-        loki.append(c, new_k[i % R], new_v[i % R], Pd, pos=S - 1)
+        app_plans[i % n_plans]()
         if ev is not None:
             ev[0].record()
-        loki.decode(qs[i % R], c, Pd, k, S=S, out=out, idx=idx, workspace=ws, path=args.path)
+        dec_plans[i % n_plans]()
         if ev is not None:
             ev[1].record()
 
@@ -205,13 +224,15 @@ def main():
     # ---- same-GPU dense baseline on the same caches
     if not args.no_dense:
         dws = loki.alloc_workspace(w.B, w.Hq, w.D, S, 1, dev)
+        dense_plans = [loki.DensePlan(qs[i % R], caches[i % L], Pd, S=S, out=out, workspace=dws)
+                       for i in range(n_plans)]
         for i in range(args.warmup):
-            loki.dense_decode(qs[i % R], caches[i % len(caches)], Pd, S=S, out=out, workspace=dws)
+            dense_plans[i % n_plans]()
         dev_evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                    for _ in range(args.steps)]
         for i in range(args.steps):
             dev_evs[i][0].record()
-            loki.dense_decode(qs[i % R], caches[i % len(caches)], Pd, S=S, out=out, workspace=dws)
+            dense_plans[i % n_plans]()
             dev_evs[i][1].record()
         torch.cuda.synchronize()
         dms = float(np.mean([a.elapsed_time(b) for a, b in dev_evs]))

@@ -274,3 +274,81 @@ def dense_decode(q, cache: KVCache, P, S: int | None = None, out=None, workspace
                                _stream(q))
     _check(st, "loki_dense_decode")
     return out
+
+
+# ------------------------------------------------- pre-marshalled calls --
+
+class DecodePlan:
+    """A decode call with every argument marshalled once, for loops that
+    call loki_decode_ex repeatedly on the same buffers (q may be refilled in
+    place between calls).  The stream is the current stream at creation."""
+
+    def __init__(self, q, cache: KVCache, P, k: int, S: int | None = None, out=None, idx=None,
+                 workspace=None, path: int = PATH_AUTO):
+        torch = _torch()
+        _need(q, "q", cache.dtype)
+        _need(P, "P", torch.float32)
+        B, Hq, D = q.shape
+        S = cache.length if S is None else S
+        kk = min(k, S)
+        self.out = out if out is not None else torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+        self.idx = idx if idx is not None else torch.empty((B, Hq, kk), dtype=torch.int32, device=q.device)
+        if workspace is None and path != PATH_FUSED:
+            workspace = alloc_workspace(B, Hq, D, cache.S_max, kk, q.device)
+        self._keep = (q, cache, P, workspace)
+        wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        self._fn = load().loki_decode_ex
+        self._args = (_ptr(q), _ptr(cache.k_slab), _ptr(cache.k_rest), _ptr(cache.v), _ptr(P),
+                      B, Hq, cache.Hkv, D, cache.d, S, cache.S_max, k, _dtype_code(q),
+                      _ptr(self.out), _ptr(self.idx), _ptr(workspace), wsb, path, _stream(q))
+
+    def __call__(self):
+        st = self._fn(*self._args)
+        if st != LOKI_OK:
+            raise LokiError(st, "loki_decode")
+        return self.out, self.idx
+
+
+class AppendPlan:
+    """An append call marshalled once (fixed source buffers and position)."""
+
+    def __init__(self, cache: KVCache, k_new, v_new, P, pos: int):
+        _need(k_new, "k_new", cache.dtype)
+        _need(v_new, "v_new", cache.dtype)
+        _need(P, "P", _torch().float32)
+        B, Hkv, T, D = k_new.shape
+        self._keep = (cache, k_new, v_new, P)
+        self._fn = load().loki_kv_append
+        self._args = (_ptr(k_new), _ptr(v_new), _ptr(P), _ptr(cache.k_slab), _ptr(cache.k_rest),
+                      _ptr(cache.v), B, Hkv, D, cache.d, cache.S_max, pos, T,
+                      _dtype_code(k_new), _stream(k_new))
+
+    def __call__(self):
+        st = self._fn(*self._args)
+        if st != LOKI_OK:
+            raise LokiError(st, "loki_kv_append")
+
+
+class DensePlan:
+    """A dense-baseline call marshalled once."""
+
+    def __init__(self, q, cache: KVCache, P, S: int | None = None, out=None, workspace=None):
+        torch = _torch()
+        _need(q, "q", cache.dtype)
+        _need(P, "P", torch.float32)
+        B, Hq, D = q.shape
+        S = cache.length if S is None else S
+        self.out = out if out is not None else torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+        if workspace is None:
+            workspace = alloc_workspace(B, Hq, D, cache.S_max, 1, q.device)
+        self._keep = (q, cache, P, workspace)
+        self._fn = load().loki_dense_decode
+        self._args = (_ptr(q), _ptr(cache.k_slab), _ptr(cache.k_rest), _ptr(cache.v), _ptr(P),
+                      B, Hq, cache.Hkv, D, cache.d, S, cache.S_max, _dtype_code(q), _ptr(self.out),
+                      _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(q))
+
+    def __call__(self):
+        st = self._fn(*self._args)
+        if st != LOKI_OK:
+            raise LokiError(st, "loki_dense_decode")
+        return self.out

@@ -4,7 +4,7 @@
 
 #include <algorithm>
 
-#include "../../include/loki.h"
+#include "loki.h"
 #include "launch.hpp"
 
 using loki::DecodeArgs;
@@ -147,7 +147,7 @@ int loki_kv_append(const void* k_new, const void* v_new, const float* P, void* k
   if (!k_new || !v_new) return LOKI_EINVAL;
   int st = check_cache_ptrs(k_slab, k_rest, v, P, D, d);
   if (st != LOKI_OK) return st;
-  if (T > 65535 * 32) return LOKI_EUNSUPPORTED;  // grid.y limit
+  if (Hkv > 65535 || static_cast<int64_t>(B) * T > (1LL << 30)) return LOKI_EUNSUPPORTED;
   return status_of(loki::launch_append(k_new, v_new, P, k_slab, d < D ? k_rest : nullptr, v, B,
                                        Hkv, D, d, S_max, pos, T, dtype,
                                        static_cast<hipStream_t>(stream)));

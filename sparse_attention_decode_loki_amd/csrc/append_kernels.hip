@@ -53,49 +53,73 @@ __device__ __forceinline__ uint16_t round_store<BF16>(double x) {
   return f64_to_bf16_rne(x);
 }
 
-constexpr int kAppendTok = 32;  // tokens per append workgroup
+constexpr int kAppendTok = 8;  // tokens rotated per pass of a workgroup
 
-// Grid (B * Hkv, ceil(T / kAppendTok)).  Each thread keeps one column of
-// P[g] in registers; the workgroup's new keys are staged in LDS as float32
-// [kAppendTok][D] (exact for both types) and read as broadcasts.
+// Grid (nblk, Hkv).  Workgroup (x, g) rotates the tokens of KV head g of every
+// sequence, flattened as n = b * T + t, in chunks of kAppendTok: chunk x,
+// x + nblk, ...  Thread (col, part) keeps rows [part*D/NP, (part+1)*D/NP) of
+// column `col` of P[g] in registers (loaded once per workgroup) and
+// accumulates one float64 partial per token of the chunk (independent
+// chains); the NP partials of each output are then added in a fixed order.
 template <class E, int D>
 __global__ void __launch_bounds__(kBlock) append_kernel(
     const typename E::T* __restrict__ k_new, const typename E::T* __restrict__ v_new,
     const float* __restrict__ P, typename E::T* __restrict__ slab, typename E::T* __restrict__ rest,
-    typename E::T* __restrict__ val, int Hkv, int d, int S_max, int pos, int T) {
-  __shared__ float ks[kAppendTok * D];
-  const int bg = blockIdx.x;
-  const int g = bg % Hkv;
-  const int t0 = blockIdx.y * kAppendTok;
-  const int nt = min(kAppendTok, T - t0);
-  constexpr int NP = kBlock / D;  // tokens rotated at once
+    typename E::T* __restrict__ val, int B, int Hkv, int d, int S_max, int pos, int T) {
+  constexpr int NP = kBlock / D;  // partial sums per output
+  constexpr int R = D / NP;       // rows of P per partial
+  __shared__ float ks[kAppendTok][D];
+  __shared__ double red[NP][kAppendTok][D];
+  const int g = blockIdx.y;
   const int col = threadIdx.x % D;
-  const int sub = threadIdx.x / D;
+  const int part = threadIdx.x / D;
   const int dr = D - d;
+  const int ntok = B * T;
 
-  float pc[D];  // column `col` of P[g]
+  float pc[R];
   const float* Pg = P + static_cast<int64_t>(g) * D * D;
 #pragma unroll
-  for (int m = 0; m < D; ++m) pc[m] = Pg[m * D + col];
-  const int64_t in0 = (static_cast<int64_t>(bg) * T + t0) * D;
-  for (int i = threadIdx.x; i < nt * D; i += kBlock) ks[i] = ld_elem<E>(k_new, in0 + i);
-  __syncthreads();
+  for (int r = 0; r < R; ++r) pc[r] = Pg[(part * R + r) * D + col];
 
-  for (int tt = sub; tt < nt; tt += NP) {
-    double acc = 0.0;
+  for (int n0 = blockIdx.x * kAppendTok; n0 < ntok; n0 += gridDim.x * kAppendTok) {
+    const int nt = min(kAppendTok, ntok - n0);
+    for (int i = threadIdx.x; i < kAppendTok * D; i += kBlock) {
+      const int tt = i / D, c = i % D;
+      float x = 0.f;
+      if (tt < nt) {
+        const int n = n0 + tt, b = n / T, t = n % T;
+        x = ld_elem<E>(k_new, ((static_cast<int64_t>(b) * Hkv + g) * T + t) * D + c);
+      }
+      ks[tt][c] = x;
+    }
+    __syncthreads();
+    double acc[kAppendTok];
 #pragma unroll
-    for (int m = 0; m < D; ++m)
-      acc = fma(static_cast<double>(ks[tt * D + m]), static_cast<double>(pc[m]), acc);
-    const int64_t slot = static_cast<int64_t>(bg) * S_max + pos + t0 + tt;
-    if (col < d)
-      slab[slot * d + col] = round_store<E>(acc);
-    else
-      rest[slot * dr + (col - d)] = round_store<E>(acc);
-  }
-  for (int i = threadIdx.x; i < nt * D; i += kBlock) {
-    const int tt = i / D, c = i % D;
-    const int64_t slot = static_cast<int64_t>(bg) * S_max + pos + t0 + tt;
-    val[slot * D + c] = v_new[in0 + i];
+    for (int tt = 0; tt < kAppendTok; ++tt) acc[tt] = 0.0;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const double pv = static_cast<double>(pc[r]);
+#pragma unroll
+      for (int tt = 0; tt < kAppendTok; ++tt)
+        acc[tt] = fma(static_cast<double>(ks[tt][part * R + r]), pv, acc[tt]);
+    }
+#pragma unroll
+    for (int tt = 0; tt < kAppendTok; ++tt) red[part][tt][col] = acc[tt];
+    __syncthreads();
+    for (int i = threadIdx.x; i < nt * D; i += kBlock) {
+      const int tt = i / D, c = i % D;
+      double x = 0.0;
+#pragma unroll
+      for (int pp = 0; pp < NP; ++pp) x += red[pp][tt][c];
+      const int n = n0 + tt, b = n / T, t = n % T;
+      const int64_t slot = (static_cast<int64_t>(b) * Hkv + g) * S_max + pos + t;
+      if (c < d)
+        slab[slot * d + c] = round_store<E>(x);
+      else
+        rest[slot * dr + (c - d)] = round_store<E>(x);
+      val[slot * D + c] = v_new[((static_cast<int64_t>(b) * Hkv + g) * T + t) * D + c];
+    }
+    __syncthreads();  // ks and red are rewritten by the next chunk
   }
 }
 
@@ -105,11 +129,16 @@ hipError_t append_t(const void* k_new, const void* v_new, const float* P, void* 
                     void* k_rest, void* v, int B, int Hkv, int d, int S_max, int pos, int T,
                     hipStream_t stream) {
   using T_ = typename E::T;
-  dim3 grid(B * Hkv, (T + kAppendTok - 1) / kAppendTok);
+  const int64_t chunks = (static_cast<int64_t>(B) * T + kAppendTok - 1) / kAppendTok;
+  // enough workgroups to fill the chip, each reusing its basis column over
+  // several chunks
+  const int64_t want = (1024 + Hkv - 1) / Hkv;
+  const int nblk = static_cast<int>(chunks < want ? chunks : want);
+  dim3 grid(nblk, Hkv);
   hipLaunchKernelGGL((append_kernel<E, D>), grid, dim3(kBlock), 0, stream,
                      static_cast<const T_*>(k_new), static_cast<const T_*>(v_new), P,
-                     static_cast<T_*>(k_slab), static_cast<T_*>(k_rest), static_cast<T_*>(v), Hkv,
-                     d, S_max, pos, T);
+                     static_cast<T_*>(k_slab), static_cast<T_*>(k_rest), static_cast<T_*>(v), B,
+                     Hkv, d, S_max, pos, T);
   return hipGetLastError();
 }
 }  // namespace

@@ -17,7 +17,7 @@
 #include <numeric>
 #include <vector>
 
-#include "../../include/loki.h"
+#include "loki.h"
 
 namespace {
 

@@ -35,28 +35,34 @@ __device__ __forceinline__ int xcd_logical(int bid, int n) {
 
 // ------------------------------------------------------------------ rotate --
 
-constexpr int kRotQ = 16;  // queries per rotate workgroup
+constexpr int kRotQ = 4;  // queries per rotate workgroup
 
+// Grid (ceil(B*G / kRotQ), Hkv).  Thread t covers columns 4*(t % (D/4)) .. +3
+// of P[g] over a block of rows, loaded as 16-byte chunks (each row of P is
+// read by D/4 consecutive threads, fully coalesced); partial sums over the
+// row blocks are added through LDS.
 template <class E, int D>
 __global__ void __launch_bounds__(kBlock) rotate_kernel(const typename E::T* __restrict__ q,
                                                         const float* __restrict__ P,
                                                         float* __restrict__ qrot, int B, int Hq,
                                                         int Hkv) {
-  constexpr int NP = kBlock / D;  // partial sums per output
-  constexpr int R = D / NP;       // rows of P per partial
+  constexpr int CQ = D / 4;        // column quads
+  constexpr int NRB = kBlock / CQ; // row blocks
+  constexpr int RB = D / NRB;      // rows per block
   __shared__ float qsh[kRotQ][D];
-  __shared__ float red[NP][kRotQ][D];
+  __shared__ float red[NRB][kRotQ][D];
   const int g = blockIdx.y;
   const int G = Hq / Hkv;
   const int n0 = blockIdx.x * kRotQ;
   const int nq = min(kRotQ, B * G - n0);
-  const int col = threadIdx.x % D;
-  const int part = threadIdx.x / D;
+  const int cq = threadIdx.x % CQ;
+  const int rb = threadIdx.x / CQ;
 
-  float p[R];
+  float4 p[RB];
   const float* Pg = P + static_cast<int64_t>(g) * D * D;
 #pragma unroll
-  for (int rr = 0; rr < R; ++rr) p[rr] = Pg[(part * R + rr) * D + col];
+  for (int rr = 0; rr < RB; ++rr)
+    p[rr] = *reinterpret_cast<const float4*>(Pg + (rb * RB + rr) * D + 4 * cq);
 
   for (int e = threadIdx.x; e < nq * D; e += kBlock) {
     const int r = e / D, m = e % D;
@@ -65,10 +71,16 @@ __global__ void __launch_bounds__(kBlock) rotate_kernel(const typename E::T* __r
   }
   __syncthreads();
   for (int r = 0; r < nq; ++r) {
-    float acc = 0.f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-    for (int rr = 0; rr < R; ++rr) acc = fmaf(qsh[r][part * R + rr], p[rr], acc);
-    red[part][r][col] = acc;
+    for (int rr = 0; rr < RB; ++rr) {
+      const float x = qsh[r][rb * RB + rr];
+      acc.x = fmaf(x, p[rr].x, acc.x);
+      acc.y = fmaf(x, p[rr].y, acc.y);
+      acc.z = fmaf(x, p[rr].z, acc.z);
+      acc.w = fmaf(x, p[rr].w, acc.w);
+    }
+    *reinterpret_cast<float4*>(&red[rb][r][4 * cq]) = acc;
   }
   __syncthreads();
   for (int e = threadIdx.x; e < nq * D; e += kBlock) {
@@ -76,7 +88,7 @@ __global__ void __launch_bounds__(kBlock) rotate_kernel(const typename E::T* __r
     const int n = n0 + r, b = n / G, h = g * G + n % G;
     float s = 0.f;
 #pragma unroll
-    for (int pp = 0; pp < NP; ++pp) s += red[pp][r][c];
+    for (int pp = 0; pp < NRB; ++pp) s += red[pp][r][c];
     qrot[(static_cast<int64_t>(b) * Hq + h) * D + c] = s;
   }
 }
@@ -86,22 +98,42 @@ __global__ void __launch_bounds__(kBlock) rotate_kernel(const typename E::T* __r
 // Scores of tokens [j0, j1) for NH heads.  LPS lanes share one token's slab
 // row (d*bytes/16 lanes rounded up to a power of two; lanes past the row
 // idle); a wave covers 64/LPS consecutive tokens per load, so the slab is
-// streamed with fully coalesced 16-byte loads.
+// streamed with fully coalesced 16-byte loads.  score_first issues the first
+// batch of loads, which do not depend on the query, so a caller can start
+// them before the query is rotated.
+template <class E, int LPS, int U>
+__device__ __forceinline__ void score_first(const typename E::T* __restrict__ slab, int d, int j0,
+                                            int j1, Chunk (&c)[U]) {
+  constexpr int VEC = E::VEC;
+  constexpr int TPI = kBlock / LPS;
+  const int part = threadIdx.x % LPS;
+  const int tk = threadIdx.x / LPS;
+  const bool active = part * VEC < d;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int j = j0 + tk + TPI * u;
+    c[u] = (active && j < j1) ? ld16(slab + static_cast<int64_t>(j) * d + part * VEC) : zero_chunk();
+  }
+}
+
+// c holds the first batch (from score_first).
 template <class E, int LPS, int NH, int U, class Write>
 __device__ __forceinline__ void score_loop(const typename E::T* __restrict__ slab, int d, int j0,
-                                           int j1, const float (&qf)[NH][E::VEC], Write write) {
+                                           int j1, const float (&qf)[NH][E::VEC], Write write,
+                                           Chunk (&c)[U]) {
   constexpr int VEC = E::VEC;
   constexpr int TPI = kBlock / LPS;
   const int part = threadIdx.x % LPS;
   const int tk = threadIdx.x / LPS;
   const bool active = part * VEC < d;
   for (int jb = j0 + tk; jb < j1; jb += TPI * U) {
-    Chunk c[U];
+    if (jb != j0 + tk) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int j = jb + TPI * u;
-      c[u] = (active && j < j1) ? ld16(slab + static_cast<int64_t>(j) * d + part * VEC)
-                                : zero_chunk();
+      for (int u = 0; u < U; ++u) {
+        const int j = jb + TPI * u;
+        c[u] = (active && j < j1) ? ld16(slab + static_cast<int64_t>(j) * d + part * VEC)
+                                  : zero_chunk();
+      }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -147,9 +179,11 @@ __global__ void __launch_bounds__(kBlock) score_kernel(const typename E::T* __re
   const int j1 = min(S, j0 + kScoreChunk);
   const typename E::T* sl = slab + static_cast<int64_t>(bg) * S_max * d;
   float* srow = scores + (static_cast<int64_t>(b) * Hq + h0) * S;
+  Chunk c[4];
+  score_first<E, LPS, 4>(sl, d, j0, j1, c);
   score_loop<E, LPS, NH, 4>(sl, d, j0, j1, qf, [&](int h, int j, float s) {
     if (h < nh) srow[static_cast<int64_t>(h) * S + j] = s;
-  });
+  }, c);
 }
 
 // -------------------------------------------------------------------- topk --
@@ -158,7 +192,7 @@ template <int BLOCK>
 __global__ void __launch_bounds__(BLOCK) topk_kernel(const float* __restrict__ scores, int S,
                                                      int64_t ld, int k, int* __restrict__ idx,
                                                      int use_lds) {
-  __shared__ SelectSmem<BLOCK> sm;
+  __shared__ SelectSmemAny<BLOCK> sm;
   extern __shared__ float sbuf[];
   const int row = blockIdx.x;
   const float* s = scores + static_cast<int64_t>(row) * ld;
@@ -170,9 +204,9 @@ __global__ void __launch_bounds__(BLOCK) topk_kernel(const float* __restrict__ s
     for (int i = threadIdx.x; i < n4; i += BLOCK) reinterpret_cast<float4*>(sbuf)[i] = s4[i];
     for (int i = (n4 << 2) + threadIdx.x; i < S; i += BLOCK) sbuf[i] = s[i];
     __syncthreads();
-    block_select_topk<BLOCK>([&](int j) { return sbuf[j]; }, S, k, emit, sm);
+    block_select_topk_any<BLOCK>([&](int j) { return sbuf[j]; }, S, k, emit, sm);
   } else {
-    block_select_topk<BLOCK>([&](int j) { return s[j]; }, S, k, emit, sm);
+    block_select_topk_any<BLOCK>([&](int j) { return s[j]; }, S, k, emit, sm);
   }
 }
 
@@ -298,7 +332,8 @@ __global__ void __launch_bounds__(128) combine_kernel(const float* __restrict__ 
 // One workgroup per (sequence, query head): rotate the query, score the
 // whole slab into LDS, select the top k in LDS, then gather and attend.
 // Dynamic LDS: q' [D] | scores [S] | kept ids [kk].
-template <class E, int D, int LPS>
+// SMALL: S <= 16 * kBlock, so the selection keeps 16 keys per thread.
+template <class E, int D, int LPS, bool SMALL>
 __global__ void __launch_bounds__(kBlock) fused_kernel(
     const typename E::T* __restrict__ q, const typename E::T* __restrict__ slab,
     const typename E::T* __restrict__ rest, const typename E::T* __restrict__ val,
@@ -306,12 +341,14 @@ __global__ void __launch_bounds__(kBlock) fused_kernel(
     int Hkv, int d, int S, int S_max, int kk, float scale_log2) {
   using Gm = Geo<E, D>;
   constexpr int VEC = E::VEC;
-  constexpr int NP = kBlock / D;
-  constexpr int R = D / NP;
+  constexpr int CQ = D / 4;          // column quads of P
+  constexpr int NRB = kBlock / CQ;   // row blocks of P
+  constexpr int RB = D / NRB;        // rows per block
+  constexpr int US = 8;              // slab loads in flight per lane
   union Scratch {
-    SelectSmem<kBlock> sel;
+    SelectSmemAny<kBlock> sel;
     MergeSmem<D, 1, Gm::NG> mrg;
-    float rot[NP][D];
+    float rot[NRB][D];
   };
   __shared__ Scratch sc;
   extern __shared__ float dyn[];
@@ -325,24 +362,35 @@ __global__ void __launch_bounds__(kBlock) fused_kernel(
   const int g = h / G;
   const int64_t row = static_cast<int64_t>(b) * Hq + h;
   const int64_t bgo = static_cast<int64_t>(b) * Hkv + g;
+  const typename E::T* sl = slab + bgo * S_max * d;
 
-  // 1. q' = q . P[g]
+  // 0. the first slab loads do not depend on q': start them now
+  Chunk c[US];
+  score_first<E, LPS, US>(sl, d, 0, S, c);
+
+  // 1. q' = q . P[g]: thread (cq, rb) adds rows [rb*RB, rb*RB + RB) for
+  //    columns 4*cq .. 4*cq + 3, read as 16-byte chunks
   {
-    const int col = threadIdx.x % D, part = threadIdx.x / D;
+    const int cq = threadIdx.x % CQ, rb = threadIdx.x / CQ;
     const float* Pg = P + static_cast<int64_t>(g) * D * D;
     const typename E::T* qr = q + row * D;
-    float acc = 0.f;
-#pragma unroll 8
-    for (int rr = 0; rr < R; ++rr) {
-      const int m = part * R + rr;
-      acc = fmaf(ld_elem<E>(qr, m), Pg[m * D + col], acc);
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int rr = 0; rr < RB; ++rr) {
+      const int m = rb * RB + rr;
+      const float x = ld_elem<E>(qr, m);
+      const float4 p = *reinterpret_cast<const float4*>(Pg + m * D + 4 * cq);
+      acc.x = fmaf(x, p.x, acc.x);
+      acc.y = fmaf(x, p.y, acc.y);
+      acc.z = fmaf(x, p.z, acc.z);
+      acc.w = fmaf(x, p.w, acc.w);
     }
-    sc.rot[part][col] = acc;
+    *reinterpret_cast<float4*>(&sc.rot[rb][4 * cq]) = acc;
     __syncthreads();
     if (threadIdx.x < D) {
       float s = 0.f;
 #pragma unroll
-      for (int pp = 0; pp < NP; ++pp) s += sc.rot[pp][threadIdx.x];
+      for (int pp = 0; pp < NRB; ++pp) s += sc.rot[pp][threadIdx.x];
       qs[threadIdx.x] = s;
     }
     __syncthreads();
@@ -354,20 +402,21 @@ __global__ void __launch_bounds__(kBlock) fused_kernel(
     float qf[1][VEC];
 #pragma unroll
     for (int v = 0; v < VEC; ++v) qf[0][v] = (part * VEC < d) ? qs[part * VEC + v] : 0.f;
-    const typename E::T* sl = slab + bgo * S_max * d;
-    score_loop<E, LPS, 1, 8>(sl, d, 0, S, qf, [&](int, int j, float s) { sb[j] = s; });
+    score_loop<E, LPS, 1, US>(sl, d, 0, S, qf, [&](int, int j, float s) { sb[j] = s; }, c);
   }
   __syncthreads();
 
   // 3. top-k -> LDS and the idx output
   {
     int* irow = idx + row * kk;
-    block_select_topk<kBlock>([&](int j) { return sb[j]; }, S, kk,
-                              [&](int p, int j) {
-                                ib[p] = j;
-                                irow[p] = j;
-                              },
-                              sc.sel);
+    auto emit = [&](int p, int j) {
+      ib[p] = j;
+      irow[p] = j;
+    };
+    if (SMALL)
+      block_select_topk_reg<kBlock, 16>([&](int j) { return sb[j]; }, S, kk, emit, sc.sel.reg);
+    else
+      block_select_topk_any<kBlock>([&](int j) { return sb[j]; }, S, kk, emit, sc.sel);
   }
   __syncthreads();
 
@@ -381,9 +430,8 @@ __global__ void __launch_bounds__(kBlock) fused_kernel(
   acc_init(st[0]);
   const typename E::T* rs = rest ? rest + bgo * S_max * (D - d) : nullptr;
   attend_loop<E, D, 1, true, 4>([&](int t) { return ib[t]; },
-                                [&](int, int, int j) { return sb[j]; }, 0, kk,
-                                slab + bgo * S_max * d, rs, val + bgo * S_max * D, d, qf,
-                                scale_log2, st);
+                                [&](int, int, int j) { return sb[j]; }, 0, kk, sl, rs,
+                                val + bgo * S_max * D, d, qf, scale_log2, st);
   __syncthreads();  // the merge scratch aliases the selection scratch
   merge_groups<E, D, 1>(st, sc.mrg, [&](int, int dim, float, float Ls, float A) {
     out[row * D + dim] = A / Ls;
@@ -485,9 +533,14 @@ hipError_t attend_t(const DecodeArgs& a, const float* qrot, const float* scores,
 template <class E, int D, int LPS>
 hipError_t fused_t(const DecodeArgs& a, int kk, size_t lds) {
   const float scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(D)));
-  hipLaunchKernelGGL((fused_kernel<E, D, LPS>), dim3(a.B * a.Hq), dim3(kBlock), lds, a.stream,
-                     cptr<E>(a.q), cptr<E>(a.k_slab), cptr<E>(a.k_rest), cptr<E>(a.v), a.P, a.out,
-                     a.idx, a.B, a.Hq, a.Hkv, a.d, a.S, a.S_max, kk, scale_log2);
+  if (a.S <= 16 * kBlock)
+    hipLaunchKernelGGL((fused_kernel<E, D, LPS, true>), dim3(a.B * a.Hq), dim3(kBlock), lds,
+                       a.stream, cptr<E>(a.q), cptr<E>(a.k_slab), cptr<E>(a.k_rest), cptr<E>(a.v),
+                       a.P, a.out, a.idx, a.B, a.Hq, a.Hkv, a.d, a.S, a.S_max, kk, scale_log2);
+  else
+    hipLaunchKernelGGL((fused_kernel<E, D, LPS, false>), dim3(a.B * a.Hq), dim3(kBlock), lds,
+                       a.stream, cptr<E>(a.q), cptr<E>(a.k_slab), cptr<E>(a.k_rest), cptr<E>(a.v),
+                       a.P, a.out, a.idx, a.B, a.Hq, a.Hkv, a.d, a.S, a.S_max, kk, scale_log2);
   return hipGetLastError();
 }
 

@@ -116,3 +116,155 @@ __device__ void block_select_topk(Src src, int S, int k, Emit emit, SelectSmem<B
 }
 
 }  // namespace loki
+
+namespace loki {
+
+// Register-resident variant: thread t owns the E = ceil(S / BLOCK)
+// consecutive elements [t*E, t*E + E) and keeps their keys in registers; the
+// radix select uses three digits (11, 11 and 10 bits) on one shared LDS
+// histogram, and the compaction needs a single block-wide scan because each
+// thread's elements are consecutive in index order.  Requires S <= BLOCK*EMAX.
+constexpr int kSelBins = 2048;
+
+template <int BLOCK>
+struct SelectSmemR {
+  static constexpr int NW = BLOCK / 64;
+  unsigned hist[kSelBins];
+  unsigned wsum[2][NW];
+  unsigned bin, above, cnt;
+};
+
+// Exclusive prefix over the block of one value per thread; returns it and
+// the block total in `total`.  Contains one barrier; `buf` selects one of two
+// LDS slots so back-to-back calls need no second barrier.
+template <int BLOCK>
+__device__ __forceinline__ unsigned block_excl_scan(unsigned x, unsigned& total,
+                                                    SelectSmemR<BLOCK>& sm, int buf) {
+  constexpr int NW = BLOCK / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const unsigned incl = wave_incl_scan(x, lane);
+  if (lane == 63) sm.wsum[buf][wave] = incl;
+  __syncthreads();
+  unsigned before = 0u, tot = 0u;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const unsigned s = sm.wsum[buf][w];
+    before += (w < wave) ? s : 0u;
+    tot += s;
+  }
+  total = tot;
+  return before + incl - x;
+}
+
+template <int BLOCK, int EMAX, class Src, class Emit>
+__device__ void block_select_topk_reg(Src src, int S, int k, Emit emit, SelectSmemR<BLOCK>& sm) {
+  constexpr int PER = kSelBins / BLOCK;  // histogram bins owned per thread in the scan
+  static_assert(kSelBins % BLOCK == 0, "bins must split evenly");
+  const int tid = threadIdx.x;
+  const int E = (S + BLOCK - 1) / BLOCK;
+  const int j0 = tid * E;
+  uint32_t key[EMAX];
+#pragma unroll
+  for (int e = 0; e < EMAX; ++e) {
+    const int j = j0 + e;
+    key[e] = (e < E && j < S) ? order_key(src(j)) : 0u;
+  }
+  int nvalid = S - j0;
+  nvalid = nvalid < 0 ? 0 : (nvalid > E ? E : nvalid);
+
+  uint32_t prefix = 0u, mask = 0u;
+  int krem = k;
+  int buf = 0;
+  if (k < S) {
+    const int shifts[3] = {21, 10, 0};
+    const int widths[3] = {11, 11, 10};
+    for (int pass = 0; pass < 3; ++pass) {
+      const int shift = shifts[pass];
+      const uint32_t dmask = (1u << widths[pass]) - 1u;
+      for (int i = tid; i < kSelBins; i += BLOCK) sm.hist[i] = 0u;
+      __syncthreads();
+#pragma unroll
+      for (int e = 0; e < EMAX; ++e)
+        if (e < nvalid && (key[e] & mask) == prefix) atomicAdd(&sm.hist[(key[e] >> shift) & dmask], 1u);
+      __syncthreads();
+      // thread t scans bins (top-down) [kSelBins - PER*(t+1), kSelBins - PER*t)
+      const int hi = kSelBins - PER * tid;
+      unsigned c[PER];
+      unsigned local = 0u;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        c[i] = sm.hist[hi - 1 - i];
+        local += c[i];
+      }
+      unsigned total;
+      unsigned above = block_excl_scan<BLOCK>(local, total, sm, buf);
+      buf ^= 1;
+      if (above < static_cast<unsigned>(krem) && static_cast<unsigned>(krem) <= above + local) {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+          if (above < static_cast<unsigned>(krem) && static_cast<unsigned>(krem) <= above + c[i]) {
+            sm.bin = static_cast<unsigned>(hi - 1 - i);
+            sm.above = above;
+            sm.cnt = c[i];
+          }
+          above += c[i];
+        }
+      }
+      __syncthreads();
+      prefix |= sm.bin << shift;
+      mask |= dmask << shift;
+      krem -= static_cast<int>(sm.above);
+      if (static_cast<int>(sm.cnt) == krem) break;
+    }
+  }
+
+  unsigned ngt = 0u, neq = 0u;
+#pragma unroll
+  for (int e = 0; e < EMAX; ++e) {
+    if (e < nvalid) {
+      const uint32_t m = key[e] & mask;
+      ngt += m > prefix;
+      neq += m == prefix;
+    }
+  }
+  unsigned tot;
+  const unsigned gt_before = block_excl_scan<BLOCK>(ngt, tot, sm, buf);
+  buf ^= 1;
+  unsigned eq_before = block_excl_scan<BLOCK>(neq, tot, sm, buf);
+  int pos = static_cast<int>(gt_before) + min(static_cast<int>(eq_before), krem);
+#pragma unroll
+  for (int e = 0; e < EMAX; ++e) {
+    if (e < nvalid) {
+      const uint32_t m = key[e] & mask;
+      const bool eq = m == prefix;
+      if (m > prefix || (eq && static_cast<int>(eq_before) < krem)) emit(pos++, j0 + e);
+      eq_before += eq;
+    }
+  }
+}
+
+}  // namespace loki
+
+namespace loki {
+
+// LDS for block_select_topk_any (either algorithm).
+template <int BLOCK>
+union SelectSmemAny {
+  SelectSmem<BLOCK> lds;
+  SelectSmemR<BLOCK> reg;
+};
+
+// Top-k with the register-resident select when each thread's share fits in
+// 32 registers, else the LDS/global-resident one.
+template <int BLOCK, class Src, class Emit>
+__device__ __forceinline__ void block_select_topk_any(Src src, int S, int k, Emit emit,
+                                                      SelectSmemAny<BLOCK>& sm) {
+  if (S <= BLOCK * 16)
+    block_select_topk_reg<BLOCK, 16>(src, S, k, emit, sm.reg);
+  else if (S <= BLOCK * 32)
+    block_select_topk_reg<BLOCK, 32>(src, S, k, emit, sm.reg);
+  else
+    block_select_topk<BLOCK>(src, S, k, emit, sm.lds);
+}
+
+}  // namespace loki
