@@ -31,7 +31,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "Loki decode attention: head-queries/s + achieved HBM GB/s (13B shape, S=3584)"
 PEAK_HBM_GBS = 8000.0
-KERNEL_SOURCES = ["device.hpp", "select.hpp", "attend.hpp", "decode_kernels.hip"]
+KERNEL_SOURCES = ["device.hpp", "select.hpp", "attend.hpp", "score.hpp", "fused_kernels.hip"]
 
 
 def kernel_source_hash() -> str:
@@ -56,7 +56,7 @@ def algorithmic_bytes(w, S, k) -> dict:
 def measured_traffic(kernel_hash: str, workload: str):
     """HBM bytes per launch from the committed counter summary, if it was
     taken on the current kernel source; else None."""
-    p = os.path.join(ROOT, "profiles", f"traffic_fused_decode_{workload}.json")
+    p = os.path.join(ROOT, "profiles", f"traffic_fused_decode_step_{workload}.json")
     if not os.path.exists(p):
         return None
     with open(p) as fh:
@@ -155,41 +155,51 @@ def main():
     idx = torch.empty((w.B, w.Hq, k), dtype=torch.int32, device=dev)
     ws = loki.alloc_workspace(w.B, w.Hq, w.D, S, k, dev)
     # every (layer, token) combination marshalled once, so the timed loop is
-    # one C call per kernel launch
+    # one C call per step: loki_decode_step appends the step's token at S-1
+    # and decodes over S tokens
     L = len(caches)
     n_plans = L * R // np.gcd(L, R)
-    app_plans = [loki.AppendPlan(caches[i % L], new_k[i % R], new_v[i % R], Pd, S - 1)
-                 for i in range(n_plans)]
+    new_k2 = [t[:, :, 0].contiguous() for t in new_k]
+    new_v2 = [t[:, :, 0].contiguous() for t in new_v]
+    step_plans = [loki.StepPlan(qs[i % R], new_k2[i % R], new_v2[i % R], caches[i % L], Pd, k,
+                                S - 1, out=out, idx=idx, workspace=ws, path=args.path)
+                  for i in range(n_plans)]
     dec_plans = [loki.DecodePlan(qs[i % R], caches[i % L], Pd, k, S=S, out=out, idx=idx,
                                  workspace=ws, path=args.path) for i in range(n_plans)]
 
-    def step(i, ev=None):
-        app_plans[i % n_plans]()
-        if ev is not None:
-            ev[0].record()
-        dec_plans[i % n_plans]()
-        if ev is not None:
-            ev[1].record()
+    def step(i):
+        step_plans[i % n_plans]()
+
+    def timed(fn, n):
+        """Launch fn n times back to back between two HIP events on the
+        launch stream; returns (wall ms per call, event ms per call)."""
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record()
+        for i in range(n):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        return (t1 - t0) * 1e3 / n, e0.elapsed_time(e1) / n
 
     for i in range(args.warmup):
         step(i)
-    torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(args.warmup + i, evs[i])
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-    dec_ms = np.array([a.elapsed_time(b) for a, b in evs])
-    dec_avg_ms = float(dec_ms.mean())
-    log(f"timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step, decode {dec_avg_ms * 1e3:.1f} us")
+    ms_per_step, step_avg_ms = timed(lambda i: step(args.warmup + i), args.steps)
+    log(f"timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step, events {step_avg_ms * 1e3:.1f} us/launch")
+
+    # decode alone (append excluded, as the pages time it), same caches
+    for i in range(args.warmup):
+        dec_plans[i % n_plans]()
+    _, dec_avg_ms = timed(lambda i: dec_plans[i % n_plans](), args.steps)
+    log(f"decode alone {dec_avg_ms * 1e3:.1f} us/launch")
 
     hq = w.B * w.Hq
     by = algorithmic_bytes(w, S, k)
-    achieved = by["total"] / (dec_avg_ms * 1e-3) / 1e9
+    # the step also reads each sequence's new key/value and writes its cache slot
+    step_bytes = by["total"] + w.B * w.Hkv * (2 * w.D + 2 * w.D) * w.esize
+    achieved = step_bytes / (step_avg_ms * 1e-3) / 1e9
     khash = kernel_source_hash()
     path_name = {1: "fused", 2: "split"}[loki.decode_path(w.B, w.Hq, w.Hkv, w.D, w.d, S, k, args.path)]
     traffic = measured_traffic(khash, args.config) if "fused" in path_name else None
@@ -209,16 +219,19 @@ def main():
         "data": "synthetic: seeded keys with a decaying PCA spectrum, N(0,1) values and queries",
         "config": {"workload": f"{w.name} steady state at S={S}", "B": w.B, "Hq": w.Hq,
                    "Hkv": w.Hkv, "D": w.D, "d": w.d, "S": S, "k": k, "cache_dtype": w.dtype,
-                   "step": "append 1 token/sequence + decode", "path": path_name,
+                   "step": "loki_decode_step: append 1 token/sequence at S-1 + decode over S",
+                   "path": path_name,
                    "layers_cycled": args.layers},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
-                     "kernel": "loki fused decode" if "fused" in path_name else "loki decode (split kernels)",
-                     "algorithmic_bytes_per_launch": by["total"],
-                     "avg_launch_ms": dec_avg_ms, "kernel_source_hash": khash},
+                     "kernel": ("fused decode step (append + decode, one launch)" if "fused" in path_name
+                                else "decode step (split kernels)"),
+                     "algorithmic_bytes_per_launch": step_bytes,
+                     "avg_launch_ms": step_avg_ms,
+                     "timing": "HIP events around the timed region's back-to-back launches",
+                     "kernel_source_hash": khash},
         "decode_only": {"head_queries_per_s": hq / (dec_avg_ms * 1e-3), "avg_ms": dec_avg_ms,
-                        "p10_ms": float(np.percentile(dec_ms, 10)),
-                        "p90_ms": float(np.percentile(dec_ms, 90))},
+                        "achieved_GBs": by["total"] / (dec_avg_ms * 1e-3) / 1e9},
     }
 
     # ---- same-GPU dense baseline on the same caches
@@ -228,58 +241,47 @@ def main():
                        for i in range(n_plans)]
         for i in range(args.warmup):
             dense_plans[i % n_plans]()
-        dev_evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                   for _ in range(args.steps)]
-        for i in range(args.steps):
-            dev_evs[i][0].record()
-            dense_plans[i % n_plans]()
-            dev_evs[i][1].record()
-        torch.cuda.synchronize()
-        dms = float(np.mean([a.elapsed_time(b) for a, b in dev_evs]))
+        _, dms = timed(lambda i: dense_plans[i % n_plans](), args.steps)
         result["dense_baseline"] = {
             "avg_ms": dms, "head_queries_per_s": hq / (dms * 1e-3),
             "achieved_GBs": by["dense"] / (dms * 1e-3) / 1e9,
             "loki_speedup": dms / dec_avg_ms}
         log(f"dense {dms * 1e3:.1f} us, loki speedup {dms / dec_avg_ms:.2f}x")
 
-    # ---- the pages' run: prompt 3072, then 512 x (append 1, decode)
+    # ---- the pages' run: prompt 3072, then 512 x (append 1, decode).  Timed
+    # as whole passes between two events: the fused step (append + decode),
+    # then the appends alone, the decodes alone (append excluded, as the pages
+    # time it) and the dense decodes over the same growing cache lengths.
     if not args.no_run and w.prefill and w.steps:
         run_cache = caches[0]
-        nk = []
+        toks = []
         for st in range(w.steps):
             kn, vn = synth.new_tokens(w, 1000 + st, Qs)
-            nk.append((up(kn), up(vn)))
+            toks.append((up(kn[:, :, 0]), up(vn[:, :, 0]), up(kn), up(vn)))
         idx_flat = torch.empty(hq * k, dtype=torch.int32, device=dev)
-        a_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                for _ in range(w.steps)]
-        d_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                for _ in range(w.steps)]
-        f_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                for _ in range(w.steps)]
-        torch.cuda.synchronize()
-        for st in range(w.steps):
-            Sst = w.prefill + st + 1
-            kst = w.k_at(Sst)
-            a_ev[st][0].record()
-            loki.append(run_cache, nk[st][0], nk[st][1], Pd, pos=Sst - 1)
-            a_ev[st][1].record()
-            d_ev[st][0].record()
-            loki.decode(qs[st % R], run_cache, Pd, kst, S=Sst, out=out,
-                        idx=idx_flat[:hq * kst].view(w.B, w.Hq, kst), workspace=ws, path=args.path)
-            d_ev[st][1].record()
-            if not args.no_dense:
-                f_ev[st][0].record()
-                loki.dense_decode(qs[st % R], run_cache, Pd, S=Sst, out=out, workspace=dws)
-                f_ev[st][1].record()
-        torch.cuda.synchronize()
-        ssum = lambda evl: float(sum(a.elapsed_time(b) for a, b in evl))
-        run = {"prompt": w.prefill, "generated": w.steps,
-               "decode_ms_total": ssum(d_ev), "append_ms_total": ssum(a_ev)}
+        Ss = [w.prefill + st + 1 for st in range(w.steps)]
+        ks = [w.k_at(x) for x in Ss]
+        run_step = [loki.StepPlan(qs[st % R], toks[st][0], toks[st][1], run_cache, Pd, ks[st],
+                                  Ss[st] - 1, out=out, idx=idx_flat[:hq * ks[st]].view(w.B, w.Hq, ks[st]),
+                                  workspace=ws, path=args.path) for st in range(w.steps)]
+        run_app = [loki.AppendPlan(run_cache, toks[st][2], toks[st][3], Pd, Ss[st] - 1)
+                   for st in range(w.steps)]
+        run_dec = [loki.DecodePlan(qs[st % R], run_cache, Pd, ks[st], S=Ss[st], out=out,
+                                   idx=idx_flat[:hq * ks[st]].view(w.B, w.Hq, ks[st]), workspace=ws,
+                                   path=args.path) for st in range(w.steps)]
+        n = w.steps
+        run = {"prompt": w.prefill, "generated": n,
+               "step_ms_total": timed(lambda i: run_step[i](), n)[1] * n,
+               "append_ms_total": timed(lambda i: run_app[i](), n)[1] * n,
+               "decode_ms_total": timed(lambda i: run_dec[i](), n)[1] * n}
         if not args.no_dense:
-            run["dense_ms_total"] = ssum(f_ev)
-            run["loki_speedup_vs_dense"] = run["dense_ms_total"] / run["decode_ms_total"]
+            run_dense = [loki.DensePlan(qs[st % R], run_cache, Pd, S=Ss[st], out=out, workspace=dws)
+                         for st in range(w.steps)]
+            run["dense_ms_total"] = timed(lambda i: run_dense[i](), n)[1] * n
+            run["loki_decode_speedup_vs_dense"] = run["dense_ms_total"] / run["decode_ms_total"]
         result["generation_run"] = run
-        log(f"run: decode {run['decode_ms_total']:.2f} ms, append {run['append_ms_total']:.2f} ms")
+        log(f"run: step {run['step_ms_total']:.2f} ms, decode {run['decode_ms_total']:.2f} ms, "
+            f"append {run['append_ms_total']:.2f} ms")
 
     # ---- CPU oracle on a bounded sample (rank 0, one GPU)
     if not args.no_cpu:

@@ -133,6 +133,23 @@ int loki_decode_ex(const void* q, const void* k_slab, const void* k_rest, const 
                    float* out, int32_t* idx, void* workspace, size_t workspace_bytes,
                    int32_t path, void* stream);
 
+/* One step of a generation loop, in one call: append each sequence's new
+ * key/value at position pos exactly as loki_kv_append does with T = 1, then
+ * decode exactly as loki_decode_ex does over S = pos + 1 tokens.  The pages
+ * time decode with the append excluded ("Key results"); here the append is
+ * folded into the decode launch on the fused path (each workgroup rotates the
+ * new key with the basis it loads for the query, one workgroup per KV head
+ * writes the slot, and the new token's score and rows are taken from LDS
+ * rather than re-read).  The split path runs the append kernel first.
+ *   k_new, v_new  device [B, Hkv, D] dtype (one token per sequence and KV head)
+ *   requires 0 <= pos < S_max; other arguments as loki_decode_ex (the
+ *   workspace rule is the same; the fused path ignores it). */
+int loki_decode_step(const void* q, const void* k_new, const void* v_new, const float* P,
+                     void* k_slab, void* k_rest, void* v, int32_t B, int32_t Hq, int32_t Hkv,
+                     int32_t D, int32_t d, int32_t pos, int32_t S_max, int32_t k, int32_t dtype,
+                     float* out, int32_t* idx, void* workspace, size_t workspace_bytes,
+                     int32_t path, void* stream);
+
 /* The path loki_decode_ex would take for these sizes with `path` (AUTO,
  * FUSED or SPLIT): LOKI_PATH_FUSED or LOKI_PATH_SPLIT, or a negative status
  * for invalid sizes or a FUSED request that does not fit.  Host only. */

@@ -33,6 +33,8 @@ _SIGS = {
                                    _P, _P, _P, ctypes.c_size_t, _P]),
     "loki_decode_ex": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I,
                                       _P, _P, _P, ctypes.c_size_t, _I, _P]),
+    "loki_decode_step": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I,
+                                        _I, _I, _P, _P, _P, ctypes.c_size_t, _I, _P]),
     "loki_decode_path": (ctypes.c_int, [_I, _I, _I, _I, _I, _I, _I, _I]),
     "loki_scores": (ctypes.c_int, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P,
                                    ctypes.c_size_t, _P]),
@@ -198,6 +200,35 @@ def decode(q, cache: KVCache, P, k: int, S: int | None = None, out=None, idx=Non
     return out, idx
 
 
+def decode_step(q, k_new, v_new, cache: KVCache, P, k: int, pos: int | None = None, out=None,
+                idx=None, workspace=None, path: int = PATH_AUTO):
+    """Append k_new/v_new [B, Hkv, D] at `pos` (default: the cache length) and
+    decode over pos + 1 tokens, in one call.  Returns (out, idx)."""
+    torch = _torch()
+    lib = load()
+    _need(q, "q", cache.dtype)
+    _need(k_new, "k_new", cache.dtype)
+    _need(v_new, "v_new", cache.dtype)
+    _need(P, "P", torch.float32)
+    B, Hq, D = q.shape
+    at = cache.length if pos is None else pos
+    kk = min(k, at + 1)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    if idx is None:
+        idx = torch.empty((B, Hq, kk), dtype=torch.int32, device=q.device)
+    if workspace is None and path != PATH_FUSED:
+        workspace = alloc_workspace(B, Hq, D, cache.S_max, kk, q.device)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.loki_decode_step(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(P), _ptr(cache.k_slab),
+                              _ptr(cache.k_rest), _ptr(cache.v), B, Hq, cache.Hkv, D, cache.d, at,
+                              cache.S_max, k, _dtype_code(q), _ptr(out), _ptr(idx),
+                              _ptr(workspace), wsb, path, _stream(q))
+    _check(st, "loki_decode_step")
+    cache.length = max(cache.length, at + 1)
+    return out, idx
+
+
 def decode_path(B, Hq, Hkv, D, d, S, k, path=PATH_AUTO) -> int:
     """The path (PATH_FUSED or PATH_SPLIT) loki_decode_ex takes for these sizes."""
     st = load().loki_decode_path(B, Hq, Hkv, D, d, S, k, path)
@@ -352,3 +383,35 @@ class DensePlan:
         if st != LOKI_OK:
             raise LokiError(st, "loki_dense_decode")
         return self.out
+
+
+class StepPlan:
+    """A decode-step call (append at `pos` + decode over pos + 1 tokens)
+    marshalled once."""
+
+    def __init__(self, q, k_new, v_new, cache: KVCache, P, k: int, pos: int, out=None, idx=None,
+                 workspace=None, path: int = PATH_AUTO):
+        torch = _torch()
+        _need(q, "q", cache.dtype)
+        _need(k_new, "k_new", cache.dtype)
+        _need(v_new, "v_new", cache.dtype)
+        _need(P, "P", torch.float32)
+        B, Hq, D = q.shape
+        kk = min(k, pos + 1)
+        self.out = out if out is not None else torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+        self.idx = idx if idx is not None else torch.empty((B, Hq, kk), dtype=torch.int32, device=q.device)
+        if workspace is None and path != PATH_FUSED:
+            workspace = alloc_workspace(B, Hq, D, cache.S_max, kk, q.device)
+        wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        self._keep = (q, k_new, v_new, cache, P, workspace)
+        self._fn = load().loki_decode_step
+        self._args = (_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(P), _ptr(cache.k_slab),
+                      _ptr(cache.k_rest), _ptr(cache.v), B, Hq, cache.Hkv, D, cache.d, pos,
+                      cache.S_max, k, _dtype_code(q), _ptr(self.out), _ptr(self.idx),
+                      _ptr(workspace), wsb, path, _stream(q))
+
+    def __call__(self):
+        st = self._fn(*self._args)
+        if st != LOKI_OK:
+            raise LokiError(st, "loki_decode_step")
+        return self.out, self.idx

@@ -208,6 +208,42 @@ int loki_decode_ex(const void* q, const void* k_slab, const void* k_rest, const 
   return status_of(e);
 }
 
+int loki_decode_step(const void* q, const void* k_new, const void* v_new, const float* P,
+                     void* k_slab, void* k_rest, void* v, int32_t B, int32_t Hq, int32_t Hkv,
+                     int32_t D, int32_t d, int32_t pos, int32_t S_max, int32_t k, int32_t dtype,
+                     float* out, int32_t* idx, void* workspace, size_t ws_bytes, int32_t path,
+                     void* stream) {
+  if (pos < 0) return LOKI_EINVAL;
+  const int S = pos + 1;
+  int st = check_shape(B, Hq, Hkv, D, d, S, S_max, dtype);
+  if (st != LOKI_OK) return st;
+  if (k < 1) return LOKI_EINVAL;
+  if (path != LOKI_PATH_AUTO && path != LOKI_PATH_FUSED && path != LOKI_PATH_SPLIT)
+    return LOKI_EINVAL;
+  if (B == 0) return LOKI_OK;
+  if (!q || !k_new || !v_new || !out || !idx) return LOKI_EINVAL;
+  st = check_cache_ptrs(k_slab, k_rest, v, P, D, d);
+  if (st != LOKI_OK) return st;
+  if (!aligned16(out) || (reinterpret_cast<uintptr_t>(idx) & 3u)) return LOKI_EINVAL;
+  const int kk = std::min(k, S);
+  const bool fused = path == LOKI_PATH_FUSED ||
+                     (path == LOKI_PATH_AUTO && auto_fused(B, Hq, Hkv, D, S, kk));
+  DecodeArgs a = make_args(q, k_slab, k_rest, v, P, B, Hq, Hkv, D, d, S, S_max, dtype, out, idx,
+                           stream);
+  if (fused) {
+    if (!fused_fits(D, S, kk)) return LOKI_EUNSUPPORTED;
+    return status_of(loki::launch_fused_step(a, k_new, v_new, pos, kk));
+  }
+  const int nsplit = sparse_nsplit(B * Hq, kk);
+  const Layout L = layout(B, Hq, D, S_max, nsplit);
+  if (!workspace || ws_bytes < L.total || !aligned16(workspace)) return LOKI_EWORKSPACE;
+  hipError_t e = loki::launch_append(k_new, v_new, P, k_slab, d < D ? k_rest : nullptr, v, B, Hkv,
+                                     D, d, S_max, pos, 1, dtype, a.stream);
+  if (e != hipSuccess) return LOKI_EDEVICE;
+  return loki_decode_ex(q, k_slab, k_rest, v, P, B, Hq, Hkv, D, d, S, S_max, k, dtype, out, idx,
+                        workspace, ws_bytes, LOKI_PATH_SPLIT, stream);
+}
+
 int loki_decode(const void* q, const void* k_slab, const void* k_rest, const void* v,
                 const float* P, int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t d,
                 int32_t S, int32_t S_max, int32_t k, int32_t dtype, float* out, int32_t* idx,

@@ -13,46 +13,6 @@
 
 namespace loki {
 
-// float64 -> bf16 bits, round to nearest, ties to even, done on the bit
-// pattern so that there is a single rounding.
-__device__ __forceinline__ uint16_t f64_to_bf16_rne(double x) {
-  const uint64_t u = static_cast<uint64_t>(__double_as_longlong(x));
-  const uint32_t sign = static_cast<uint32_t>(u >> 63) << 15;
-  const int e = static_cast<int>((u >> 52) & 0x7ffu);
-  const uint64_t m = u & ((1ull << 52) - 1);
-  if (e == 0x7ff) return static_cast<uint16_t>(sign | 0x7f80u | (m ? 0x40u : 0u));
-  if (e == 0) return static_cast<uint16_t>(sign);  // |x| < 2^-1022 rounds to zero
-  int E = e - 1023 + 127;                          // bf16 biased exponent
-  const uint64_t sig = (1ull << 52) | m;           // 53-bit significand
-  int shift = 45;                                  // keep 8 significant bits
-  if (E < 1) {                                     // bf16 subnormal range
-    shift += 1 - E;
-    E = 0;
-    if (shift > 54) return static_cast<uint16_t>(sign);
-  }
-  uint64_t keep = sig >> shift;
-  const uint64_t rem = sig & ((1ull << shift) - 1);
-  const uint64_t half = 1ull << (shift - 1);
-  if (rem > half || (rem == half && (keep & 1ull))) ++keep;
-  uint32_t bits = (E == 0) ? static_cast<uint32_t>(keep)
-                           : (static_cast<uint32_t>(E) << 7) + static_cast<uint32_t>(keep - 128);
-  if (bits >= 0x7f80u) bits = 0x7f80u;  // overflow -> infinity
-  return static_cast<uint16_t>(sign | bits);
-}
-
-template <class E>
-__device__ __forceinline__ typename E::T round_store(double x);
-
-template <>
-__device__ __forceinline__ float round_store<F32>(double x) {
-  return static_cast<float>(x);  // round to nearest even
-}
-
-template <>
-__device__ __forceinline__ uint16_t round_store<BF16>(double x) {
-  return f64_to_bf16_rne(x);
-}
-
 constexpr int kAppendTok = 8;  // tokens rotated per pass of a workgroup
 
 // Grid (nblk, Hkv).  Workgroup (x, g) rotates the tokens of KV head g of every

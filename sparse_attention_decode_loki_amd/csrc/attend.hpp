@@ -46,13 +46,17 @@ __device__ __forceinline__ void acc_init(Acc<VEC>& s) {
 //   in [d, D) load the key (from k_rest).  DENSE: every lane loads its key
 //   chunk from k_slab or k_rest.
 // qf[h][v] = q'_h[lane_dim0 + v] (zero where the lane's dims come from get_s).
+// Token jo (if >= 0) is not read from the cache: its rotated key row
+// [slab | rest] and value row are taken from ko / vo (LDS, storage format).
 template <class E, int D, int NH, bool SPARSE, int U, class GetJ, class GetS>
 __device__ __forceinline__ void attend_loop(GetJ get_j, GetS get_s, int t0, int t1,
                                             const typename E::T* __restrict__ slab,
                                             const typename E::T* __restrict__ rest,
                                             const typename E::T* __restrict__ val, int d,
                                             const float (&qf)[NH][E::VEC], float scale_log2,
-                                            Acc<E::VEC> (&st)[NH]) {
+                                            Acc<E::VEC> (&st)[NH], int jo = -1,
+                                            const typename E::T* ko = nullptr,
+                                            const typename E::T* vo = nullptr) {
   using G = Geo<E, D>;
   constexpr int VEC = G::VEC;
   constexpr int LPV = G::LPV;
@@ -79,8 +83,17 @@ __device__ __forceinline__ void attend_loop(GetJ get_j, GetS get_s, int t0, int 
     for (int u = 0; u < U; ++u) {
       const int64_t jj = j[u];
       const typename E::T* kp = in_rest ? rest + jj * dr + (kd0 - d) : slab + jj * d + kd0;
-      kc[u] = (ok[u] && kload) ? ld16(kp) : zero_chunk();
-      vc[u] = ok[u] ? ld16(val + jj * D + kd0) : zero_chunk();
+      kc[u] = zero_chunk();
+      vc[u] = zero_chunk();
+      if (ok[u]) {
+        if (j[u] != jo) {  // separate branches keep each load's address space known
+          if (kload) kc[u] = ld16_stream(kp);
+          vc[u] = ld16_stream(val + jj * D + kd0);
+        } else {
+          if (kload) kc[u] = ld16(ko + kd0);
+          vc[u] = ld16(vo + kd0);
+        }
+      }
     }
     if (SPARSE) {
 #pragma unroll

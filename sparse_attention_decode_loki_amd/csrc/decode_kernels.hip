@@ -15,23 +15,13 @@
 //   attend_kernel   gather + online softmax over a slice of the kept tokens
 //                   (also the dense baseline, with all tokens)
 //   combine_kernel  log-sum-exp merge of the slices
-//   fused_kernel    one workgroup per (sequence, query head) doing all of
-//                   the above with the scores and indices held in LDS
+// The single-kernel path (fused_kernel) is in fused_kernels.hip.
 #include "launch.hpp"
 #include "attend.hpp"
+#include "score.hpp"
 #include "select.hpp"
 
 namespace loki {
-
-// ----------------------------------------------------------------- helpers --
-
-// Workgroup id -> logical id such that consecutive logical ids land on the
-// same XCD (workgroups are dealt round-robin over the 8 XCDs), so the
-// sequences of one head share that head's basis in one L2.
-__device__ __forceinline__ int xcd_logical(int bid, int n) {
-  if ((n & 7) != 0) return bid;
-  return (bid & 7) * (n >> 3) + (bid >> 3);
-}
 
 // ------------------------------------------------------------------ rotate --
 
@@ -94,63 +84,6 @@ __global__ void __launch_bounds__(kBlock) rotate_kernel(const typename E::T* __r
 }
 
 // ------------------------------------------------------------------- score --
-
-// Scores of tokens [j0, j1) for NH heads.  LPS lanes share one token's slab
-// row (d*bytes/16 lanes rounded up to a power of two; lanes past the row
-// idle); a wave covers 64/LPS consecutive tokens per load, so the slab is
-// streamed with fully coalesced 16-byte loads.  score_first issues the first
-// batch of loads, which do not depend on the query, so a caller can start
-// them before the query is rotated.
-template <class E, int LPS, int U>
-__device__ __forceinline__ void score_first(const typename E::T* __restrict__ slab, int d, int j0,
-                                            int j1, Chunk (&c)[U]) {
-  constexpr int VEC = E::VEC;
-  constexpr int TPI = kBlock / LPS;
-  const int part = threadIdx.x % LPS;
-  const int tk = threadIdx.x / LPS;
-  const bool active = part * VEC < d;
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int j = j0 + tk + TPI * u;
-    c[u] = (active && j < j1) ? ld16(slab + static_cast<int64_t>(j) * d + part * VEC) : zero_chunk();
-  }
-}
-
-// c holds the first batch (from score_first).
-template <class E, int LPS, int NH, int U, class Write>
-__device__ __forceinline__ void score_loop(const typename E::T* __restrict__ slab, int d, int j0,
-                                           int j1, const float (&qf)[NH][E::VEC], Write write,
-                                           Chunk (&c)[U]) {
-  constexpr int VEC = E::VEC;
-  constexpr int TPI = kBlock / LPS;
-  const int part = threadIdx.x % LPS;
-  const int tk = threadIdx.x / LPS;
-  const bool active = part * VEC < d;
-  for (int jb = j0 + tk; jb < j1; jb += TPI * U) {
-    if (jb != j0 + tk) {
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int j = jb + TPI * u;
-        c[u] = (active && j < j1) ? ld16(slab + static_cast<int64_t>(j) * d + part * VEC)
-                                  : zero_chunk();
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      float x[VEC];
-      unpack<E>(c[u], x);
-      const int j = jb + TPI * u;
-#pragma unroll
-      for (int h = 0; h < NH; ++h) {
-        float dot = 0.f;
-#pragma unroll
-        for (int v = 0; v < VEC; ++v) dot = fmaf(qf[h][v], x[v], dot);
-        dot = group_sum<LPS>(dot);
-        if (part == 0 && j < j1) write(h, j, dot);
-      }
-    }
-  }
-}
 
 constexpr int kScoreChunk = 1024;  // tokens per score workgroup
 
@@ -327,117 +260,6 @@ __global__ void __launch_bounds__(128) combine_kernel(const float* __restrict__ 
   }
 }
 
-// ------------------------------------------------------------------- fused --
-
-// One workgroup per (sequence, query head): rotate the query, score the
-// whole slab into LDS, select the top k in LDS, then gather and attend.
-// Dynamic LDS: q' [D] | scores [S] | kept ids [kk].
-// SMALL: S <= 16 * kBlock, so the selection keeps 16 keys per thread.
-template <class E, int D, int LPS, bool SMALL>
-__global__ void __launch_bounds__(kBlock) fused_kernel(
-    const typename E::T* __restrict__ q, const typename E::T* __restrict__ slab,
-    const typename E::T* __restrict__ rest, const typename E::T* __restrict__ val,
-    const float* __restrict__ P, float* __restrict__ out, int* __restrict__ idx, int B, int Hq,
-    int Hkv, int d, int S, int S_max, int kk, float scale_log2) {
-  using Gm = Geo<E, D>;
-  constexpr int VEC = E::VEC;
-  constexpr int CQ = D / 4;          // column quads of P
-  constexpr int NRB = kBlock / CQ;   // row blocks of P
-  constexpr int RB = D / NRB;        // rows per block
-  constexpr int US = 8;              // slab loads in flight per lane
-  union Scratch {
-    SelectSmemAny<kBlock> sel;
-    MergeSmem<D, 1, Gm::NG> mrg;
-    float rot[NRB][D];
-  };
-  __shared__ Scratch sc;
-  extern __shared__ float dyn[];
-  float* qs = dyn;
-  float* sb = dyn + D;
-  int* ib = reinterpret_cast<int*>(dyn + D + S);
-
-  const int L = xcd_logical(blockIdx.x, gridDim.x);
-  const int h = L / B, b = L % B;
-  const int G = Hq / Hkv;
-  const int g = h / G;
-  const int64_t row = static_cast<int64_t>(b) * Hq + h;
-  const int64_t bgo = static_cast<int64_t>(b) * Hkv + g;
-  const typename E::T* sl = slab + bgo * S_max * d;
-
-  // 0. the first slab loads do not depend on q': start them now
-  Chunk c[US];
-  score_first<E, LPS, US>(sl, d, 0, S, c);
-
-  // 1. q' = q . P[g]: thread (cq, rb) adds rows [rb*RB, rb*RB + RB) for
-  //    columns 4*cq .. 4*cq + 3, read as 16-byte chunks
-  {
-    const int cq = threadIdx.x % CQ, rb = threadIdx.x / CQ;
-    const float* Pg = P + static_cast<int64_t>(g) * D * D;
-    const typename E::T* qr = q + row * D;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-    for (int rr = 0; rr < RB; ++rr) {
-      const int m = rb * RB + rr;
-      const float x = ld_elem<E>(qr, m);
-      const float4 p = *reinterpret_cast<const float4*>(Pg + m * D + 4 * cq);
-      acc.x = fmaf(x, p.x, acc.x);
-      acc.y = fmaf(x, p.y, acc.y);
-      acc.z = fmaf(x, p.z, acc.z);
-      acc.w = fmaf(x, p.w, acc.w);
-    }
-    *reinterpret_cast<float4*>(&sc.rot[rb][4 * cq]) = acc;
-    __syncthreads();
-    if (threadIdx.x < D) {
-      float s = 0.f;
-#pragma unroll
-      for (int pp = 0; pp < NRB; ++pp) s += sc.rot[pp][threadIdx.x];
-      qs[threadIdx.x] = s;
-    }
-    __syncthreads();
-  }
-
-  // 2. ranking scores of all S tokens -> LDS
-  {
-    const int part = threadIdx.x % LPS;
-    float qf[1][VEC];
-#pragma unroll
-    for (int v = 0; v < VEC; ++v) qf[0][v] = (part * VEC < d) ? qs[part * VEC + v] : 0.f;
-    score_loop<E, LPS, 1, US>(sl, d, 0, S, qf, [&](int, int j, float s) { sb[j] = s; }, c);
-  }
-  __syncthreads();
-
-  // 3. top-k -> LDS and the idx output
-  {
-    int* irow = idx + row * kk;
-    auto emit = [&](int p, int j) {
-      ib[p] = j;
-      irow[p] = j;
-    };
-    if (SMALL)
-      block_select_topk_reg<kBlock, 16>([&](int j) { return sb[j]; }, S, kk, emit, sc.sel.reg);
-    else
-      block_select_topk_any<kBlock>([&](int j) { return sb[j]; }, S, kk, emit, sc.sel);
-  }
-  __syncthreads();
-
-  // 4. gather + exact attention over the kept tokens
-  const int r = threadIdx.x % Gm::LPV;
-  const int kd0 = r * VEC;
-  float qf[1][VEC];
-#pragma unroll
-  for (int v = 0; v < VEC; ++v) qf[0][v] = (kd0 >= d) ? qs[kd0 + v] : 0.f;
-  Acc<VEC> st[1];
-  acc_init(st[0]);
-  const typename E::T* rs = rest ? rest + bgo * S_max * (D - d) : nullptr;
-  attend_loop<E, D, 1, true, 4>([&](int t) { return ib[t]; },
-                                [&](int, int, int j) { return sb[j]; }, 0, kk, sl, rs,
-                                val + bgo * S_max * D, d, qf, scale_log2, st);
-  __syncthreads();  // the merge scratch aliases the selection scratch
-  merge_groups<E, D, 1>(st, sc.mrg, [&](int, int dim, float, float Ls, float A) {
-    out[row * D + dim] = A / Ls;
-  });
-}
-
 // --------------------------------------------------------------- launchers --
 
 namespace {
@@ -530,32 +352,6 @@ hipError_t attend_t(const DecodeArgs& a, const float* qrot, const float* scores,
   return hipGetLastError();
 }
 
-template <class E, int D, int LPS>
-hipError_t fused_t(const DecodeArgs& a, int kk, size_t lds) {
-  const float scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(D)));
-  if (a.S <= 16 * kBlock)
-    hipLaunchKernelGGL((fused_kernel<E, D, LPS, true>), dim3(a.B * a.Hq), dim3(kBlock), lds,
-                       a.stream, cptr<E>(a.q), cptr<E>(a.k_slab), cptr<E>(a.k_rest), cptr<E>(a.v),
-                       a.P, a.out, a.idx, a.B, a.Hq, a.Hkv, a.d, a.S, a.S_max, kk, scale_log2);
-  else
-    hipLaunchKernelGGL((fused_kernel<E, D, LPS, false>), dim3(a.B * a.Hq), dim3(kBlock), lds,
-                       a.stream, cptr<E>(a.q), cptr<E>(a.k_slab), cptr<E>(a.k_rest), cptr<E>(a.v),
-                       a.P, a.out, a.idx, a.B, a.Hq, a.Hkv, a.d, a.S, a.S_max, kk, scale_log2);
-  return hipGetLastError();
-}
-
-template <class E, int D>
-hipError_t fused_lps(const DecodeArgs& a, int kk, size_t lds) {
-  switch (lps_for(a.d, E::VEC)) {
-    case 1: return fused_t<E, D, 1>(a, kk, lds);
-    case 2: return fused_t<E, D, 2>(a, kk, lds);
-    case 4: return fused_t<E, D, 4>(a, kk, lds);
-    case 8: return fused_t<E, D, 8>(a, kk, lds);
-    case 16: return fused_t<E, D, 16>(a, kk, lds);
-    default: return fused_t<E, D, 32>(a, kk, lds);
-  }
-}
-
 }  // namespace
 
 hipError_t launch_rotate(const DecodeArgs& a, float* qrot) {
@@ -601,16 +397,6 @@ hipError_t launch_attend(const DecodeArgs& a, const float* qrot, const float* sc
                   : attend_t<BF16, 64, false>(a, qrot, scores, idx, kk, part, nsplit);
   return sparse ? attend_t<BF16, 128, true>(a, qrot, scores, idx, kk, part, nsplit)
                 : attend_t<BF16, 128, false>(a, qrot, scores, idx, kk, part, nsplit);
-}
-
-size_t fused_lds_bytes(int D, int S, int kk) {
-  return (static_cast<size_t>(D) + S + kk) * sizeof(float);
-}
-
-hipError_t launch_fused(const DecodeArgs& a, int kk) {
-  const size_t lds = fused_lds_bytes(a.D, a.S, kk);
-  if (a.dtype == kF32) return a.D == 64 ? fused_lps<F32, 64>(a, kk, lds) : fused_lps<F32, 128>(a, kk, lds);
-  return a.D == 64 ? fused_lps<BF16, 64>(a, kk, lds) : fused_lps<BF16, 128>(a, kk, lds);
 }
 
 }  // namespace loki

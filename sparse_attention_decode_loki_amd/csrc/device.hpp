@@ -38,6 +38,17 @@ __device__ __forceinline__ Chunk ld16(const void* p) {
   return c;
 }
 
+// 16-byte load of data read once per launch (key slab stream, gathered key
+// and value rows): marked nontemporal, so it does not displace reused lines
+// from the caches.
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ Chunk ld16_stream(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  Chunk c;
+  c.u = make_uint4(v.x, v.y, v.z, v.w);
+  return c;
+}
+
 __device__ __forceinline__ Chunk zero_chunk() {
   Chunk c;
   c.u = make_uint4(0u, 0u, 0u, 0u);
@@ -79,23 +90,51 @@ __device__ __forceinline__ float ld_elem<BF16>(const uint16_t* p, int64_t i) {
   return __uint_as_float(static_cast<uint32_t>(p[i]) << 16);
 }
 
+// Data-parallel-primitive (DPP) lane moves.  dpp<CTRL, ROW_MASK, BANK_MASK>
+// returns, per lane, the value of the lane selected by CTRL within its row of
+// 16 lanes; lanes whose source is out of range, or that the masks disable,
+// get 0.  Controls used: quad_perm [1,0,3,2] (0xB1) and [2,3,0,1] (0x4E),
+// row_shr:n (0x110 + n), row_mirror (0x140), row_half_mirror (0x141),
+// row_bcast:15 (0x142), row_bcast:31 (0x143).
+template <int CTRL, int ROW_MASK = 0xf, int BANK_MASK = 0xf>
+__device__ __forceinline__ unsigned dpp_u(unsigned v) {
+  return static_cast<unsigned>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, ROW_MASK, BANK_MASK, true));
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, true));
+}
+
 // Sum over aligned groups of W consecutive lanes (W a power of two <= 64);
-// every lane of the group receives the group total.
+// every lane of the group receives the group total.  Within a row of 16 the
+// butterfly uses DPP (quad swaps, then half-row and row mirrors, which pair
+// each lane with one holding the complementary partial sum); wider groups
+// cross rows with lane shuffles.
 template <int W>
 __device__ __forceinline__ float group_sum(float x) {
-#pragma unroll
-  for (int off = W / 2; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+  if (W >= 2) x += dpp_f<0xB1>(x);
+  if (W >= 4) x += dpp_f<0x4E>(x);
+  if (W >= 8) x += dpp_f<0x141>(x);
+  if (W >= 16) x += dpp_f<0x140>(x);
+  if (W >= 32) x += __shfl_xor(x, 16, 64);
+  if (W >= 64) x += __shfl_xor(x, 32, 64);
   return x;
 }
 
-// Inclusive prefix sum over the 64 lanes of a wave.
-__device__ __forceinline__ unsigned wave_incl_scan(unsigned x, int lane) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    unsigned y = __shfl_up(x, off, 64);
-    if (lane >= off) x += y;
-  }
-  return x;
+// Inclusive prefix sum over the 64 lanes of a wave: prefix within rows of 16
+// from shifted copies (shifts 1-3 of the input, then 4 and 8 of the partial
+// result on the upper banks), then row totals broadcast to the later rows.
+__device__ __forceinline__ unsigned wave_incl_scan(unsigned x, int /*lane*/) {
+  unsigned v = x;
+  v += dpp_u<0x111>(x);
+  v += dpp_u<0x112>(x);
+  v += dpp_u<0x113>(x);
+  v += dpp_u<0x114, 0xf, 0xe>(v);
+  v += dpp_u<0x118, 0xf, 0xc>(v);
+  v += dpp_u<0x142, 0xa, 0xf>(v);
+  v += dpp_u<0x143, 0xc, 0xf>(v);
+  return v;
 }
 
 // Number of set bits of `m` in lanes below this one.
@@ -112,5 +151,45 @@ __device__ __forceinline__ uint32_t order_key(float x) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// float64 -> bf16 bits, round to nearest, ties to even, done on the bit
+// pattern so that there is a single rounding.
+__device__ __forceinline__ uint16_t f64_to_bf16_rne(double x) {
+  const uint64_t u = static_cast<uint64_t>(__double_as_longlong(x));
+  const uint32_t sign = static_cast<uint32_t>(u >> 63) << 15;
+  const int e = static_cast<int>((u >> 52) & 0x7ffu);
+  const uint64_t m = u & ((1ull << 52) - 1);
+  if (e == 0x7ff) return static_cast<uint16_t>(sign | 0x7f80u | (m ? 0x40u : 0u));
+  if (e == 0) return static_cast<uint16_t>(sign);  // |x| < 2^-1022 rounds to zero
+  int E = e - 1023 + 127;                          // bf16 biased exponent
+  const uint64_t sig = (1ull << 52) | m;           // 53-bit significand
+  int shift = 45;                                  // keep 8 significant bits
+  if (E < 1) {                                     // bf16 subnormal range
+    shift += 1 - E;
+    E = 0;
+    if (shift > 54) return static_cast<uint16_t>(sign);
+  }
+  uint64_t keep = sig >> shift;
+  const uint64_t rem = sig & ((1ull << shift) - 1);
+  const uint64_t half = 1ull << (shift - 1);
+  if (rem > half || (rem == half && (keep & 1ull))) ++keep;
+  uint32_t bits = (E == 0) ? static_cast<uint32_t>(keep)
+                           : (static_cast<uint32_t>(E) << 7) + static_cast<uint32_t>(keep - 128);
+  if (bits >= 0x7f80u) bits = 0x7f80u;  // overflow -> infinity
+  return static_cast<uint16_t>(sign | bits);
+}
+
+template <class E>
+__device__ __forceinline__ typename E::T round_store(double x);
+
+template <>
+__device__ __forceinline__ float round_store<F32>(double x) {
+  return static_cast<float>(x);  // round to nearest even
+}
+
+template <>
+__device__ __forceinline__ uint16_t round_store<BF16>(double x) {
+  return f64_to_bf16_rne(x);
+}
 
 }  // namespace loki

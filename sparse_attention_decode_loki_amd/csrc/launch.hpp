@@ -37,6 +37,9 @@ hipError_t launch_attend(const DecodeArgs& a, const float* qrot, const float* sc
                          const int* idx, int kk, float* part, int nsplit, bool sparse);
 size_t fused_lds_bytes(int D, int S, int kk);
 hipError_t launch_fused(const DecodeArgs& a, int kk);
+// append (k_new, v_new [B, Hkv, D]) at pos and decode over a.S = pos + 1
+hipError_t launch_fused_step(const DecodeArgs& a, const void* k_new, const void* v_new, int pos,
+                             int kk);
 
 hipError_t launch_append(const void* k_new, const void* v_new, const float* P, void* k_slab,
                          void* k_rest, void* v, int B, int Hkv, int D, int d, int S_max, int pos,

@@ -249,3 +249,102 @@ def test_full_size_decode_sampled(lib, name):
     assert np.all(np.diff(idx.astype(np.int64), axis=-1) > 0)
     assert idx.min() >= 0 and idx.max() < w.S
     assert np.all(np.isfinite(out))
+
+
+# ------------------------------------------------------- decode step (fused append) --
+
+STEP_CASES = {
+    "step_mha": synth.custom("step_mha", 301, B=2, Hq=4, Hkv=4, S=700),
+    "step_gqa": synth.custom("step_gqa", 302, B=2, Hq=8, Hkv=2, S=1000),
+    "step_f32": synth.custom("step_f32", 303, B=1, Hq=2, Hkv=2, D=64, d=16, S=300, dtype="f32",
+                             tau=8.0),
+    "step_first": synth.custom("step_first", 304, B=2, Hq=2, Hkv=2, S=1),
+}
+
+
+def _oracle_token(w, P, kn, vn):
+    """The oracle's cache rows for the step's token: [B, Hkv, 1, ...]."""
+    st = np.uint16 if w.dtype == "bf16" else np.float32
+    slab = np.empty((w.B, w.Hkv, 1, w.d), st)
+    rest = np.empty((w.B, w.Hkv, 1, w.D - w.d), st)
+    vv = np.empty((w.B, w.Hkv, 1, w.D), st)
+    for g in range(w.Hkv):
+        slab[:, g], rest[:, g], vv[:, g] = oracle.append(
+            oracle.to_f64(kn[:, g], w.dtype), oracle.to_f64(vn[:, g], w.dtype),
+            P[g].astype(np.float64), w.d, w.dtype)
+    return slab, rest, vv
+
+
+@pytest.mark.parametrize("path", [1, 2], ids=["fused", "split"])
+@pytest.mark.parametrize("name", sorted(STEP_CASES))
+def test_decode_step_matches_oracle(lib, name, path):
+    """Append at pos = S-1 and decode over S tokens in one call; the written
+    slot equals the oracle's append and the decode equals the oracle's decode
+    over the oracle's full cache."""
+    w = STEP_CASES[name]
+    S = w.S
+    c = make_case(w, S - 1, S + 3) if S > 1 else None
+    from gpu_cases import basis
+    P = basis(w) if c is None else c.P
+    kn, vn = synth.new_tokens(w, 7)            # [B, Hkv, 1, D]
+    o_slab, o_rest, o_v = _oracle_token(w, P, kn, vn)
+    st = np.uint16 if w.dtype == "bf16" else np.float32
+    full = {}
+    for nm, tok, width in (("slab", o_slab, w.d), ("rest", o_rest, w.D - w.d), ("v", o_v, w.D)):
+        arr = np.zeros((w.B, w.Hkv, S + 3, width), st)
+        if c is not None:
+            arr[:, :, :S - 1] = getattr(c, nm)[:, :, :S - 1]
+        arr[:, :, S - 1] = tok[:, :, 0]
+        full[nm] = arr
+    import torch
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    cache = lib.KVCache(w.B, w.Hkv, S + 3, w.D, w.d, tdt)
+    if c is not None:
+        cache.k_slab[:, :, :S - 1].copy_(to_dev(c.slab[:, :, :S - 1], w.dtype))
+        if w.d < w.D:
+            cache.k_rest[:, :, :S - 1].copy_(to_dev(c.rest[:, :, :S - 1], w.dtype))
+        cache.v[:, :, :S - 1].copy_(to_dev(c.v[:, :, :S - 1], w.dtype))
+    cache.length = S - 1
+    q = synth.queries(w, step=7)
+    k = w.k_at(S)
+    out, idx = lib.decode_step(to_dev(q, w.dtype), to_dev(kn[:, :, 0], w.dtype),
+                               to_dev(vn[:, :, 0], w.dtype), cache, to_dev(P, "f32"), k,
+                               pos=S - 1, path=path)
+    torch.cuda.synchronize()
+    # the written slot
+    for nm, t in (("slab", cache.k_slab), ("rest", cache.k_rest), ("v", cache.v)):
+        if t is None:
+            continue
+        got = to_host(t, w.dtype)[:, :, S - 1]
+        want = full[nm][:, :, S - 1]
+        ud = ulp_diff_bf16(got, want) if w.dtype == "bf16" else ulp_diff_f32(got, want)
+        assert ud.max() <= 1 and (ud == 0).mean() >= 0.999, nm
+    ref_out, ref_idx, ref_s = oracle.decode(q, full["slab"], full["rest"], full["v"], P, k,
+                                            w.dtype, S=S)
+    check_decode(w.dtype, k, out.cpu().numpy(), idx.cpu().numpy(), ref_out, ref_idx, ref_s,
+                 all_pairs(w))
+
+
+def test_decode_steps_in_sequence_paths_agree(lib):
+    """Eight consecutive steps on the fused and on the split path from the same
+    starting cache: identical selections, outputs within float32 rounding, and
+    identical cache contents afterwards."""
+    import torch
+    w = synth.custom("step_seq", 305, B=2, Hq=4, Hkv=4, S=500)
+    c = make_case(w, 500, 520)
+    caches = [device_cache(lib, c), device_cache(lib, c)]
+    P = to_dev(c.P, "f32")
+    for step in range(8):
+        kn, vn = synth.new_tokens(w, 100 + step)
+        q = to_dev(synth.queries(w, step=100 + step), w.dtype)
+        res = [lib.decode_step(q, to_dev(kn[:, :, 0], w.dtype), to_dev(vn[:, :, 0], w.dtype),
+                               caches[i], P, w.k_at(501 + step), path=p)
+               for i, p in ((0, 1), (1, 2))]
+        assert np.array_equal(res[0][1].cpu().numpy(), res[1][1].cpu().numpy())
+        assert np.max(np.abs(res[0][0].cpu().numpy() - res[1][0].cpu().numpy())) < 1e-5
+    torch.cuda.synchronize()
+    for a, b in ((caches[0].k_slab, caches[1].k_slab), (caches[0].k_rest, caches[1].k_rest),
+                 (caches[0].v, caches[1].v)):
+        ud = ulp_diff_bf16(to_host(a, "bf16"), to_host(b, "bf16"))
+        assert ud.max() <= 1 and (ud == 0).mean() >= 0.9999
+    assert caches[0].length == caches[1].length == 508
