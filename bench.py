@@ -56,14 +56,18 @@ def algorithmic_bytes(w, S, k) -> dict:
 def measured_traffic(kernel_hash: str, workload: str):
     """HBM bytes per launch from the committed counter summary, if it was
     taken on the current kernel source; else None."""
-    p = os.path.join(ROOT, "profiles", f"traffic_fused_decode_step_{workload}.json")
+    p = os.path.join(ROOT, "profiles", f"traffic_fused_decode_step_{workload}.txt")
     if not os.path.exists(p):
         return None
+    t = {}
     with open(p) as fh:
-        t = json.load(fh)
+        for line in fh:
+            if "=" in line:
+                key, val = line.split("=", 1)
+                t[key.strip()] = val.strip()
     if t.get("kernel_source_hash") != kernel_hash:
         return None
-    return t.get("hbm_bytes_per_launch")
+    return float(t["hbm_bytes_per_launch"])
 
 
 def main():
