@@ -69,6 +69,8 @@ int check_shape(int B, int Hq, int Hkv, int D, int d, int S, int S_max, int dtyp
   if ((d * esize(dtype)) % 16 != 0) return LOKI_EUNSUPPORTED;
   if (static_cast<int64_t>(B) * Hq > (1 << 30) || Hkv > 65535) return LOKI_EUNSUPPORTED;
   if (S > 65535 * 1024) return LOKI_EUNSUPPORTED;  // score grid.y limit
+  // loads address one (sequence, KV head) region with 31-bit byte offsets
+  if (static_cast<int64_t>(S_max) * D * esize(dtype) >= (1LL << 31)) return LOKI_EUNSUPPORTED;
   return LOKI_OK;
 }
 

@@ -67,6 +67,14 @@ __device__ __forceinline__ void attend_loop(GetJ get_j, GetS get_s, int t0, int 
   const int dr = D - d;
   const bool in_rest = kd0 >= d;
   const bool kload = SPARSE ? in_rest : true;
+  constexpr uint32_t EB = E::BYTES;
+  // regions of this (sequence, KV head): slab, rest and value rows
+  const Region gs = make_region(slab, 0x7fffffffu);
+  const Region gr = make_region(rest ? rest : slab, 0x7fffffffu);
+  const Region gv = make_region(val, 0x7fffffffu);
+  const uint32_t srow = static_cast<uint32_t>(d) * EB, rrow = static_cast<uint32_t>(dr) * EB;
+  const uint32_t scol = static_cast<uint32_t>(kd0) * EB;
+  const uint32_t rcol = static_cast<uint32_t>(in_rest ? kd0 - d : 0) * EB;
 
   for (int tb = t0 + grp; tb < t1; tb += NG * U) {
     int j[U];
@@ -81,14 +89,18 @@ __device__ __forceinline__ void attend_loop(GetJ get_j, GetS get_s, int t0, int 
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int64_t jj = j[u];
-      const typename E::T* kp = in_rest ? rest + jj * dr + (kd0 - d) : slab + jj * d + kd0;
+      const uint32_t jj = static_cast<uint32_t>(j[u]);
       kc[u] = zero_chunk();
       vc[u] = zero_chunk();
       if (ok[u]) {
         if (j[u] != jo) {  // separate branches keep each load's address space known
-          if (kload) kc[u] = ld16_stream(kp);
-          vc[u] = ld16_stream(val + jj * D + kd0);
+          if (kload) {  // each branch keeps its buffer resource wave-uniform
+            if (in_rest)
+              kc[u] = ld16_region(gr, jj * rrow + rcol);
+            else
+              kc[u] = ld16_region(gs, jj * srow + scol);
+          }
+          vc[u] = ld16_region(gv, jj * static_cast<uint32_t>(D) * EB + kd0 * EB);
         } else {
           if (kload) kc[u] = ld16(ko + kd0);
           vc[u] = ld16(vo + kd0);

@@ -49,6 +49,32 @@ __device__ __forceinline__ Chunk ld16_stream(const void* p) {
   return c;
 }
 
+// Buffer resource over one (sequence, KV head) region of a cache tensor:
+// loads take 32-bit byte offsets from the region base (wave-uniform in
+// SGPRs), and an offset past `bytes` reads zeros.
+struct Region {
+  __amdgpu_buffer_rsrc_t r;
+};
+
+__device__ __forceinline__ Region make_region(const void* base, uint32_t bytes) {
+  Region g;
+  g.r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                          static_cast<int>(bytes), 0x00020000);
+  return g;
+}
+
+// Cache policy of the streamed and gathered loads (read once per launch):
+// nontemporal.
+constexpr int kStreamPolicy = 2;
+
+__device__ __forceinline__ Chunk ld16_region(const Region& g, uint32_t off) {
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(g.r, static_cast<int>(off), 0,
+                                                          kStreamPolicy);
+  Chunk c;
+  c.u = make_uint4(v.x, v.y, v.z, v.w);
+  return c;
+}
+
 __device__ __forceinline__ Chunk zero_chunk() {
   Chunk c;
   c.u = make_uint4(0u, 0u, 0u, 0u);

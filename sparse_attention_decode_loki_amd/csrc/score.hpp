@@ -30,10 +30,12 @@ __device__ __forceinline__ void score_first(const typename E::T* __restrict__ sl
   const int part = threadIdx.x % LPS;
   const int tk = threadIdx.x / LPS;
   const bool active = part * VEC < d;
+  const Region gs = make_region(slab, 0x7fffffffu);
+  const uint32_t row = static_cast<uint32_t>(d) * E::BYTES;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int j = j0 + tk + TPI * u;
-    c[u] = (active && j < j1) ? ld16_stream(slab + static_cast<int64_t>(j) * d + part * VEC)
+    c[u] = (active && j < j1) ? ld16_region(gs, static_cast<uint32_t>(j) * row + part * 16u)
                               : zero_chunk();
   }
 }
@@ -48,12 +50,14 @@ __device__ __forceinline__ void score_loop(const typename E::T* __restrict__ sla
   const int part = threadIdx.x % LPS;
   const int tk = threadIdx.x / LPS;
   const bool active = part * VEC < d;
+  const Region gs = make_region(slab, 0x7fffffffu);
+  const uint32_t row = static_cast<uint32_t>(d) * E::BYTES;
   for (int jb = j0 + tk; jb < j1; jb += TPI * U) {
     if (jb != j0 + tk) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int j = jb + TPI * u;
-        c[u] = (active && j < j1) ? ld16_stream(slab + static_cast<int64_t>(j) * d + part * VEC)
+        c[u] = (active && j < j1) ? ld16_region(gs, static_cast<uint32_t>(j) * row + part * 16u)
                                   : zero_chunk();
       }
     }
