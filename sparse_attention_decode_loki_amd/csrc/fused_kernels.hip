@@ -111,26 +111,26 @@ __global__ void __launch_bounds__(kBlock) fused_kernel(FusedArgs a) {
   }
   __syncthreads();
   if (threadIdx.x < D) {
-    const int c = threadIdx.x;
+    const int col = threadIdx.x;
     float s = 0.f;
 #pragma unroll
-    for (int pp = 0; pp < NRB; ++pp) s += sc.rot.q[pp][c];
-    qs[c] = s;
+    for (int pp = 0; pp < NRB; ++pp) s += sc.rot.q[pp][col];
+    qs[col] = s;
     if (STEP) {
       double x = 0.0;
 #pragma unroll
-      for (int pp = 0; pp < NRB; ++pp) x += sc.rot.k[STEP ? pp : 0][c];
+      for (int pp = 0; pp < NRB; ++pp) x += sc.rot.k[STEP ? pp : 0][col];
       const T st = round_store<E>(x);
-      const T vn = static_cast<const T*>(a.v_new)[bgo * D + c];
-      kslot[c] = st;
-      vslot[c] = vn;
+      const T vn = static_cast<const T*>(a.v_new)[bgo * D + col];
+      kslot[col] = st;
+      vslot[col] = vn;
       if (h % G == 0) {  // one writer per KV head
         const int64_t slot = bgo * a.S_max + a.pos;
-        if (c < d)
-          static_cast<T*>(a.slab)[slot * d + c] = st;
+        if (col < d)
+          static_cast<T*>(a.slab)[slot * d + col] = st;
         else
-          static_cast<T*>(a.rest)[slot * (D - d) + (c - d)] = st;
-        static_cast<T*>(a.val)[slot * D + c] = vn;
+          static_cast<T*>(a.rest)[slot * (D - d) + (col - d)] = st;
+        static_cast<T*>(a.val)[slot * D + col] = vn;
       }
     }
   }
