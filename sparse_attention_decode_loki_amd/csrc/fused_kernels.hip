@@ -46,12 +46,18 @@ __global__ void __launch_bounds__(kBlock) fused_kernel(FusedArgs a) {
     float q[NRB][D];
     double k[STEP ? NRB : 1][D];
   };
+  constexpr int CAP = 64;  // crossing bins up to this size are ranked directly
+  struct Sel {
+    SelectSmemAny<kBlock> s;
+    uint32_t cand[CAP];
+  };
   union Scratch {
-    SelectSmemAny<kBlock> sel;
+    Sel sel;
     MergeSmem<D, 1, Gm::NG> mrg;
     Rot rot;
   };
   __shared__ Scratch sc;
+  __shared__ unsigned hist0[SMALL ? kSelBins : 1];  // first-digit histogram of the scores
   __shared__ float rin[STEP ? 2 : 1][D];  // q (and the new key) as float
   __shared__ __align__(16) T kslot[STEP ? D : VEC];  // new key row [slab | rest], stored values
   __shared__ __align__(16) T vslot[STEP ? D : VEC];  // new value row
@@ -70,6 +76,9 @@ __global__ void __launch_bounds__(kBlock) fused_kernel(FusedArgs a) {
   const T* sl = static_cast<const T*>(a.slab) + bgo * a.S_max * d;
   const T* rs = d < D ? static_cast<const T*>(a.rest) + bgo * a.S_max * (D - d) : nullptr;
   const T* vv = static_cast<const T*>(a.val) + bgo * a.S_max * D;
+
+  if (SMALL)
+    for (int i = threadIdx.x; i < kSelBins; i += kBlock) hist0[i] = 0u;
 
   // 1. q' = q . P[g] (and, for STEP, k' = k_new . P[g] in float64): thread
   //    (cq, rb) adds rows [rb*RB, rb*RB + RB) for columns 4*cq .. 4*cq + 3,
@@ -145,7 +154,11 @@ __global__ void __launch_bounds__(kBlock) fused_kernel(FusedArgs a) {
     constexpr int US = 8;
     Chunk c[US];
     score_first<E, LPS, US>(sl, d, 0, S, c);
-    score_loop<E, LPS, 1, US>(sl, d, 0, S, qf, [&](int, int j, float s) { sb[j] = s; }, c);
+    // the selection's first radix digit is counted here, under the stream
+    score_loop<E, LPS, 1, US>(sl, d, 0, S, qf, [&](int, int j, float s) {
+      sb[j] = s;
+      if (SMALL) atomicAdd(&hist0[first_digit(order_key(s))], 1u);
+    }, c);
     if (STEP) {
       // the new token's score from its LDS row, with the streaming pass's
       // arithmetic (wave 0; sb[pos] written by the loop is discarded)
@@ -158,7 +171,13 @@ __global__ void __launch_bounds__(kBlock) fused_kernel(FusedArgs a) {
 #pragma unroll
         for (int v = 0; v < VEC; ++v) dot = fmaf(qf[0][v], x[v], dot);
         dot = group_sum<LPS>(dot);
-        if (threadIdx.x == 0) sb[a.pos] = dot;
+        if (threadIdx.x == 0) {
+          if (SMALL) {
+            atomicSub(&hist0[first_digit(order_key(sb[a.pos]))], 1u);
+            atomicAdd(&hist0[first_digit(order_key(dot))], 1u);
+          }
+          sb[a.pos] = dot;
+        }
       }
     }
   }
@@ -172,9 +191,10 @@ __global__ void __launch_bounds__(kBlock) fused_kernel(FusedArgs a) {
       irow[p] = j;
     };
     if (SMALL)
-      block_select_topk_reg<kBlock, 16>([&](int j) { return sb[j]; }, S, kk, emit, sc.sel.reg);
+      block_select_topk_hist<kBlock, 16, CAP>([&](int j) { return sb[j]; }, S, kk, hist0, emit,
+                                              sc.sel.s.reg, sc.sel.cand);
     else
-      block_select_topk_any<kBlock>([&](int j) { return sb[j]; }, S, kk, emit, sc.sel);
+      block_select_topk_any<kBlock>([&](int j) { return sb[j]; }, S, kk, emit, sc.sel.s);
   }
   __syncthreads();
 

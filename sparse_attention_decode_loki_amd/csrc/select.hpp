@@ -268,3 +268,145 @@ __device__ __forceinline__ void block_select_topk_any(Src src, int S, int k, Emi
 }
 
 }  // namespace loki
+
+namespace loki {
+
+// First radix digit of a key: bits 31..21 (sign, exponent, 2 mantissa bits).
+__device__ __forceinline__ uint32_t first_digit(uint32_t key) { return key >> 21; }
+
+// Top-k from a histogram of the first digit that the producer of the scores
+// has already accumulated (hist0, kSelBins counters in LDS, zeroed before the
+// scores were written).  Thread t owns the E = ceil(S / BLOCK) consecutive
+// elements [t*E, t*E + E) as register keys.  After the crossing bin of the
+// first digit is known, its candidates (at most CAP; the usual case is about
+// a percent of S) are gathered into `cand` (LDS) in index order and the exact
+// threshold is found by ranking them against each other; when the bin holds
+// more than CAP keys the remaining two digits are resolved by radix passes.
+// Requires S <= BLOCK * EMAX.
+template <int BLOCK, int EMAX, int CAP, class Src, class Emit>
+__device__ void block_select_topk_hist(Src src, int S, int k, const unsigned* hist0, Emit emit,
+                                       SelectSmemR<BLOCK>& sm, uint32_t* cand) {
+  constexpr int PER = kSelBins / BLOCK;
+  const int tid = threadIdx.x;
+  const int E = (S + BLOCK - 1) / BLOCK;
+  const int j0 = tid * E;
+  uint32_t key[EMAX];
+#pragma unroll
+  for (int e = 0; e < EMAX; ++e) {
+    const int j = j0 + e;
+    key[e] = (e < E && j < S) ? order_key(src(j)) : 0u;
+  }
+  int nvalid = S - j0;
+  nvalid = nvalid < 0 ? 0 : (nvalid > E ? E : nvalid);
+
+  uint32_t prefix = 0u, mask = 0u;
+  int krem = k;
+  int buf = 0;
+  // crossing bin of digit `shift` in `hist`: sets prefix/mask/krem
+  auto resolve_digit = [&](const unsigned* hist, int shift, uint32_t dmask) -> bool {
+    const int hi = kSelBins - PER * tid;
+    unsigned c[PER];
+    unsigned local = 0u;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      c[i] = hist[hi - 1 - i];
+      local += c[i];
+    }
+    unsigned total;
+    unsigned above = block_excl_scan<BLOCK>(local, total, sm, buf);
+    buf ^= 1;
+    if (above < static_cast<unsigned>(krem) && static_cast<unsigned>(krem) <= above + local) {
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        if (above < static_cast<unsigned>(krem) && static_cast<unsigned>(krem) <= above + c[i]) {
+          sm.bin = static_cast<unsigned>(hi - 1 - i);
+          sm.above = above;
+          sm.cnt = c[i];
+        }
+        above += c[i];
+      }
+    }
+    __syncthreads();
+    prefix |= sm.bin << shift;
+    mask |= dmask << shift;
+    krem -= static_cast<int>(sm.above);
+    return static_cast<int>(sm.cnt) == krem;  // the whole bin is kept
+  };
+
+  if (k < S && !resolve_digit(hist0, 21, 0x7ffu)) {
+    const int nbin = static_cast<int>(sm.cnt);
+    if (nbin <= CAP) {
+      // gather the bin's keys in index order, then rank them exactly
+      unsigned mine = 0u;
+#pragma unroll
+      for (int e = 0; e < EMAX; ++e) mine += (e < nvalid && (key[e] & mask) == prefix);
+      unsigned total;
+      unsigned at = block_excl_scan<BLOCK>(mine, total, sm, buf);
+      buf ^= 1;
+#pragma unroll
+      for (int e = 0; e < EMAX; ++e)
+        if (e < nvalid && (key[e] & mask) == prefix) cand[at++] = key[e];
+      __syncthreads();
+      for (int i = tid; i < nbin; i += BLOCK) {
+        const uint32_t x = cand[i];
+        int gt = 0, ge = 0;
+        for (int m = 0; m < nbin; ++m) {
+          const uint32_t y = cand[m];
+          gt += y > x;
+          ge += y >= x;
+        }
+        if (gt < krem && krem <= ge) {  // every thread holding this key value agrees
+          sm.bin = x;
+          sm.above = static_cast<unsigned>(gt);
+        }
+      }
+      __syncthreads();
+      prefix = sm.bin;
+      mask = 0xffffffffu;
+      krem -= static_cast<int>(sm.above);
+    } else {
+      const int shifts[2] = {10, 0};
+      const int widths[2] = {11, 10};
+      for (int pass = 0; pass < 2; ++pass) {
+        const int shift = shifts[pass];
+        const uint32_t dmask = (1u << widths[pass]) - 1u;
+        for (int i = tid; i < kSelBins; i += BLOCK) sm.hist[i] = 0u;
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < EMAX; ++e)
+          if (e < nvalid && (key[e] & mask) == prefix)
+            atomicAdd(&sm.hist[(key[e] >> shift) & dmask], 1u);
+        __syncthreads();
+        if (resolve_digit(sm.hist, shift, dmask)) break;
+      }
+    }
+  }
+
+  // compaction in index order: one scan of the above-threshold counts and
+  // one of the at-threshold counts
+  unsigned ngt = 0u, neq = 0u;
+#pragma unroll
+  for (int e = 0; e < EMAX; ++e) {
+    if (e < nvalid) {
+      const uint32_t m = key[e] & mask;
+      ngt += m > prefix;
+      neq += m == prefix;
+    }
+  }
+  unsigned tot;
+  const unsigned gt_before = block_excl_scan<BLOCK>(ngt, tot, sm, buf);
+  buf ^= 1;
+  unsigned eq_before = block_excl_scan<BLOCK>(neq, tot, sm, buf);
+  int pos = static_cast<int>(gt_before) + min(static_cast<int>(eq_before), krem);
+#pragma unroll
+  for (int e = 0; e < EMAX; ++e) {
+    if (e < nvalid) {
+      const uint32_t m = key[e] & mask;
+      const bool eq = m == prefix;
+      if (m > prefix || (eq && static_cast<int>(eq_before) < krem)) emit(pos++, j0 + e);
+      eq_before += eq;
+    }
+  }
+}
+
+}  // namespace loki

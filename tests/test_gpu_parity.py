@@ -348,3 +348,27 @@ def test_decode_steps_in_sequence_paths_agree(lib):
         ud = ulp_diff_bf16(to_host(a, "bf16"), to_host(b, "bf16"))
         assert ud.max() <= 1 and (ud == 0).mean() >= 0.9999
     assert caches[0].length == caches[1].length == 508
+
+
+@pytest.mark.parametrize("S,k,nrows", [(3000, 750, 7), (4096, 1000, 3), (2048, 17, 2), (1500, 1499, 5)])
+def test_decode_exact_ties_from_repeated_rows(lib, S, k, nrows):
+    """Slab rows drawn from a handful of distinct rows: scores tie exactly
+    (bit-identical on every side), so thousands of tokens share the crossing
+    bin; equal scores must go to the lower index on both paths."""
+    import torch
+    w = synth.custom("ties", 400 + nrows, B=2, Hq=3, Hkv=3, S=S)
+    c = make_case(w, S, S)
+    rng = np.random.default_rng(S + nrows)
+    pick = rng.integers(0, nrows, size=(w.B, w.Hkv, S))
+    for b in range(w.B):
+        for g in range(w.Hkv):
+            c.slab[b, g] = c.slab[b, g, pick[b, g]]
+    cache = device_cache(lib, c)
+    ref_out, ref_idx, ref_s = oracle.decode(c.q, c.slab, c.rest, c.v, c.P, k, w.dtype, S=S)
+    for path in (1, 2):
+        out, idx = lib.decode(to_dev(c.q, w.dtype), cache, to_dev(c.P, "f32"), k, path=path)
+        idx = idx.cpu().numpy()
+        assert np.array_equal(idx.astype(np.int64), ref_idx), f"path {path}"
+        out = out.cpu().numpy()
+        for b, h in all_pairs(w):
+            assert out_error(w.dtype, out[b, h], ref_out[b, h]) <= TOL[w.dtype]
