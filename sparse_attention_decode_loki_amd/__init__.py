@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libloki.so")
 
 LOKI_OK, LOKI_EINVAL, LOKI_EWORKSPACE, LOKI_EDEVICE, LOKI_EUNSUPPORTED = 0, -1, -2, -3, -4
 LOKI_F32, LOKI_BF16 = 0, 1
-PATH_AUTO, PATH_FUSED, PATH_SPLIT = 0, 1, 2
+PATH_AUTO, PATH_FUSED, PATH_SPLIT, PATH_UNION = 0, 1, 2, 3
 
 # name -> (restype, argtypes); mirrors include/loki.h
 _P = ctypes.c_void_p
@@ -230,7 +230,8 @@ def decode_step(q, k_new, v_new, cache: KVCache, P, k: int, pos: int | None = No
 
 
 def decode_path(B, Hq, Hkv, D, d, S, k, path=PATH_AUTO) -> int:
-    """The path (PATH_FUSED or PATH_SPLIT) loki_decode_ex takes for these sizes."""
+    """The path (PATH_FUSED, PATH_SPLIT or PATH_UNION) loki_decode_ex takes
+    for these sizes."""
     st = load().loki_decode_path(B, Hq, Hkv, D, d, S, k, path)
     if st < 0:
         raise LokiError(st, "loki_decode_path")

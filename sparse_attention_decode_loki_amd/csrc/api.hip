@@ -28,6 +28,21 @@ int sparse_nsplit(int rows, int kk) {
 
 int heads_per_dense_block(int G) { return G >= 4 ? 4 : (G >= 2 ? 2 : 1); }
 
+// Union gather (grouped-query heads): position ranges of at most
+// kUnionMaxTok tokens, enough of them to give about four workgroups per CU.
+bool union_ok(int Hq, int Hkv, int S) {
+  const int G = Hq / Hkv;
+  return (G == 2 || G == 4) && S <= loki::kUnionMaxS;
+}
+
+// Position ranges are whole bitmap words (R a multiple of 32).
+int union_nsplit(int B, int Hkv, int S) {
+  int n = std::min(cdiv(kTargetWorkgroups, static_cast<int64_t>(B) * Hkv), cdiv(S, 128));
+  n = std::max({1, n, cdiv(S, loki::kUnionMaxTok)});
+  const int R = cdiv(cdiv(S, n), 32) * 32;
+  return cdiv(S, R);
+}
+
 int dense_nsplit(int B, int Hq, int Hkv, int S) {
   const int G = Hq / Hkv;
   const int rows = B * Hkv * cdiv(G, heads_per_dense_block(G));
@@ -35,24 +50,40 @@ int dense_nsplit(int B, int Hq, int Hkv, int S) {
 }
 
 struct Layout {
-  size_t qrot, scores, part, total;
+  size_t qrot, scores, part, bits, total;
 };
 
+// qrot [B*Hq, D] | scores [B*Hq, S_max] | split partials |
+// kept-position bitmaps [B*Hq, ceil(S_max/32)] (union gather)
 Layout layout(int B, int Hq, int D, int S_max, int nsplit) {
   Layout L;
   const size_t rows = static_cast<size_t>(B) * Hq;
   L.qrot = 0;
   L.scores = align256(rows * D * sizeof(float));
   L.part = L.scores + align256(rows * static_cast<size_t>(S_max) * sizeof(float));
-  L.total = L.part + align256(rows * static_cast<size_t>(nsplit) * (D + 2) * sizeof(float));
+  L.bits = L.part + align256(rows * static_cast<size_t>(nsplit) * (D + 2) * sizeof(float));
+  L.total = L.bits + align256(rows * static_cast<size_t>(cdiv(S_max, 32)) * sizeof(unsigned));
   return L;
+}
+
+// Workspace layout of the split / union paths for these sizes.
+Layout split_layout(int B, int Hq, int Hkv, int D, int S, int S_max, int kk, bool uni) {
+  return layout(B, Hq, D, S_max, uni ? union_nsplit(B, Hkv, S) : sparse_nsplit(B * Hq, kk));
+}
+
+bool valid_path(int path) {
+  return path == LOKI_PATH_AUTO || path == LOKI_PATH_FUSED || path == LOKI_PATH_SPLIT ||
+         path == LOKI_PATH_UNION;
 }
 
 int max_nsplit(int B, int Hq, int S_max, int k_max) {
   const int kk = std::max(1, std::min(k_max, S_max));
   // dense_nsplit over any Hkv dividing Hq: its row count is at least B
   const int dense_max = std::max(1, std::min(cdiv(kTargetWorkgroups, B), cdiv(S_max, 256)));
-  return std::max(sparse_nsplit(B * Hq, kk), dense_max);
+  // union_nsplit never exceeds its range count before rounding, at Hkv = 1
+  const int union_max = std::max(
+      {1, std::min(cdiv(kTargetWorkgroups, B), cdiv(S_max, 128)), cdiv(S_max, loki::kUnionMaxTok)});
+  return std::max({sparse_nsplit(B * Hq, kk), dense_max, union_max});
 }
 
 size_t workspace_bytes(int B, int Hq, int D, int S_max, int k_max) {
@@ -168,6 +199,7 @@ int loki_decode_path(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t d, i
   const int kk = std::min(k, S);
   if (path == LOKI_PATH_SPLIT) return LOKI_PATH_SPLIT;
   if (path == LOKI_PATH_FUSED) return fused_fits(D, S, kk) ? LOKI_PATH_FUSED : LOKI_EUNSUPPORTED;
+  if (path == LOKI_PATH_UNION) return union_ok(Hq, Hkv, S) ? LOKI_PATH_UNION : LOKI_EUNSUPPORTED;
   if (path != LOKI_PATH_AUTO) return LOKI_EINVAL;
   return auto_fused(B, Hq, Hkv, D, S, kk) ? LOKI_PATH_FUSED : LOKI_PATH_SPLIT;
 }
@@ -179,8 +211,9 @@ int loki_decode_ex(const void* q, const void* k_slab, const void* k_rest, const 
   int st = check_shape(B, Hq, Hkv, D, d, S, S_max, dtype);
   if (st != LOKI_OK) return st;
   if (k < 1) return LOKI_EINVAL;
-  if (path != LOKI_PATH_AUTO && path != LOKI_PATH_FUSED && path != LOKI_PATH_SPLIT)
-    return LOKI_EINVAL;
+  if (!valid_path(path)) return LOKI_EINVAL;
+  const bool uni = path == LOKI_PATH_UNION;
+  if (uni && !union_ok(Hq, Hkv, S)) return LOKI_EUNSUPPORTED;
   if (B == 0) return LOKI_OK;
   if (!q || !out || !idx) return LOKI_EINVAL;
   st = check_cache_ptrs(k_slab, k_rest, v, P, D, d);
@@ -196,17 +229,21 @@ int loki_decode_ex(const void* q, const void* k_slab, const void* k_rest, const 
     return status_of(loki::launch_fused(a, kk));
   }
   const int rows = B * Hq;
-  const int nsplit = sparse_nsplit(rows, kk);
-  const Layout L = layout(B, Hq, D, S_max, nsplit);
+  const int nsplit = uni ? union_nsplit(B, Hkv, S) : sparse_nsplit(rows, kk);
+  const Layout L = split_layout(B, Hq, Hkv, D, S, S_max, kk, uni);
   if (!workspace || ws_bytes < L.total || !aligned16(workspace)) return LOKI_EWORKSPACE;
   char* ws = static_cast<char*>(workspace);
   float* qrot = reinterpret_cast<float*>(ws + L.qrot);
   float* scores = reinterpret_cast<float*>(ws + L.scores);
   float* part = reinterpret_cast<float*>(ws + L.part);
+  unsigned* bits = reinterpret_cast<unsigned*>(ws + L.bits);
   hipError_t e = loki::launch_rotate(a, qrot);
   if (e == hipSuccess) e = loki::launch_scores(a, qrot, scores);
-  if (e == hipSuccess) e = loki::launch_topk(scores, rows, S, S, kk, idx, a.stream);
-  if (e == hipSuccess) e = loki::launch_attend(a, qrot, scores, idx, kk, part, nsplit, true);
+  if (e == hipSuccess)
+    e = loki::launch_topk(scores, rows, S, S, kk, idx, a.stream, uni ? bits : nullptr);
+  if (e == hipSuccess)
+    e = uni ? loki::launch_attend_union(a, qrot, scores, bits, part, nsplit)
+            : loki::launch_attend(a, qrot, scores, idx, kk, part, nsplit, true);
   return status_of(e);
 }
 
@@ -220,8 +257,9 @@ int loki_decode_step(const void* q, const void* k_new, const void* v_new, const 
   int st = check_shape(B, Hq, Hkv, D, d, S, S_max, dtype);
   if (st != LOKI_OK) return st;
   if (k < 1) return LOKI_EINVAL;
-  if (path != LOKI_PATH_AUTO && path != LOKI_PATH_FUSED && path != LOKI_PATH_SPLIT)
-    return LOKI_EINVAL;
+  if (!valid_path(path)) return LOKI_EINVAL;
+  const bool uni = path == LOKI_PATH_UNION;
+  if (uni && !union_ok(Hq, Hkv, S)) return LOKI_EUNSUPPORTED;
   if (B == 0) return LOKI_OK;
   if (!q || !k_new || !v_new || !out || !idx) return LOKI_EINVAL;
   st = check_cache_ptrs(k_slab, k_rest, v, P, D, d);
@@ -236,14 +274,13 @@ int loki_decode_step(const void* q, const void* k_new, const void* v_new, const 
     if (!fused_fits(D, S, kk)) return LOKI_EUNSUPPORTED;
     return status_of(loki::launch_fused_step(a, k_new, v_new, pos, kk));
   }
-  const int nsplit = sparse_nsplit(B * Hq, kk);
-  const Layout L = layout(B, Hq, D, S_max, nsplit);
+  const Layout L = split_layout(B, Hq, Hkv, D, S, S_max, kk, uni);
   if (!workspace || ws_bytes < L.total || !aligned16(workspace)) return LOKI_EWORKSPACE;
   hipError_t e = loki::launch_append(k_new, v_new, P, k_slab, d < D ? k_rest : nullptr, v, B, Hkv,
                                      D, d, S_max, pos, 1, dtype, a.stream);
   if (e != hipSuccess) return LOKI_EDEVICE;
   return loki_decode_ex(q, k_slab, k_rest, v, P, B, Hq, Hkv, D, d, S, S_max, k, dtype, out, idx,
-                        workspace, ws_bytes, LOKI_PATH_SPLIT, stream);
+                        workspace, ws_bytes, uni ? LOKI_PATH_UNION : LOKI_PATH_SPLIT, stream);
 }
 
 int loki_decode(const void* q, const void* k_slab, const void* k_rest, const void* v,
@@ -330,7 +367,8 @@ int loki_dense_decode(const void* q, const void* k_slab, const void* k_rest, con
   float* qrot = reinterpret_cast<float*>(ws + L.qrot);
   float* part = reinterpret_cast<float*>(ws + L.part);
   hipError_t e = loki::launch_rotate(a, qrot);
-  if (e == hipSuccess) e = loki::launch_attend(a, qrot, nullptr, nullptr, S, part, nsplit, false);
+  if (e == hipSuccess)
+    e = loki::launch_attend(a, qrot, nullptr, nullptr, S, part, nsplit, false);
   return status_of(e);
 }
 

@@ -48,7 +48,14 @@ __device__ __forceinline__ void acc_init(Acc<VEC>& s) {
 // qf[h][v] = q'_h[lane_dim0 + v] (zero where the lane's dims come from get_s).
 // Token jo (if >= 0) is not read from the cache: its rotated key row
 // [slab | rest] and value row are taken from ko / vo (LDS, storage format).
-template <class E, int D, int NH, bool SPARSE, int U, class GetJ, class GetS>
+// NoMask: every head takes every token.  A union list (GQA) passes get_mask(t),
+// a bitmask of the heads that kept token t; the other heads skip it.
+struct NoMask {
+  __device__ __forceinline__ unsigned operator()(int) const { return 0xffffffffu; }
+};
+
+template <class E, int D, int NH, bool SPARSE, int U, class GetJ, class GetS,
+          class GetMask = NoMask>
 __device__ __forceinline__ void attend_loop(GetJ get_j, GetS get_s, int t0, int t1,
                                             const typename E::T* __restrict__ slab,
                                             const typename E::T* __restrict__ rest,
@@ -56,7 +63,8 @@ __device__ __forceinline__ void attend_loop(GetJ get_j, GetS get_s, int t0, int 
                                             const float (&qf)[NH][E::VEC], float scale_log2,
                                             Acc<E::VEC> (&st)[NH], int jo = -1,
                                             const typename E::T* ko = nullptr,
-                                            const typename E::T* vo = nullptr) {
+                                            const typename E::T* vo = nullptr,
+                                            GetMask get_mask = GetMask()) {
   using G = Geo<E, D>;
   constexpr int VEC = G::VEC;
   constexpr int LPV = G::LPV;
@@ -79,6 +87,7 @@ __device__ __forceinline__ void attend_loop(GetJ get_j, GetS get_s, int t0, int 
   for (int tb = t0 + grp; tb < t1; tb += NG * U) {
     int j[U];
     bool ok[U];
+    unsigned hm[U];
     Chunk kc[U], vc[U];
     float sv[NH][U];
 #pragma unroll
@@ -86,6 +95,7 @@ __device__ __forceinline__ void attend_loop(GetJ get_j, GetS get_s, int t0, int 
       const int t = tb + NG * u;
       ok[u] = t < t1;
       j[u] = ok[u] ? get_j(t) : 0;
+      hm[u] = ok[u] ? get_mask(t) : 0u;
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -111,7 +121,8 @@ __device__ __forceinline__ void attend_loop(GetJ get_j, GetS get_s, int t0, int 
 #pragma unroll
       for (int h = 0; h < NH; ++h)
 #pragma unroll
-        for (int u = 0; u < U; ++u) sv[h][u] = (ok[u] && r == 0) ? get_s(h, tb + NG * u, j[u]) : 0.f;
+        for (int u = 0; u < U; ++u)
+          sv[h][u] = (((hm[u] >> h) & 1u) && r == 0) ? get_s(h, tb + NG * u, j[u]) : 0.f;
     }
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
@@ -125,7 +136,7 @@ __device__ __forceinline__ void attend_loop(GetJ get_j, GetS get_s, int t0, int 
 #pragma unroll
         for (int v = 0; v < VEC; ++v) dot = fmaf(qf[h][v], kf[v], dot);
         dot = group_sum<LPV>(dot);
-        x[u] = ok[u] ? dot * scale_log2 : -INFINITY;
+        x[u] = ((hm[u] >> h) & 1u) ? dot * scale_log2 : -INFINITY;
         mx = fmaxf(mx, x[u]);
       }
       const float c = (st[h].m == mx) ? 1.f : fast_exp2(st[h].m - mx);
@@ -134,7 +145,7 @@ __device__ __forceinline__ void attend_loop(GetJ get_j, GetS get_s, int t0, int 
       for (int v = 0; v < VEC; ++v) st[h].a[v] *= c;
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const float p = ok[u] ? fast_exp2(x[u] - mx) : 0.f;
+        const float p = ((hm[u] >> h) & 1u) ? fast_exp2(x[u] - mx) : 0.f;
         float vf[VEC];
         unpack<E>(vc[u], vf);
         st[h].l += p;

@@ -14,6 +14,8 @@
 //   topk_kernel     exact top-k of one score row, ascending indices
 //   attend_kernel   gather + online softmax over a slice of the kept tokens
 //                   (also the dense baseline, with all tokens)
+//   attend_union_kernel  the grouped-query variant: the union of the G query
+//                   heads' kept tokens is gathered once per KV head
 //   combine_kernel  log-sum-exp merge of the slices
 // The single-kernel path (fused_kernel) is in fused_kernels.hip.
 #include "launch.hpp"
@@ -121,16 +123,26 @@ __global__ void __launch_bounds__(kBlock) score_kernel(const typename E::T* __re
 
 // -------------------------------------------------------------------- topk --
 
+// Dynamic LDS: the score row (when use_lds) followed by the kept-position
+// bitmap (when `bits` is given: ceil(S/32) words per row, written out for
+// the union gather).
 template <int BLOCK>
 __global__ void __launch_bounds__(BLOCK) topk_kernel(const float* __restrict__ scores, int S,
                                                      int64_t ld, int k, int* __restrict__ idx,
-                                                     int use_lds) {
+                                                     int use_lds, unsigned* __restrict__ bits) {
   __shared__ SelectSmemAny<BLOCK> sm;
   extern __shared__ float sbuf[];
   const int row = blockIdx.x;
+  const int nw = (S + 31) >> 5;
+  unsigned* lbits = reinterpret_cast<unsigned*>(sbuf + (use_lds ? S : 0));
+  if (bits)
+    for (int i = threadIdx.x; i < nw; i += BLOCK) lbits[i] = 0u;
   const float* s = scores + static_cast<int64_t>(row) * ld;
   int* out = idx + static_cast<int64_t>(row) * k;
-  auto emit = [&](int p, int j) { out[p] = j; };
+  auto emit = [&](int p, int j) {
+    out[p] = j;
+    if (bits) atomicOr(&lbits[j >> 5], 1u << (j & 31));
+  };
   if (use_lds) {
     const int n4 = S >> 2;
     const float4* s4 = reinterpret_cast<const float4*>(s);
@@ -139,7 +151,13 @@ __global__ void __launch_bounds__(BLOCK) topk_kernel(const float* __restrict__ s
     __syncthreads();
     block_select_topk_any<BLOCK>([&](int j) { return sbuf[j]; }, S, k, emit, sm);
   } else {
+    __syncthreads();
     block_select_topk_any<BLOCK>([&](int j) { return s[j]; }, S, k, emit, sm);
+  }
+  if (bits) {
+    __syncthreads();
+    unsigned* brow = bits + static_cast<int64_t>(row) * nw;
+    for (int i = threadIdx.x; i < nw; i += BLOCK) brow[i] = lbits[i];
   }
 }
 
@@ -166,10 +184,21 @@ __global__ void __launch_bounds__(kBlock) attend_kernel(
   __shared__ float sst[SPARSE ? kAttendStage : 1];
 
   const int G = Hq / Hkv;
-  const int split = blockIdx.y;
+  int split = blockIdx.y;
   int b, g, h0, nh;
   if (SPARSE) {
-    const int row = blockIdx.x;  // b*Hq + h
+    int row = blockIdx.x;  // b*Hq + h
+    if (G > 1) {
+      // the G query heads of one KV head with the same split index read
+      // overlapping position ranges: give them consecutive logical ids on one
+      // XCD, so rows that several heads kept come from HBM once and then
+      // from that XCD's L2
+      const int n = gridDim.x * gridDim.y;
+      const int L = xcd_logical(blockIdx.x + blockIdx.y * gridDim.x, n);
+      const int rest = L / G;
+      split = rest % nsplit;
+      row = (rest / nsplit) * G + L % G;
+    }
     b = row / Hq;
     h0 = row % Hq;
     g = h0 / G;
@@ -241,21 +270,190 @@ __global__ void __launch_bounds__(kBlock) attend_kernel(
   });
 }
 
+constexpr int kUnionMax = kUnionMaxTok;  // token positions per union-gather workgroup
+static_assert(kUnionMax % 32 == 0 && kUnionMax / 8 <= kBlock, "one byte of positions per thread");
+static_assert(kUnionMaxS <= (1 << 24), "token id and head mask share one word");
+
+template <int D, int NH, int NG>
+union UnionSmem {
+  struct {
+    unsigned bw[NH][kUnionMax / 32];  // the G heads' bitmap words of the range
+    unsigned ulist[kUnionMax];        // token id | head mask << 24
+    unsigned wsum[kBlock / 64];
+  } g;
+  MergeSmem<D, NH, NG> m;  // after the gather
+};
+
+// Union gather for grouped-query attention.  Grid (B*Hkv, nsplit); workgroup
+// (bg, split) covers positions [split*R, split*R + R), R a multiple of 32 and
+// at most kUnionMax.  The G = NH query heads' kept-position bitmap words of
+// the range are read once into LDS; thread t takes 8 positions (one byte of
+// each head's bitmap), and the positions that any head kept are compacted in
+// ascending order with their head mask.  Each union token's key and value
+// rows are then loaded once for all G heads; a head that did not keep a
+// token skips it.
+template <class E, int D, int NH>
+__global__ void __launch_bounds__(kBlock, 4) attend_union_kernel(
+    const typename E::T* __restrict__ slab, const typename E::T* __restrict__ rest,
+    const typename E::T* __restrict__ val, const float* __restrict__ qrot,
+    const float* __restrict__ scores, const unsigned* __restrict__ bits, float* __restrict__ part,
+    float* __restrict__ out, int Hq, int Hkv, int d, int S, int S_max, int R, int nsplit,
+    float scale_log2) {
+  using Gm = Geo<E, D>;
+  constexpr int VEC = Gm::VEC;
+  constexpr int LPV = Gm::LPV;
+  constexpr int NW = kBlock / 64;
+  __shared__ UnionSmem<D, NH, Gm::NG> sm;
+
+  const int bg = blockIdx.x, split = blockIdx.y;
+  const int b = bg / Hkv, g = bg % Hkv;
+  const int h0 = g * NH;
+  const int j0 = split * R;
+  const int n = max(0, min(S, j0 + R) - j0);
+  const int tid = threadIdx.x;
+
+  // this lane's q' dims of the G heads and the heads' bitmap words, all
+  // issued together (one round trip)
+  const int r = tid % LPV;
+  const int kd0 = r * VEC;
+  float qf[NH][VEC];
+#pragma unroll
+  for (int h = 0; h < NH; ++h) {
+    const float* qr = qrot + (static_cast<int64_t>(b) * Hq + h0 + h) * D + kd0;
+#pragma unroll
+    for (int v = 0; v < VEC; v += 4) {
+      const float4 x = (kd0 >= d) ? *reinterpret_cast<const float4*>(qr + v)
+                                  : make_float4(0.f, 0.f, 0.f, 0.f);
+      qf[h][v] = x.x;
+      qf[h][v + 1] = x.y;
+      qf[h][v + 2] = x.z;
+      qf[h][v + 3] = x.w;
+    }
+  }
+  const int nw = (S + 31) >> 5;
+  const int nwr = (n + 31) >> 5;
+  const unsigned* brow = bits + (static_cast<int64_t>(b) * Hq + h0) * nw + (j0 >> 5);
+  for (int i = tid; i < NH * nwr; i += kBlock) {
+    const int h = i / nwr, w = i - h * nwr;
+    sm.g.bw[h][w] = brow[static_cast<int64_t>(h) * nw + w];
+  }
+  __syncthreads();
+
+  // compaction: thread t owns positions [8t, 8t + 8) of the range
+  unsigned hb[NH];
+  unsigned any = 0u;
+  {
+    const int p0 = tid * 8;
+    const unsigned valid = p0 < n ? (n - p0 >= 8 ? 0xffu : (1u << (n - p0)) - 1u) : 0u;
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+      hb[h] = valid ? (sm.g.bw[h][p0 >> 5] >> (p0 & 31)) & valid : 0u;
+      any |= hb[h];
+    }
+  }
+  const unsigned mine = __popc(any);
+  const int lane = tid & 63, wave = tid >> 6;
+  const unsigned incl = wave_incl_scan(mine, lane);
+  if (lane == 63) sm.g.wsum[wave] = incl;
+  __syncthreads();
+  unsigned before = 0u, ucnt = 0u;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    before += (w < wave) ? sm.g.wsum[w] : 0u;
+    ucnt += sm.g.wsum[w];
+  }
+  unsigned at = before + incl - mine;
+  while (any) {
+    const int e = __ffs(any) - 1;
+    any &= any - 1u;
+    unsigned m = 0u;
+#pragma unroll
+    for (int h = 0; h < NH; ++h) m |= ((hb[h] >> e) & 1u) << h;
+    sm.g.ulist[at++] = static_cast<unsigned>(j0 + tid * 8 + e) | (m << 24);
+  }
+  __syncthreads();
+
+  Acc<VEC> st[NH];
+#pragma unroll
+  for (int h = 0; h < NH; ++h) acc_init(st[h]);
+  const int64_t bgo = static_cast<int64_t>(b) * Hkv + g;
+  const typename E::T* sl = slab + bgo * S_max * d;
+  const typename E::T* rs = rest ? rest + bgo * S_max * (D - d) : nullptr;
+  const typename E::T* vv = val + bgo * S_max * D;
+  const float* srow = scores + (static_cast<int64_t>(b) * Hq + h0) * S;
+  // two tokens in flight per lane group at NH = 4 keeps the kernel within 128
+  // VGPRs (four waves per SIMD)
+  attend_loop<E, D, NH, true, (NH >= 4 ? 2 : 4)>(
+      [&](int t) { return static_cast<int>(sm.g.ulist[t] & 0xffffffu); },
+      [&](int h, int, int j) { return srow[static_cast<int64_t>(h) * S + j]; }, 0,
+      static_cast<int>(ucnt), sl, rs, vv, d, qf, scale_log2, st, -1, nullptr, nullptr,
+      [&](int t) { return sm.g.ulist[t] >> 24; });
+  __syncthreads();  // the merge buffer aliases the token list
+
+  merge_groups<E, D, NH>(st, sm.m, [&](int h, int dim, float M, float L, float A) {
+    const int64_t row = static_cast<int64_t>(b) * Hq + h0 + h;
+    if (nsplit == 1) {
+      out[row * D + dim] = A / L;
+    } else {
+      float* pp = part + (row * nsplit + split) * (D + 2);
+      pp[dim] = A;
+      if (dim == 0) {
+        pp[D] = M;
+        pp[D + 1] = L;
+      }
+    }
+  });
+}
+
+// Log-sum-exp merge of the nsplit slices of each row (a separate launch:
+// a device-wide fence in every attention workgroup would cost more on a
+// multi-XCD part, where each XCD's L2 must be written back).  The slice
+// weights exp(m_s - M) are computed once per row into LDS (dynamic, nsplit
+// floats); each thread then sums its output dims over the slices.
+constexpr int kCombineBlock = 128;
+constexpr int kCombineMaxSplit = 8192;
+
 template <int D>
-__global__ void __launch_bounds__(128) combine_kernel(const float* __restrict__ part,
-                                                     float* __restrict__ out, int nsplit) {
+__global__ void __launch_bounds__(kCombineBlock) combine_kernel(const float* __restrict__ part,
+                                                               float* __restrict__ out,
+                                                               int nsplit) {
+  extern __shared__ float cw[];
+  __shared__ float red[kCombineBlock / 64];
   const int64_t row = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float* pr = part + row * nsplit * (D + 2);
   float M = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, pr[s * (D + 2) + D]);
-  for (int dim = threadIdx.x; dim < D; dim += 128) {
-    float L = 0.f, A = 0.f;
-    for (int s = 0; s < nsplit; ++s) {
-      const float ms = pr[s * (D + 2) + D];
-      const float w = (ms == -INFINITY) ? 0.f : fast_exp2(ms - M);
-      L = fmaf(pr[s * (D + 2) + D + 1], w, L);
-      A = fmaf(pr[s * (D + 2) + dim], w, A);
-    }
+  for (int s = tid; s < nsplit; s += kCombineBlock) {
+    const float m = pr[s * (D + 2) + D];
+    cw[s] = m;
+    M = fmaxf(M, m);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+  if (lane == 0) red[wave] = M;
+  __syncthreads();
+  M = red[0];
+#pragma unroll
+  for (int w = 1; w < kCombineBlock / 64; ++w) M = fmaxf(M, red[w]);
+  __syncthreads();
+  float L = 0.f;
+  for (int s = tid; s < nsplit; s += kCombineBlock) {
+    const float m = cw[s];
+    const float w = (m == -INFINITY) ? 0.f : fast_exp2(m - M);
+    cw[s] = w;
+    L = fmaf(pr[s * (D + 2) + D + 1], w, L);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o);
+  if (lane == 0) red[wave] = L;
+  __syncthreads();
+  L = 0.f;
+#pragma unroll
+  for (int w = 0; w < kCombineBlock / 64; ++w) L += red[w];
+  for (int dim = tid; dim < D; dim += kCombineBlock) {
+    float A = 0.f;
+#pragma unroll 8
+    for (int s = 0; s < nsplit; ++s) A = fmaf(pr[s * (D + 2) + dim], cw[s], A);
     out[row * D + dim] = A / L;
   }
 }
@@ -315,6 +513,20 @@ hipError_t score_lps(const DecodeArgs& a, const float* qrot, float* scores) {
   }
 }
 
+hipError_t combine(const DecodeArgs& a, const float* part, int nsplit) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || nsplit == 1) return e;
+  if (nsplit > kCombineMaxSplit) return hipErrorInvalidValue;
+  const size_t lds = static_cast<size_t>(nsplit) * sizeof(float);
+  if (a.D == 64)
+    hipLaunchKernelGGL((combine_kernel<64>), dim3(a.B * a.Hq), dim3(kCombineBlock), lds, a.stream,
+                       part, a.out, nsplit);
+  else
+    hipLaunchKernelGGL((combine_kernel<128>), dim3(a.B * a.Hq), dim3(kCombineBlock), lds,
+                       a.stream, part, a.out, nsplit);
+  return hipGetLastError();
+}
+
 template <class E, int D, bool SPARSE>
 hipError_t attend_t(const DecodeArgs& a, const float* qrot, const float* scores, const int* idx,
                     int kk, float* part, int nsplit) {
@@ -325,8 +537,8 @@ hipError_t attend_t(const DecodeArgs& a, const float* qrot, const float* scores,
   if (SPARSE) {
     dim3 grid(a.B * a.Hq, nsplit);
     hipLaunchKernelGGL((attend_kernel<E, D, 1, true>), grid, dim3(kBlock), 0, a.stream, sl, rs, vv,
-                       qrot, scores, idx, part, a.out, a.Hq, a.Hkv, a.d, a.S, a.S_max, kk, nsplit,
-                       1, scale_log2);
+                       qrot, scores, idx, part, a.out, a.Hq, a.Hkv, a.d, a.S, a.S_max, kk,
+                       nsplit, 1, scale_log2);
   } else {
     const int G = a.Hq / a.Hkv;
     const int nh = G >= 4 ? 4 : (G >= 2 ? 2 : 1);
@@ -334,22 +546,37 @@ hipError_t attend_t(const DecodeArgs& a, const float* qrot, const float* scores,
     dim3 grid(a.B * a.Hkv * nhb, nsplit);
     if (nh == 4)
       hipLaunchKernelGGL((attend_kernel<E, D, 4, false>), grid, dim3(kBlock), 0, a.stream, sl, rs,
-                         vv, qrot, scores, idx, part, a.out, a.Hq, a.Hkv, a.d, a.S, a.S_max, kk,
-                         nsplit, nhb, scale_log2);
+                         vv, qrot, scores, idx, part, a.out, a.Hq, a.Hkv, a.d, a.S, a.S_max,
+                         kk, nsplit, nhb, scale_log2);
     else if (nh == 2)
       hipLaunchKernelGGL((attend_kernel<E, D, 2, false>), grid, dim3(kBlock), 0, a.stream, sl, rs,
-                         vv, qrot, scores, idx, part, a.out, a.Hq, a.Hkv, a.d, a.S, a.S_max, kk,
-                         nsplit, nhb, scale_log2);
+                         vv, qrot, scores, idx, part, a.out, a.Hq, a.Hkv, a.d, a.S, a.S_max,
+                         kk, nsplit, nhb, scale_log2);
     else
       hipLaunchKernelGGL((attend_kernel<E, D, 1, false>), grid, dim3(kBlock), 0, a.stream, sl, rs,
-                         vv, qrot, scores, idx, part, a.out, a.Hq, a.Hkv, a.d, a.S, a.S_max, kk,
-                         nsplit, nhb, scale_log2);
+                         vv, qrot, scores, idx, part, a.out, a.Hq, a.Hkv, a.d, a.S, a.S_max,
+                         kk, nsplit, nhb, scale_log2);
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || nsplit == 1) return e;
-  hipLaunchKernelGGL((combine_kernel<D>), dim3(a.B * a.Hq), dim3(128), 0, a.stream, part, a.out,
-                     nsplit);
-  return hipGetLastError();
+  return combine(a, part, nsplit);
+}
+
+template <class E, int D>
+hipError_t union_t(const DecodeArgs& a, const float* qrot, const float* scores,
+                   const unsigned* bits, float* part, int nsplit) {
+  const float scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(D)));
+  const int R = ((a.S + nsplit - 1) / nsplit + 31) / 32 * 32;
+  if (R > kUnionMax) return hipErrorInvalidValue;
+  dim3 grid(a.B * a.Hkv, nsplit);
+  const int G = a.Hq / a.Hkv;
+  if (G == 4)
+    hipLaunchKernelGGL((attend_union_kernel<E, D, 4>), grid, dim3(kBlock), 0, a.stream,
+                       cptr<E>(a.k_slab), cptr<E>(a.k_rest), cptr<E>(a.v), qrot, scores, bits, part,
+                       a.out, a.Hq, a.Hkv, a.d, a.S, a.S_max, R, nsplit, scale_log2);
+  else
+    hipLaunchKernelGGL((attend_union_kernel<E, D, 2>), grid, dim3(kBlock), 0, a.stream,
+                       cptr<E>(a.k_slab), cptr<E>(a.k_rest), cptr<E>(a.v), qrot, scores, bits, part,
+                       a.out, a.Hq, a.Hkv, a.d, a.S, a.S_max, R, nsplit, scale_log2);
+  return combine(a, part, nsplit);
 }
 
 }  // namespace
@@ -366,20 +593,21 @@ hipError_t launch_scores(const DecodeArgs& a, const float* qrot, float* scores) 
 int topk_block_for(int S) { return S <= 4096 ? 256 : (S <= 8192 ? 512 : 1024); }
 
 hipError_t launch_topk(const float* scores, int rows, int S, int64_t ld, int k, int* idx,
-                       hipStream_t stream) {
+                       hipStream_t stream, unsigned* bits) {
   const int blk = topk_block_for(S);
   const size_t lds_bytes = static_cast<size_t>(S) * sizeof(float);
   const int use_lds = (lds_bytes <= kTopkLdsMax) && (ld % 4 == 0) ? 1 : 0;
-  const size_t dyn = use_lds ? lds_bytes : 0;
+  const size_t dyn = (use_lds ? lds_bytes : 0) +
+                     (bits ? static_cast<size_t>((S + 31) >> 5) * sizeof(unsigned) : 0);
   if (blk == 256)
     hipLaunchKernelGGL((topk_kernel<256>), dim3(rows), dim3(256), dyn, stream, scores, S, ld, k, idx,
-                       use_lds);
+                       use_lds, bits);
   else if (blk == 512)
     hipLaunchKernelGGL((topk_kernel<512>), dim3(rows), dim3(512), dyn, stream, scores, S, ld, k, idx,
-                       use_lds);
+                       use_lds, bits);
   else
     hipLaunchKernelGGL((topk_kernel<1024>), dim3(rows), dim3(1024), dyn, stream, scores, S, ld, k,
-                       idx, use_lds);
+                       idx, use_lds, bits);
   return hipGetLastError();
 }
 
@@ -397,6 +625,15 @@ hipError_t launch_attend(const DecodeArgs& a, const float* qrot, const float* sc
                   : attend_t<BF16, 64, false>(a, qrot, scores, idx, kk, part, nsplit);
   return sparse ? attend_t<BF16, 128, true>(a, qrot, scores, idx, kk, part, nsplit)
                 : attend_t<BF16, 128, false>(a, qrot, scores, idx, kk, part, nsplit);
+}
+
+hipError_t launch_attend_union(const DecodeArgs& a, const float* qrot, const float* scores,
+                               const unsigned* bits, float* part, int nsplit) {
+  if (a.dtype == kF32)
+    return a.D == 64 ? union_t<F32, 64>(a, qrot, scores, bits, part, nsplit)
+                     : union_t<F32, 128>(a, qrot, scores, bits, part, nsplit);
+  return a.D == 64 ? union_t<BF16, 64>(a, qrot, scores, bits, part, nsplit)
+                   : union_t<BF16, 128>(a, qrot, scores, bits, part, nsplit);
 }
 
 }  // namespace loki

@@ -29,12 +29,22 @@ struct DecodeArgs {
 
 hipError_t launch_rotate(const DecodeArgs& a, float* qrot);
 hipError_t launch_scores(const DecodeArgs& a, const float* qrot, float* scores);
+// bits (optional): also write each row's kept-position bitmap, ceil(S/32)
+// words per row, bit j%32 of word j/32 set when token j is kept
 hipError_t launch_topk(const float* scores, int rows, int S, int64_t ld, int k, int* idx,
-                       hipStream_t stream);
+                       hipStream_t stream, unsigned* bits = nullptr);
 // sparse: attention over idx (k_eff = kk per row, scores from `scores`);
 // dense: over all S tokens.  nsplit > 1 writes `part` and combines into out.
 hipError_t launch_attend(const DecodeArgs& a, const float* qrot, const float* scores,
                          const int* idx, int kk, float* part, int nsplit, bool sparse);
+// grouped-query sparse attention over the union of the G = Hq/Hkv heads' kept
+// tokens (G in {2, 4}), read from their kept-position bitmaps; nsplit position
+// ranges of at most kUnionMaxTok tokens
+constexpr int kUnionMaxTok = 1024;
+// longest context the union gather takes (bitmap row in LDS: S/8 bytes)
+constexpr int kUnionMaxS = 1 << 17;
+hipError_t launch_attend_union(const DecodeArgs& a, const float* qrot, const float* scores,
+                               const unsigned* bits, float* part, int nsplit);
 size_t fused_lds_bytes(int D, int S, int kk);
 hipError_t launch_fused(const DecodeArgs& a, int kk);
 // append (k_new, v_new [B, Hkv, D]) at pos and decode over a.S = pos + 1

@@ -88,6 +88,20 @@ def test_decode_fused_rejects_when_lds_too_small(L):
     assert lib.loki_decode_path(1, 4, 4, 128, 33, 100, 25, 0) == -4
 
 
+def test_union_path_only_for_two_or_four_heads_per_kv_head(L):
+    lib = L.load()
+    assert lib.loki_decode_path(8, 32, 8, 128, 32, 8192, 2048, 3) == 3    # G = 4
+    assert lib.loki_decode_path(2, 8, 4, 128, 32, 700, 100, 3) == 3       # G = 2
+    assert lib.loki_decode_path(2, 8, 8, 128, 32, 700, 100, 3) == -4      # G = 1
+    assert lib.loki_decode_path(2, 16, 2, 128, 32, 700, 100, 3) == -4     # G = 8
+    assert lib.loki_decode_path(1, 4, 1, 128, 32, 1 << 17, 100, 3) == 3
+    assert lib.loki_decode_path(1, 4, 1, 128, 32, (1 << 17) + 1, 100, 3) == -4
+    assert lib.loki_decode_path(1, 4, 1, 128, 32, 100, 10, 4) == -1       # no such path
+    # rejected before any pointer is looked at
+    assert _decode(lib, Hq=4, Hkv=4, path=3) == -4
+    assert _decode(lib, path=4) == -1
+
+
 def test_empty_batch_is_a_noop(L):
     lib = L.load()
     assert _decode(lib, B=0) == 0

@@ -33,7 +33,14 @@ SMALL = {
     "long_20000": (synth.custom("long_20000", 110, B=1, Hq=2, Hkv=1, S=20000, d=64, k_f=0.125,
                                 tau=48.0), 20000, 20000),
     "f32_D128": (synth.custom("f32_D128", 111, B=2, Hq=2, Hkv=2, S=600, dtype="f32", d=16), 600, 640),
+    "gqa4_f32": (synth.custom("gqa4_f32", 112, B=2, Hq=8, Hkv=2, D=64, d=16, S=900, dtype="f32",
+                              tau=8.0), 900, 960),
 }
+
+
+def union_applies(w):
+    """The union gather takes 2 or 4 query heads per KV head."""
+    return w.Hq // w.Hkv in (2, 4)
 
 _cases = {}
 
@@ -123,14 +130,16 @@ def test_attend_given_indices_matches_oracle(lib, name):
 
 # ------------------------------------------------------------- end to end --
 
-@pytest.mark.parametrize("path", [1, 2], ids=["fused", "split"])
+@pytest.mark.parametrize("path", [1, 2, 3], ids=["fused", "split", "union"])
 @pytest.mark.parametrize("name", sorted(SMALL))
 def test_decode_matches_oracle(lib, name, path):
     c = case(name)
-    cache = device_cache(lib, c)
     kk = min(c.k, c.S)
     if path == 1 and (c.w.D + c.S + kk) * 4 > 56 * 1024:
         pytest.skip("fused path needs q', scores and kept ids within 56 KiB of LDS")
+    if path == 3 and not union_applies(c.w):
+        pytest.skip("union gather needs 2 or 4 query heads per KV head")
+    cache = device_cache(lib, c)
     out, idx = lib.decode(_q(c), cache, _P(c), c.k, path=path)
     out, idx = out.cpu().numpy(), idx.cpu().numpy()
     ref_out, ref_idx, ref_s = oracle.decode(c.q, c.slab, c.rest, c.v, c.P, c.k, c.w.dtype, S=c.S)
@@ -143,7 +152,7 @@ def test_decode_budget_edges(lib, k):
     c = case("ragged_gqa2")
     cache = device_cache(lib, c)
     ref_out, ref_idx, ref_s = oracle.decode(c.q, c.slab, c.rest, c.v, c.P, k, c.w.dtype, S=c.S)
-    for path in (1, 2):
+    for path in (1, 2, 3):
         out, idx = lib.decode(_q(c), cache, _P(c), k, path=path)
         check_decode(c.w.dtype, k, out.cpu().numpy(), idx.cpu().numpy(), ref_out, ref_idx, ref_s,
                      all_pairs(c.w))
@@ -155,7 +164,7 @@ def test_decode_shorter_S_than_filled(lib):
     cache = device_cache(lib, c)
     S = 1234
     ref_out, ref_idx, ref_s = oracle.decode(c.q, c.slab, c.rest, c.v, c.P, 300, c.w.dtype, S=S)
-    for path in (1, 2):
+    for path in (1, 2, 3):
         out, idx = lib.decode(_q(c), cache, _P(c), 300, S=S, path=path)
         check_decode(c.w.dtype, 300, out.cpu().numpy(), idx.cpu().numpy(), ref_out, ref_idx,
                      ref_s, all_pairs(c.w))
@@ -167,11 +176,16 @@ def test_decode_deterministic_and_paths_agree(lib):
     o1, i1 = lib.decode(_q(c), cache, _P(c), c.k, path=2)
     o2, i2 = lib.decode(_q(c), cache, _P(c), c.k, path=2)
     o3, i3 = lib.decode(_q(c), cache, _P(c), c.k, path=1)
+    o4, i4 = lib.decode(_q(c), cache, _P(c), c.k, path=3)
+    o5, _ = lib.decode(_q(c), cache, _P(c), c.k, path=3)
     assert np.array_equal(o1.cpu().numpy(), o2.cpu().numpy())
     assert np.array_equal(i1.cpu().numpy(), i2.cpu().numpy())
-    # same float32 scores on both paths -> same selection
+    assert np.array_equal(o4.cpu().numpy(), o5.cpu().numpy())
+    # same float32 scores on every path -> same selection
     assert np.array_equal(i1.cpu().numpy(), i3.cpu().numpy())
+    assert np.array_equal(i1.cpu().numpy(), i4.cpu().numpy())
     assert np.max(np.abs(o1.cpu().numpy() - o3.cpu().numpy())) < 1e-5
+    assert np.max(np.abs(o1.cpu().numpy() - o4.cpu().numpy())) < 1e-5
 
 
 # ------------------------------------------------------------------ append --
@@ -232,15 +246,17 @@ def test_dense_matches_oracle(lib, name):
 FULL = ["l2_7b", "l2_13b_run", "l3_8b_gqa", "mistral_32k"]
 
 
-@pytest.mark.parametrize("name", FULL)
-def test_full_size_decode_sampled(lib, name):
+@pytest.mark.parametrize("name,path", [(n, 0) for n in FULL] +
+                         [("l3_8b_gqa", 3), ("mistral_32k", 3)])
+def test_full_size_decode_sampled(lib, name, path):
     """Full benchmark shapes, launched exactly as the benchmark launches them
-    (AUTO path); 16 sampled (sequence, head) pairs checked against the
-    oracle, plus properties that hold for every pair."""
+    (AUTO path; the union gather too for the grouped-query shapes); 16
+    sampled (sequence, head) pairs checked against the oracle, plus
+    properties that hold for every pair."""
     w = synth.WORKLOADS[name]
     c = make_case(w)
     cache = device_cache(lib, c)
-    out, idx = lib.decode(_q(c), cache, _P(c), w.k)
+    out, idx = lib.decode(_q(c), cache, _P(c), w.k, path=path)
     out, idx = out.cpu().numpy(), idx.cpu().numpy()
     pairs = sample_pairs(w, 16, seed=w.wid)
     ref_out, ref_idx, ref_s = oracle.decode(c.q, c.slab, c.rest, c.v, c.P, w.k, w.dtype, heads=pairs)
@@ -275,13 +291,15 @@ def _oracle_token(w, P, kn, vn):
     return slab, rest, vv
 
 
-@pytest.mark.parametrize("path", [1, 2], ids=["fused", "split"])
+@pytest.mark.parametrize("path", [1, 2, 3], ids=["fused", "split", "union"])
 @pytest.mark.parametrize("name", sorted(STEP_CASES))
 def test_decode_step_matches_oracle(lib, name, path):
     """Append at pos = S-1 and decode over S tokens in one call; the written
     slot equals the oracle's append and the decode equals the oracle's decode
     over the oracle's full cache."""
     w = STEP_CASES[name]
+    if path == 3 and not union_applies(w):
+        pytest.skip("union gather needs 2 or 4 query heads per KV head")
     S = w.S
     c = make_case(w, S - 1, S + 3) if S > 1 else None
     from gpu_cases import basis
