@@ -125,7 +125,13 @@ __global__ void __launch_bounds__(kBlock) score_kernel(const typename E::T* __re
 
 // Dynamic LDS: the score row (when use_lds) followed by the kept-position
 // bitmap (when `bits` is given: ceil(S/32) words per row, written out for
-// the union gather).
+// the union gather).  The row is staged with coalesced loads, one pad word
+// after every 32 scores, so that the register-resident select, where each
+// thread takes a contiguous run of up to 32 scores, reads it without bank
+// conflicts.  Once the keys are in registers the row's LDS is dead and
+// collects the kept ids, which are written out coalesced at the end.
+__host__ __device__ constexpr int topk_padded(int S) { return S + (S >> 5) + 1; }
+
 template <int BLOCK>
 __global__ void __launch_bounds__(BLOCK) topk_kernel(const float* __restrict__ scores, int S,
                                                      int64_t ld, int k, int* __restrict__ idx,
@@ -134,25 +140,43 @@ __global__ void __launch_bounds__(BLOCK) topk_kernel(const float* __restrict__ s
   extern __shared__ float sbuf[];
   const int row = blockIdx.x;
   const int nw = (S + 31) >> 5;
-  unsigned* lbits = reinterpret_cast<unsigned*>(sbuf + (use_lds ? S : 0));
+  unsigned* lbits = reinterpret_cast<unsigned*>(sbuf + (use_lds ? topk_padded(S) : 0));
   if (bits)
     for (int i = threadIdx.x; i < nw; i += BLOCK) lbits[i] = 0u;
   const float* s = scores + static_cast<int64_t>(row) * ld;
   int* out = idx + static_cast<int64_t>(row) * k;
+  // the register-resident select reads the row only before its first barrier
+  const bool stage_out = use_lds && S <= BLOCK * 32;
+  int* lidx = reinterpret_cast<int*>(sbuf);
   auto emit = [&](int p, int j) {
-    out[p] = j;
+    if (stage_out)
+      lidx[p] = j;
+    else
+      out[p] = j;
     if (bits) atomicOr(&lbits[j >> 5], 1u << (j & 31));
   };
   if (use_lds) {
     const int n4 = S >> 2;
     const float4* s4 = reinterpret_cast<const float4*>(s);
-    for (int i = threadIdx.x; i < n4; i += BLOCK) reinterpret_cast<float4*>(sbuf)[i] = s4[i];
-    for (int i = (n4 << 2) + threadIdx.x; i < S; i += BLOCK) sbuf[i] = s[i];
+    for (int i = threadIdx.x; i < n4; i += BLOCK) {
+      const float4 x = s4[i];
+      float* dst = sbuf + 4 * i + (i >> 3);  // 4 scores never straddle a pad word
+      dst[0] = x.x;
+      dst[1] = x.y;
+      dst[2] = x.z;
+      dst[3] = x.w;
+    }
+    for (int i = (n4 << 2) + threadIdx.x; i < S; i += BLOCK) sbuf[i + (i >> 5)] = s[i];
     __syncthreads();
-    block_select_topk_any<BLOCK>([&](int j) { return sbuf[j]; }, S, k, emit, sm);
+    block_select_topk_any<BLOCK>([&](int j) { return sbuf[j + (j >> 5)]; }, S, k, emit, sm);
   } else {
     __syncthreads();
     block_select_topk_any<BLOCK>([&](int j) { return s[j]; }, S, k, emit, sm);
+  }
+  if (stage_out) {
+    __syncthreads();
+    const int kk = min(k, S);
+    for (int p = threadIdx.x; p < kk; p += BLOCK) out[p] = lidx[p];
   }
   if (bits) {
     __syncthreads();
@@ -595,7 +619,7 @@ int topk_block_for(int S) { return S <= 4096 ? 256 : (S <= 8192 ? 512 : 1024); }
 hipError_t launch_topk(const float* scores, int rows, int S, int64_t ld, int k, int* idx,
                        hipStream_t stream, unsigned* bits) {
   const int blk = topk_block_for(S);
-  const size_t lds_bytes = static_cast<size_t>(S) * sizeof(float);
+  const size_t lds_bytes = static_cast<size_t>(topk_padded(S)) * sizeof(float);
   const int use_lds = (lds_bytes <= kTopkLdsMax) && (ld % 4 == 0) ? 1 : 0;
   const size_t dyn = (use_lds ? lds_bytes : 0) +
                      (bits ? static_cast<size_t>((S + 31) >> 5) * sizeof(unsigned) : 0);

@@ -11,7 +11,7 @@ namespace loki {
 
 constexpr int kF32 = 0;
 constexpr int kBF16 = 1;
-constexpr size_t kTopkLdsMax = 48 * 1024;    // scores staged in LDS up to this size
+constexpr size_t kTopkLdsMax = 136 * 1024;   // scores staged in LDS up to this size
 constexpr size_t kFusedLdsMax = 56 * 1024;   // fused path: q' + scores + kept ids (dynamic LDS)
 
 struct DecodeArgs {

@@ -156,6 +156,46 @@ __device__ __forceinline__ unsigned block_excl_scan(unsigned x, unsigned& total,
   return before + incl - x;
 }
 
+// Final compaction of the register-resident selects, in index order.  Key
+// e of the calling thread (element j0 + e) is kept when its masked value is
+// above `prefix`, or equal to it and among the first krem such keys in
+// index order.  One scan of the above-threshold counts and one of the
+// at-threshold counts give each thread its first output position; the
+// thread then writes its kept elements by walking the set bits of a keep
+// mask.
+template <int BLOCK, int EMAX, class Emit>
+__device__ __forceinline__ void emit_kept(const uint32_t (&key)[EMAX], int nvalid, uint32_t prefix,
+                                          uint32_t mask, int krem, int j0, Emit emit,
+                                          SelectSmemR<BLOCK>& sm, int buf) {
+  static_assert(EMAX <= 32, "one keep mask bit per key");
+  uint32_t gtm = 0u, eqm = 0u;
+#pragma unroll
+  for (int e = 0; e < EMAX; ++e) {
+    const uint32_t m = key[e] & mask;
+    const uint32_t live = e < nvalid ? 1u : 0u;
+    gtm |= (live & static_cast<uint32_t>(m > prefix)) << e;
+    eqm |= (live & static_cast<uint32_t>(m == prefix)) << e;
+  }
+  const int ngt = __popc(gtm), neq = __popc(eqm);
+  unsigned tot;
+  const int gt_before = static_cast<int>(block_excl_scan<BLOCK>(ngt, tot, sm, buf));
+  const int eq_before = static_cast<int>(block_excl_scan<BLOCK>(neq, tot, sm, buf ^ 1));
+  // this thread keeps its first `take` equal keys
+  const int take = max(0, min(neq, krem - eq_before));
+  uint32_t keep = gtm;
+  uint32_t rest = eqm;
+  for (int i = 0; i < take; ++i) {
+    keep |= rest & (0u - rest);  // lowest set bit
+    rest &= rest - 1u;
+  }
+  int pos = gt_before + min(eq_before, krem);
+  while (keep) {
+    const int e = __ffs(keep) - 1;
+    keep &= keep - 1u;
+    emit(pos++, j0 + e);
+  }
+}
+
 template <int BLOCK, int EMAX, class Src, class Emit>
 __device__ void block_select_topk_reg(Src src, int S, int k, Emit emit, SelectSmemR<BLOCK>& sm) {
   constexpr int PER = kSelBins / BLOCK;  // histogram bins owned per thread in the scan
@@ -218,29 +258,7 @@ __device__ void block_select_topk_reg(Src src, int S, int k, Emit emit, SelectSm
     }
   }
 
-  unsigned ngt = 0u, neq = 0u;
-#pragma unroll
-  for (int e = 0; e < EMAX; ++e) {
-    if (e < nvalid) {
-      const uint32_t m = key[e] & mask;
-      ngt += m > prefix;
-      neq += m == prefix;
-    }
-  }
-  unsigned tot;
-  const unsigned gt_before = block_excl_scan<BLOCK>(ngt, tot, sm, buf);
-  buf ^= 1;
-  unsigned eq_before = block_excl_scan<BLOCK>(neq, tot, sm, buf);
-  int pos = static_cast<int>(gt_before) + min(static_cast<int>(eq_before), krem);
-#pragma unroll
-  for (int e = 0; e < EMAX; ++e) {
-    if (e < nvalid) {
-      const uint32_t m = key[e] & mask;
-      const bool eq = m == prefix;
-      if (m > prefix || (eq && static_cast<int>(eq_before) < krem)) emit(pos++, j0 + e);
-      eq_before += eq;
-    }
-  }
+  emit_kept<BLOCK, EMAX>(key, nvalid, prefix, mask, krem, j0, emit, sm, buf);
 }
 
 }  // namespace loki
@@ -384,29 +402,7 @@ __device__ void block_select_topk_hist(Src src, int S, int k, const unsigned* hi
 
   // compaction in index order: one scan of the above-threshold counts and
   // one of the at-threshold counts
-  unsigned ngt = 0u, neq = 0u;
-#pragma unroll
-  for (int e = 0; e < EMAX; ++e) {
-    if (e < nvalid) {
-      const uint32_t m = key[e] & mask;
-      ngt += m > prefix;
-      neq += m == prefix;
-    }
-  }
-  unsigned tot;
-  const unsigned gt_before = block_excl_scan<BLOCK>(ngt, tot, sm, buf);
-  buf ^= 1;
-  unsigned eq_before = block_excl_scan<BLOCK>(neq, tot, sm, buf);
-  int pos = static_cast<int>(gt_before) + min(static_cast<int>(eq_before), krem);
-#pragma unroll
-  for (int e = 0; e < EMAX; ++e) {
-    if (e < nvalid) {
-      const uint32_t m = key[e] & mask;
-      const bool eq = m == prefix;
-      if (m > prefix || (eq && static_cast<int>(eq_before) < krem)) emit(pos++, j0 + e);
-      eq_before += eq;
-    }
-  }
+  emit_kept<BLOCK, EMAX>(key, nvalid, prefix, mask, krem, j0, emit, sm, buf);
 }
 
 }  // namespace loki

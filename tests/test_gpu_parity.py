@@ -85,6 +85,7 @@ TOPK_CASES = [
     ("dup", 777, 780, 300), ("dup", 5000, 5000, 2500), ("dup", 20000, 20000, 1),
     ("zeros", 300, 300, 150), ("zeros", 9000, 9000, 4000), ("sorted", 2048, 2048, 512),
     ("normal", 50, 52, 50), ("normal", 50, 52, 70), ("normal", 1, 4, 1), ("normal", 33, 36, 32),
+    ("dup", 32768, 32768, 16384), ("normal", 32769, 32772, 4096), ("normal", 40000, 40000, 5000),
 ]
 
 
