@@ -81,6 +81,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-run", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-read-probe", action="store_true")
     ap.add_argument("--no-jaccard", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="first run a plain device copy of this size (counter calibration)")
@@ -239,6 +240,22 @@ def main():
         "decode_only": {"head_queries_per_s": hq / (dec_avg_ms * 1e-3), "avg_ms": dec_avg_ms,
                         "achieved_GBs": by["total"] / (dec_avg_ms * 1e-3) / 1e9},
     }
+
+    # ---- the practical read ceiling: the library's streaming-read probe over
+    # 4 GiB (16x the last-level cache), best of three launch widths
+    if not args.no_read_probe:
+        buf = torch.zeros(4 << 30, dtype=torch.uint8, device=dev)
+        best = 0.0
+        for wg in (1024, 2048, 4096):
+            sink = torch.empty(wg * 256, dtype=torch.float32, device=dev)
+            for _ in range(2):
+                loki.stream_read(buf, sink, wg)
+            _, rms = timed(lambda i: loki.stream_read(buf, sink, wg), 10)
+            best = max(best, buf.numel() / (rms * 1e-3) / 1e9)
+        del buf
+        result["roofline"]["measured_stream_read_GBs"] = best
+        result["roofline"]["frac_of_measured_stream_read"] = achieved / best
+        log(f"streaming-read probe {best:.0f} GB/s; step at {achieved / best:.3f} of it")
 
     # ---- grouped-query shapes: the union gather on the same caches
     if w.Hq // w.Hkv in (2, 4) and path_name != "union":

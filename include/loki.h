@@ -204,6 +204,15 @@ int loki_dense_decode(const void* q, const void* k_slab, const void* k_rest, con
                       int32_t S, int32_t S_max, int32_t dtype, float* out,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/* Measurement helper, not part of the method: reads `bytes` of device memory
+ * at buf (16-byte aligned, bytes a multiple of 16) with nontemporal 16-byte
+ * loads in a grid-stride loop of `workgroups` workgroups of 256 threads, and
+ * writes one float per thread (the sum of what it read) to sink (device,
+ * workgroups * 256 floats).  Timing it gives the HBM read rate a plain
+ * streaming kernel reaches on the device, the practical ceiling next to the
+ * published peak.  1 <= workgroups <= 65536. */
+int loki_stream_read(const void* buf, size_t bytes, float* sink, int32_t workgroups, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -43,6 +43,7 @@ _SIGS = {
                                            _I, _P, _P, ctypes.c_size_t, _P]),
     "loki_dense_decode": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P,
                                          _P, ctypes.c_size_t, _P]),
+    "loki_stream_read": (ctypes.c_int, [_P, ctypes.c_size_t, _P, _I, _P]),
 }
 
 _lib = None
@@ -306,6 +307,20 @@ def dense_decode(q, cache: KVCache, P, S: int | None = None, out=None, workspace
                                _stream(q))
     _check(st, "loki_dense_decode")
     return out
+
+
+def stream_read(buf, sink, workgroups: int):
+    """Measurement helper: read all of `buf` (a contiguous device tensor whose
+    byte size is a multiple of 16) with the library's streaming-read probe;
+    `sink` is a float32 device tensor of at least workgroups * 256 entries."""
+    torch = _torch()
+    _need(buf, "buf")
+    _need(sink, "sink", torch.float32)
+    if sink.numel() < workgroups * 256:
+        raise ValueError("sink needs workgroups * 256 floats")
+    st = load().loki_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
+                                 workgroups, _stream(buf))
+    _check(st, "loki_stream_read")
 
 
 # ------------------------------------------------- pre-marshalled calls --

@@ -18,7 +18,8 @@ OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libloki.so")
 
 ARCH = os.environ.get("LOKI_OFFLOAD_ARCH", "gfx950")
-HIP_SOURCES = ["decode_kernels.hip", "fused_kernels.hip", "append_kernels.hip", "api.hip"]
+HIP_SOURCES = ["decode_kernels.hip", "fused_kernels.hip", "append_kernels.hip", "probe_kernels.hip",
+               "api.hip"]
 CXX_SOURCES = ["calibrate.cpp"]
 # Packed-FP32 instructions are disabled for all device code.
 HIPCC_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",

@@ -372,4 +372,14 @@ int loki_dense_decode(const void* q, const void* k_slab, const void* k_rest, con
   return status_of(e);
 }
 
+int loki_stream_read(const void* buf, size_t bytes, float* sink, int32_t workgroups,
+                     void* stream) {
+  if (workgroups < 1 || workgroups > 65536 || bytes % 16 != 0) return LOKI_EINVAL;
+  if (bytes == 0) return LOKI_OK;
+  if (!buf || !sink || !aligned16(buf) || (reinterpret_cast<uintptr_t>(sink) & 3u))
+    return LOKI_EINVAL;
+  return status_of(loki::launch_stream_read(buf, bytes, sink, workgroups,
+                                            static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

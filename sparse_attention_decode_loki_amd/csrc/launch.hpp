@@ -55,4 +55,9 @@ hipError_t launch_append(const void* k_new, const void* v_new, const float* P, v
                          void* k_rest, void* v, int B, int Hkv, int D, int d, int S_max, int pos,
                          int T, int dtype, hipStream_t stream);
 
+// streaming read of bytes (multiple of 16) with nontemporal 16-byte loads;
+// sink receives workgroups * 256 floats
+hipError_t launch_stream_read(const void* buf, size_t bytes, float* sink, int workgroups,
+                              hipStream_t stream);
+
 }  // namespace loki

@@ -173,3 +173,13 @@ def test_calibrate_small_and_degenerate(L):
     P1 = np.zeros(1, np.float32)
     assert lib.loki_calibrate(np.ones(1, np.float32).ctypes.data, 1, 1, P1.ctypes.data, None) == -1
     assert lib.loki_calibrate(None, 5, 1, P1.ctypes.data, None) == -1
+
+
+def test_stream_read_rejects_bad_arguments(L):
+    lib = L.load()
+    assert lib.loki_stream_read(FAKE, 1024, FAKE, 0, None) == -1
+    assert lib.loki_stream_read(FAKE, 1024, FAKE, 65537, None) == -1
+    assert lib.loki_stream_read(FAKE, 1000, FAKE, 4, None) == -1
+    assert lib.loki_stream_read(None, 1024, FAKE, 4, None) == -1
+    assert lib.loki_stream_read(FAKE_MIS, 1024, FAKE, 4, None) == -1
+    assert lib.loki_stream_read(FAKE, 0, FAKE, 4, None) == 0

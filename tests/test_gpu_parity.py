@@ -391,3 +391,18 @@ def test_decode_exact_ties_from_repeated_rows(lib, S, k, nrows):
         out = out.cpu().numpy()
         for b, h in all_pairs(w):
             assert out_error(w.dtype, out[b, h], ref_out[b, h]) <= TOL[w.dtype]
+
+
+# ------------------------------------------------------- measurement helper --
+
+def test_stream_read_probe_reads_every_element(lib):
+    """The streaming-read probe's per-thread sums add up to the sum of the
+    buffer, so every 16-byte chunk was read exactly once."""
+    import torch
+    n = (1 << 20) + 12  # float32 elements: a ragged tail for the grid-stride loop
+    buf = torch.arange(n, dtype=torch.float32, device="cuda") % 7
+    for wg in (1, 3, 64):
+        sink = torch.full((wg * 256,), float("nan"), dtype=torch.float32, device="cuda")
+        lib.stream_read(buf, sink, wg)
+        got = sink.double().sum().item()
+        assert got == float((torch.arange(n, dtype=torch.float64) % 7).sum())
