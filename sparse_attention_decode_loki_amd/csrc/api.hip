@@ -237,8 +237,7 @@ int loki_decode_ex(const void* q, const void* k_slab, const void* k_rest, const 
   float* scores = reinterpret_cast<float*>(ws + L.scores);
   float* part = reinterpret_cast<float*>(ws + L.part);
   unsigned* bits = reinterpret_cast<unsigned*>(ws + L.bits);
-  hipError_t e = loki::launch_rotate(a, qrot);
-  if (e == hipSuccess) e = loki::launch_scores(a, qrot, scores);
+  hipError_t e = loki::launch_scores(a, qrot, scores);
   if (e == hipSuccess)
     e = loki::launch_topk(scores, rows, S, S, kk, idx, a.stream, uni ? bits : nullptr);
   if (e == hipSuccess)
@@ -304,8 +303,7 @@ int loki_scores(const void* q, const void* k_slab, const float* P, int32_t B, in
   DecodeArgs a = make_args(q, k_slab, nullptr, k_slab, P, B, Hq, Hkv, D, d, S, S_max, dtype,
                            nullptr, nullptr, stream);
   float* qrot = static_cast<float*>(workspace);
-  hipError_t e = loki::launch_rotate(a, qrot);
-  if (e == hipSuccess) e = loki::launch_scores(a, qrot, scores);
+  hipError_t e = loki::launch_scores(a, qrot, scores);
   return status_of(e);
 }
 
@@ -341,8 +339,7 @@ int loki_attend_indices(const void* q, const void* k_slab, const void* k_rest, c
   float* qrot = reinterpret_cast<float*>(ws + L.qrot);
   float* scores = reinterpret_cast<float*>(ws + L.scores);
   float* part = reinterpret_cast<float*>(ws + L.part);
-  hipError_t e = loki::launch_rotate(a, qrot);
-  if (e == hipSuccess) e = loki::launch_scores(a, qrot, scores);
+  hipError_t e = loki::launch_scores(a, qrot, scores);
   if (e == hipSuccess) e = loki::launch_attend(a, qrot, scores, idx, k, part, nsplit, true);
   return status_of(e);
 }

@@ -9,8 +9,10 @@
 // wide coalesced loads and no matrix cores.
 //
 // Kernels:
-//   rotate_kernel   q' = q . P[g] for all query heads of one KV head
-//   score_kernel    s_j over a chunk of the key slab for up to 4 query heads
+//   rotate_kernel   q' = q . P[g] for all query heads of one KV head (dense
+//                   baseline)
+//   score_kernel    q' and s_j over a chunk of the key slab for up to 4 query
+//                   heads; chunk 0 also stores q' for the attention kernels
 //   topk_kernel     exact top-k of one score row, ascending indices
 //   attend_kernel   gather + online softmax over a slice of the kept tokens
 //                   (also the dense baseline, with all tokens)
@@ -89,33 +91,90 @@ __global__ void __launch_bounds__(kBlock) rotate_kernel(const typename E::T* __r
 
 constexpr int kScoreChunk = 1024;  // tokens per score workgroup
 
-template <class E, int LPS, int NH>
+// Grid (B*Hkv*nhb, ceil(S / kScoreChunk)).  Workgroup (bg*nhb + hb, chunk)
+// scores tokens [chunk*kScoreChunk, +kScoreChunk) for the NH query heads
+// hb*NH.. of KV head g.  The queries are rotated here: the slab loads are
+// issued first, then q' = q . P[g] is formed exactly as rotate_kernel and the
+// fused kernel form it (thread (cq, rb) adds rows [rb*RB, rb*RB + RB) of
+// columns 4*cq .. +3 in order, then the NRB partials are added in order), so
+// every path ranks with the same float32 q'.  Chunk-0 workgroups form all D
+// columns and store q' for the attention kernel; the others form only the d
+// columns that ranking needs.
+template <class E, int D, int LPS, int NH>
 __global__ void __launch_bounds__(kBlock) score_kernel(const typename E::T* __restrict__ slab,
-                                                       const float* __restrict__ qrot,
+                                                       const typename E::T* __restrict__ q,
+                                                       const float* __restrict__ P,
+                                                       float* __restrict__ qrot,
                                                        float* __restrict__ scores, int Hq, int Hkv,
-                                                       int D, int d, int S, int S_max, int nhb) {
+                                                       int d, int S, int S_max, int nhb) {
   constexpr int VEC = E::VEC;
+  constexpr int CQ = D / 4;         // column quads of P
+  constexpr int NRB = kBlock / CQ;  // row blocks of P
+  constexpr int RB = D / NRB;       // rows per block
+  __shared__ float qin[NH][D];
+  __shared__ float red[NRB][NH][D];
+  __shared__ float qr[NH][D];
   const int G = Hq / Hkv;
   const int bg = blockIdx.x / nhb;
   const int hb = blockIdx.x % nhb;
   const int b = bg / Hkv, g = bg % Hkv;
   const int h0 = g * G + hb * NH;
   const int nh = min(NH, G - hb * NH);
+  const int j0 = blockIdx.y * kScoreChunk;
+  const int j1 = min(S, j0 + kScoreChunk);
+  const typename E::T* sl = slab + static_cast<int64_t>(bg) * S_max * d;
+  Chunk c[4];
+  score_first<E, LPS, 4>(sl, d, j0, j1, c);
+
+  for (int e = threadIdx.x; e < NH * D; e += kBlock) {
+    const int h = e / D, m = e % D;
+    qin[h][m] = h < nh ? ld_elem<E>(q, (static_cast<int64_t>(b) * Hq + h0 + h) * D + m) : 0.f;
+  }
+  __syncthreads();
+  const int ncols = blockIdx.y == 0 ? D : d;
+  {
+    const int cq = threadIdx.x % CQ, rb = threadIdx.x / CQ;
+    if (4 * cq < ncols) {
+      const float* Pg = P + static_cast<int64_t>(g) * D * D;
+      float4 acc[NH];
+#pragma unroll
+      for (int h = 0; h < NH; ++h) acc[h] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int rr = 0; rr < RB; ++rr) {
+        const int m = rb * RB + rr;
+        const float4 pv = *reinterpret_cast<const float4*>(Pg + m * D + 4 * cq);
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
+          const float x = qin[h][m];
+          acc[h].x = fmaf(x, pv.x, acc[h].x);
+          acc[h].y = fmaf(x, pv.y, acc[h].y);
+          acc[h].z = fmaf(x, pv.z, acc[h].z);
+          acc[h].w = fmaf(x, pv.w, acc[h].w);
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < NH; ++h) *reinterpret_cast<float4*>(&red[rb][h][4 * cq]) = acc[h];
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < NH * ncols; e += kBlock) {
+    const int h = e / ncols, col = e % ncols;
+    float x = 0.f;
+#pragma unroll
+    for (int pp = 0; pp < NRB; ++pp) x += red[pp][h][col];
+    qr[h][col] = x;
+    if (blockIdx.y == 0 && h < nh) qrot[(static_cast<int64_t>(b) * Hq + h0 + h) * D + col] = x;
+  }
+  __syncthreads();
+
   const int part = threadIdx.x % LPS;
   float qf[NH][VEC];
 #pragma unroll
   for (int h = 0; h < NH; ++h)
 #pragma unroll
     for (int v = 0; v < VEC; ++v)
-      qf[h][v] = (h < nh && part * VEC < d)
-                     ? qrot[(static_cast<int64_t>(b) * Hq + h0 + h) * D + part * VEC + v]
-                     : 0.f;
-  const int j0 = blockIdx.y * kScoreChunk;
-  const int j1 = min(S, j0 + kScoreChunk);
-  const typename E::T* sl = slab + static_cast<int64_t>(bg) * S_max * d;
+      qf[h][v] = (part * VEC < d) ? qr[h][part * VEC + v] : 0.f;
   float* srow = scores + (static_cast<int64_t>(b) * Hq + h0) * S;
-  Chunk c[4];
-  score_first<E, LPS, 4>(sl, d, j0, j1, c);
   score_loop<E, LPS, NH, 4>(sl, d, j0, j1, qf, [&](int h, int j, float s) {
     if (h < nh) srow[static_cast<int64_t>(h) * S + j] = s;
   }, c);
@@ -506,35 +565,43 @@ hipError_t rotate_t(const DecodeArgs& a, float* qrot) {
   return hipGetLastError();
 }
 
-template <class E, int LPS>
-hipError_t score_t(const DecodeArgs& a, const float* qrot, float* scores) {
+template <class E, int D, int LPS>
+hipError_t score_t(const DecodeArgs& a, float* qrot, float* scores) {
   const int G = a.Hq / a.Hkv;
   const int nh = G >= 4 ? 4 : (G >= 2 ? 2 : 1);
   const int nhb = (G + nh - 1) / nh;
   dim3 grid(a.B * a.Hkv * nhb, (a.S + kScoreChunk - 1) / kScoreChunk);
   const auto* sl = cptr<E>(a.k_slab);
+  const auto* qq = cptr<E>(a.q);
   if (nh == 4)
-    hipLaunchKernelGGL((score_kernel<E, LPS, 4>), grid, dim3(kBlock), 0, a.stream, sl, qrot, scores,
-                       a.Hq, a.Hkv, a.D, a.d, a.S, a.S_max, nhb);
+    hipLaunchKernelGGL((score_kernel<E, D, LPS, 4>), grid, dim3(kBlock), 0, a.stream, sl, qq, a.P,
+                       qrot, scores, a.Hq, a.Hkv, a.d, a.S, a.S_max, nhb);
   else if (nh == 2)
-    hipLaunchKernelGGL((score_kernel<E, LPS, 2>), grid, dim3(kBlock), 0, a.stream, sl, qrot, scores,
-                       a.Hq, a.Hkv, a.D, a.d, a.S, a.S_max, nhb);
+    hipLaunchKernelGGL((score_kernel<E, D, LPS, 2>), grid, dim3(kBlock), 0, a.stream, sl, qq, a.P,
+                       qrot, scores, a.Hq, a.Hkv, a.d, a.S, a.S_max, nhb);
   else
-    hipLaunchKernelGGL((score_kernel<E, LPS, 1>), grid, dim3(kBlock), 0, a.stream, sl, qrot, scores,
-                       a.Hq, a.Hkv, a.D, a.d, a.S, a.S_max, nhb);
+    hipLaunchKernelGGL((score_kernel<E, D, LPS, 1>), grid, dim3(kBlock), 0, a.stream, sl, qq, a.P,
+                       qrot, scores, a.Hq, a.Hkv, a.d, a.S, a.S_max, nhb);
   return hipGetLastError();
 }
 
-template <class E>
-hipError_t score_lps(const DecodeArgs& a, const float* qrot, float* scores) {
+template <class E, int D>
+hipError_t score_lps(const DecodeArgs& a, float* qrot, float* scores) {
+  constexpr int MAXL = D / E::VEC;
   switch (lps_for(a.d, E::VEC)) {
-    case 1: return score_t<E, 1>(a, qrot, scores);
-    case 2: return score_t<E, 2>(a, qrot, scores);
-    case 4: return score_t<E, 4>(a, qrot, scores);
-    case 8: return score_t<E, 8>(a, qrot, scores);
-    case 16: return score_t<E, 16>(a, qrot, scores);
-    default: return score_t<E, 32>(a, qrot, scores);
+    case 1: return score_t<E, D, 1>(a, qrot, scores);
+    case 2: return score_t<E, D, 2>(a, qrot, scores);
+    case 4: return score_t<E, D, 4>(a, qrot, scores);
+    case 8: return score_t<E, D, 8>(a, qrot, scores);
+    case 16:
+      if constexpr (MAXL >= 16) return score_t<E, D, 16>(a, qrot, scores);
+      break;
+    case 32:
+      if constexpr (MAXL >= 32) return score_t<E, D, 32>(a, qrot, scores);
+      break;
+    default: break;
   }
+  return hipErrorInvalidValue;
 }
 
 hipError_t combine(const DecodeArgs& a, const float* part, int nsplit) {
@@ -610,8 +677,10 @@ hipError_t launch_rotate(const DecodeArgs& a, float* qrot) {
   return a.D == 64 ? rotate_t<BF16, 64>(a, qrot) : rotate_t<BF16, 128>(a, qrot);
 }
 
-hipError_t launch_scores(const DecodeArgs& a, const float* qrot, float* scores) {
-  return a.dtype == kF32 ? score_lps<F32>(a, qrot, scores) : score_lps<BF16>(a, qrot, scores);
+hipError_t launch_scores(const DecodeArgs& a, float* qrot, float* scores) {
+  if (a.dtype == kF32)
+    return a.D == 64 ? score_lps<F32, 64>(a, qrot, scores) : score_lps<F32, 128>(a, qrot, scores);
+  return a.D == 64 ? score_lps<BF16, 64>(a, qrot, scores) : score_lps<BF16, 128>(a, qrot, scores);
 }
 
 int topk_block_for(int S) { return S <= 4096 ? 256 : (S <= 8192 ? 512 : 1024); }

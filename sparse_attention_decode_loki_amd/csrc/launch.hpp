@@ -28,7 +28,8 @@ struct DecodeArgs {
 };
 
 hipError_t launch_rotate(const DecodeArgs& a, float* qrot);
-hipError_t launch_scores(const DecodeArgs& a, const float* qrot, float* scores);
+// rotates the queries itself (q' of every query head also stored to qrot)
+hipError_t launch_scores(const DecodeArgs& a, float* qrot, float* scores);
 // bits (optional): also write each row's kept-position bitmap, ceil(S/32)
 // words per row, bit j%32 of word j/32 set when token j is kept
 hipError_t launch_topk(const float* scores, int rows, int S, int64_t ld, int k, int* idx,
