@@ -76,7 +76,9 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="l2_13b_run")
-    ap.add_argument("--layers", type=int, default=4)
+    ap.add_argument("--layers", type=int, default=0,
+                    help="cache copies cycled; 0: at least 4 and at least 1 GiB in all, "
+                         "4x the last-level cache, so no step finds its bytes cached")
     ap.add_argument("--path", type=int, default=0, help="0 auto, 1 fused, 2 split, 3 union")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-run", action="store_true")
@@ -143,6 +145,10 @@ def main():
         new_v.append(up(vn))
         qs.append(up(synth.queries(w, step=r)))
     loki.append(base, new_k[0], new_v[0], Pd, pos=S - 1)
+    cache_bytes = sum(t.numel() * t.element_size() for t in (base.k_slab, base.k_rest, base.v)
+                      if t is not None)
+    if args.layers <= 0:
+        args.layers = max(4, -(-(1 << 30) // cache_bytes))
     caches = [base]
     for _ in range(args.layers - 1):
         c = loki.KVCache(w.B, w.Hkv, S, w.D, w.d, tdt, dev)
@@ -153,8 +159,6 @@ def main():
         c.length = S
         caches.append(c)
     torch.cuda.synchronize()
-    cache_bytes = sum(t.numel() * t.element_size() for t in (base.k_slab, base.k_rest, base.v)
-                      if t is not None)
     log(f"caches ready: {args.layers} x {cache_bytes / 1e9:.2f} GB")
 
     out = torch.empty((w.B, w.Hq, w.D), dtype=torch.float32, device=dev)

@@ -406,3 +406,21 @@ def test_stream_read_probe_reads_every_element(lib):
         lib.stream_read(buf, sink, wg)
         got = sink.double().sum().item()
         assert got == float((torch.arange(n, dtype=torch.float64) % 7).sum())
+
+
+@pytest.mark.parametrize("path", [2, 3], ids=["split", "union"])
+def test_split_paths_ignore_stale_workspace(lib, path):
+    """The split and union paths read nothing from the workspace that the same
+    call did not write: a workspace full of NaN bit patterns and a zeroed one
+    give bit-identical selections and outputs."""
+    import torch
+    c = case("sinks")
+    cache = device_cache(lib, c)
+    ws = lib.alloc_workspace(c.w.B, c.w.Hq, c.w.D, c.S_max, c.k, torch.device("cuda"))
+    res = []
+    for fill in (0xFF, 0x00):
+        ws.fill_(fill)
+        out, idx = lib.decode(_q(c), cache, _P(c), c.k, workspace=ws, path=path)
+        res.append((out.cpu().numpy(), idx.cpu().numpy()))
+    assert np.array_equal(res[0][1], res[1][1])
+    assert np.array_equal(res[0][0].view(np.uint32), res[1][0].view(np.uint32))
