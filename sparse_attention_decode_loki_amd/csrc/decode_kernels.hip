@@ -89,10 +89,17 @@ __global__ void __launch_bounds__(kBlock) rotate_kernel(const typename E::T* __r
 
 // ------------------------------------------------------------------- score --
 
-constexpr int kScoreChunk = 1024;  // tokens per score workgroup
+// Tokens per score workgroup: the largest of 1024, 512, 256 that still gives
+// about four workgroups per CU (the rotation at the start of each workgroup
+// is amortised over its chunk).
+int score_chunk(int units, int S) {
+  for (int c = 1024; c > 256; c >>= 1)
+    if (static_cast<int64_t>(units) * ((S + c - 1) / c) >= 1024) return c;
+  return 256;
+}
 
-// Grid (B*Hkv*nhb, ceil(S / kScoreChunk)).  Workgroup (bg*nhb + hb, chunk)
-// scores tokens [chunk*kScoreChunk, +kScoreChunk) for the NH query heads
+// Grid (B*Hkv*nhb, ceil(S / chunk)).  Workgroup (bg*nhb + hb, i) scores
+// tokens [i*chunk, i*chunk + chunk) for the NH query heads
 // hb*NH.. of KV head g.  The queries are rotated here: the slab loads are
 // issued first, then q' = q . P[g] is formed exactly as rotate_kernel and the
 // fused kernel form it (thread (cq, rb) adds rows [rb*RB, rb*RB + RB) of
@@ -106,7 +113,8 @@ __global__ void __launch_bounds__(kBlock) score_kernel(const typename E::T* __re
                                                        const float* __restrict__ P,
                                                        float* __restrict__ qrot,
                                                        float* __restrict__ scores, int Hq, int Hkv,
-                                                       int d, int S, int S_max, int nhb) {
+                                                       int d, int S, int S_max, int nhb,
+                                                       int chunk) {
   constexpr int VEC = E::VEC;
   constexpr int CQ = D / 4;         // column quads of P
   constexpr int NRB = kBlock / CQ;  // row blocks of P
@@ -120,8 +128,8 @@ __global__ void __launch_bounds__(kBlock) score_kernel(const typename E::T* __re
   const int b = bg / Hkv, g = bg % Hkv;
   const int h0 = g * G + hb * NH;
   const int nh = min(NH, G - hb * NH);
-  const int j0 = blockIdx.y * kScoreChunk;
-  const int j1 = min(S, j0 + kScoreChunk);
+  const int j0 = blockIdx.y * chunk;
+  const int j1 = min(S, j0 + chunk);
   const typename E::T* sl = slab + static_cast<int64_t>(bg) * S_max * d;
   Chunk c[4];
   score_first<E, LPS, 4>(sl, d, j0, j1, c);
@@ -570,18 +578,19 @@ hipError_t score_t(const DecodeArgs& a, float* qrot, float* scores) {
   const int G = a.Hq / a.Hkv;
   const int nh = G >= 4 ? 4 : (G >= 2 ? 2 : 1);
   const int nhb = (G + nh - 1) / nh;
-  dim3 grid(a.B * a.Hkv * nhb, (a.S + kScoreChunk - 1) / kScoreChunk);
+  const int chunk = score_chunk(a.B * a.Hkv * nhb, a.S);
+  dim3 grid(a.B * a.Hkv * nhb, (a.S + chunk - 1) / chunk);
   const auto* sl = cptr<E>(a.k_slab);
   const auto* qq = cptr<E>(a.q);
   if (nh == 4)
     hipLaunchKernelGGL((score_kernel<E, D, LPS, 4>), grid, dim3(kBlock), 0, a.stream, sl, qq, a.P,
-                       qrot, scores, a.Hq, a.Hkv, a.d, a.S, a.S_max, nhb);
+                       qrot, scores, a.Hq, a.Hkv, a.d, a.S, a.S_max, nhb, chunk);
   else if (nh == 2)
     hipLaunchKernelGGL((score_kernel<E, D, LPS, 2>), grid, dim3(kBlock), 0, a.stream, sl, qq, a.P,
-                       qrot, scores, a.Hq, a.Hkv, a.d, a.S, a.S_max, nhb);
+                       qrot, scores, a.Hq, a.Hkv, a.d, a.S, a.S_max, nhb, chunk);
   else
     hipLaunchKernelGGL((score_kernel<E, D, LPS, 1>), grid, dim3(kBlock), 0, a.stream, sl, qq, a.P,
-                       qrot, scores, a.Hq, a.Hkv, a.d, a.S, a.S_max, nhb);
+                       qrot, scores, a.Hq, a.Hkv, a.d, a.S, a.S_max, nhb, chunk);
   return hipGetLastError();
 }
 
