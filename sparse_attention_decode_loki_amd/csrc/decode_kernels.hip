@@ -365,24 +365,76 @@ constexpr int kUnionMax = kUnionMaxTok;  // token positions per union-gather wor
 static_assert(kUnionMax % 32 == 0 && kUnionMax / 8 <= kBlock, "one byte of positions per thread");
 static_assert(kUnionMaxS <= (1 << 24), "token id and head mask share one word");
 
+template <int NH>
+struct UnionList {
+  unsigned bw[NH][kUnionMax / 32];  // the G heads' bitmap words of the range
+  unsigned ulist[kUnionMax];        // token id | head mask << 24
+  unsigned wsum[kBlock / 64];
+};
+
 template <int D, int NH, int NG>
 union UnionSmem {
-  struct {
-    unsigned bw[NH][kUnionMax / 32];  // the G heads' bitmap words of the range
-    unsigned ulist[kUnionMax];        // token id | head mask << 24
-    unsigned wsum[kBlock / 64];
-  } g;
+  UnionList<NH> g;
   MergeSmem<D, NH, NG> m;  // after the gather
 };
 
+// The union of the NH heads' kept tokens in positions [j0, j0 + n) (j0 a
+// multiple of 32, n <= kUnionMax), in ascending order with each token's head
+// mask: the heads' bitmap words of the range (brow: head h's row at
+// brow + h * nw) are read once into LDS; thread t takes 8 positions (one
+// byte of each head's bitmap) and the positions that any head kept are
+// compacted with a block scan.  Returns the count; ends with a barrier.
+template <int NH>
+__device__ int union_compact(const unsigned* __restrict__ brow, int nw, int j0, int n,
+                             UnionList<NH>& L) {
+  constexpr int NW = kBlock / 64;
+  const int tid = threadIdx.x;
+  const int nwr = (n + 31) >> 5;
+  for (int i = tid; i < NH * nwr; i += kBlock) {
+    const int h = i / nwr, w = i - h * nwr;
+    L.bw[h][w] = brow[static_cast<int64_t>(h) * nw + w];
+  }
+  __syncthreads();
+  unsigned hb[NH];
+  unsigned any = 0u;
+  {
+    const int p0 = tid * 8;
+    const unsigned valid = p0 < n ? (n - p0 >= 8 ? 0xffu : (1u << (n - p0)) - 1u) : 0u;
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+      hb[h] = valid ? (L.bw[h][p0 >> 5] >> (p0 & 31)) & valid : 0u;
+      any |= hb[h];
+    }
+  }
+  const unsigned mine = __popc(any);
+  const int lane = tid & 63, wave = tid >> 6;
+  const unsigned incl = wave_incl_scan(mine, lane);
+  if (lane == 63) L.wsum[wave] = incl;
+  __syncthreads();
+  unsigned before = 0u, ucnt = 0u;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    before += (w < wave) ? L.wsum[w] : 0u;
+    ucnt += L.wsum[w];
+  }
+  unsigned at = before + incl - mine;
+  while (any) {
+    const int e = __ffs(any) - 1;
+    any &= any - 1u;
+    unsigned m = 0u;
+#pragma unroll
+    for (int h = 0; h < NH; ++h) m |= ((hb[h] >> e) & 1u) << h;
+    L.ulist[at++] = static_cast<unsigned>(j0 + tid * 8 + e) | (m << 24);
+  }
+  __syncthreads();
+  return static_cast<int>(ucnt);
+}
+
 // Union gather for grouped-query attention.  Grid (B*Hkv, nsplit); workgroup
 // (bg, split) covers positions [split*R, split*R + R), R a multiple of 32 and
-// at most kUnionMax.  The G = NH query heads' kept-position bitmap words of
-// the range are read once into LDS; thread t takes 8 positions (one byte of
-// each head's bitmap), and the positions that any head kept are compacted in
-// ascending order with their head mask.  Each union token's key and value
-// rows are then loaded once for all G heads; a head that did not keep a
-// token skips it.
+// at most kUnionMax, whose union tokens come from union_compact.  Each union
+// token's key and value rows are loaded once for all G = NH heads; a head that
+// did not keep a token skips it.
 template <class E, int D, int NH>
 __global__ void __launch_bounds__(kBlock, 4) attend_union_kernel(
     const typename E::T* __restrict__ slab, const typename E::T* __restrict__ rest,
@@ -393,7 +445,6 @@ __global__ void __launch_bounds__(kBlock, 4) attend_union_kernel(
   using Gm = Geo<E, D>;
   constexpr int VEC = Gm::VEC;
   constexpr int LPV = Gm::LPV;
-  constexpr int NW = kBlock / 64;
   __shared__ UnionSmem<D, NH, Gm::NG> sm;
 
   const int bg = blockIdx.x, split = blockIdx.y;
@@ -403,8 +454,8 @@ __global__ void __launch_bounds__(kBlock, 4) attend_union_kernel(
   const int n = max(0, min(S, j0 + R) - j0);
   const int tid = threadIdx.x;
 
-  // this lane's q' dims of the G heads and the heads' bitmap words, all
-  // issued together (one round trip)
+  // this lane's q' dims of the G heads, issued first so that their latency
+  // overlaps the bitmap reads
   const int r = tid % LPV;
   const int kd0 = r * VEC;
   float qf[NH][VEC];
@@ -422,47 +473,8 @@ __global__ void __launch_bounds__(kBlock, 4) attend_union_kernel(
     }
   }
   const int nw = (S + 31) >> 5;
-  const int nwr = (n + 31) >> 5;
-  const unsigned* brow = bits + (static_cast<int64_t>(b) * Hq + h0) * nw + (j0 >> 5);
-  for (int i = tid; i < NH * nwr; i += kBlock) {
-    const int h = i / nwr, w = i - h * nwr;
-    sm.g.bw[h][w] = brow[static_cast<int64_t>(h) * nw + w];
-  }
-  __syncthreads();
-
-  // compaction: thread t owns positions [8t, 8t + 8) of the range
-  unsigned hb[NH];
-  unsigned any = 0u;
-  {
-    const int p0 = tid * 8;
-    const unsigned valid = p0 < n ? (n - p0 >= 8 ? 0xffu : (1u << (n - p0)) - 1u) : 0u;
-#pragma unroll
-    for (int h = 0; h < NH; ++h) {
-      hb[h] = valid ? (sm.g.bw[h][p0 >> 5] >> (p0 & 31)) & valid : 0u;
-      any |= hb[h];
-    }
-  }
-  const unsigned mine = __popc(any);
-  const int lane = tid & 63, wave = tid >> 6;
-  const unsigned incl = wave_incl_scan(mine, lane);
-  if (lane == 63) sm.g.wsum[wave] = incl;
-  __syncthreads();
-  unsigned before = 0u, ucnt = 0u;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    before += (w < wave) ? sm.g.wsum[w] : 0u;
-    ucnt += sm.g.wsum[w];
-  }
-  unsigned at = before + incl - mine;
-  while (any) {
-    const int e = __ffs(any) - 1;
-    any &= any - 1u;
-    unsigned m = 0u;
-#pragma unroll
-    for (int h = 0; h < NH; ++h) m |= ((hb[h] >> e) & 1u) << h;
-    sm.g.ulist[at++] = static_cast<unsigned>(j0 + tid * 8 + e) | (m << 24);
-  }
-  __syncthreads();
+  const int ucnt = union_compact<NH>(
+      bits + (static_cast<int64_t>(b) * Hq + h0) * nw + (j0 >> 5), nw, j0, n, sm.g);
 
   Acc<VEC> st[NH];
 #pragma unroll
@@ -476,12 +488,188 @@ __global__ void __launch_bounds__(kBlock, 4) attend_union_kernel(
   // VGPRs (four waves per SIMD)
   attend_loop<E, D, NH, true, (NH >= 4 ? 2 : 4)>(
       [&](int t) { return static_cast<int>(sm.g.ulist[t] & 0xffffffu); },
-      [&](int h, int, int j) { return srow[static_cast<int64_t>(h) * S + j]; }, 0,
-      static_cast<int>(ucnt), sl, rs, vv, d, qf, scale_log2, st, -1, nullptr, nullptr,
+      [&](int h, int, int j) { return srow[static_cast<int64_t>(h) * S + j]; }, 0, ucnt, sl, rs,
+      vv, d, qf, scale_log2, st, -1, nullptr, nullptr,
       [&](int t) { return sm.g.ulist[t] >> 24; });
   __syncthreads();  // the merge buffer aliases the token list
 
   merge_groups<E, D, NH>(st, sm.m, [&](int h, int dim, float M, float L, float A) {
+    const int64_t row = static_cast<int64_t>(b) * Hq + h0 + h;
+    if (nsplit == 1) {
+      out[row * D + dim] = A / L;
+    } else {
+      float* pp = part + (row * nsplit + split) * (D + 2);
+      pp[dim] = A;
+      if (dim == 0) {
+        pp[D] = M;
+        pp[D + 1] = L;
+      }
+    }
+  });
+}
+
+// Union gather with the key products on the matrix cores (bf16 caches).
+// The VALU union gather spends most of its issue slots on the G heads' key
+// dot products and their lane reductions; here each wave takes the union
+// tokens 16 at a time and forms the rest-dims products of all G heads for the
+// 16 tokens with 16x16x16 bf16 MFMAs: A = q' (heads x dims; q' split into bf16
+// high and low parts, so the products keep ~16 bits of q' beyond bf16 and
+// float32 accumulation), B = the tokens' rest rows (dims x tokens, each lane
+// loading 16 bytes of one token's row), D = heads x tokens in float32.  Lane
+// l (< 16) then holds the G logits of token l; the softmax statistics are
+// taken per wave and tile, and the value rows are accumulated on the VALU by
+// groups of LPV lanes per token as in attend_loop, each group fetching its
+// token's weights from the logit lanes.  NT = ceil((D - d) / 32) chunk steps
+// of the rest row per lane.
+typedef short bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ unsigned short f32_to_bf16_bits(float x) {
+  uint32_t u = __float_as_uint(x);
+  u += 0x7fffu + ((u >> 16) & 1u);  // round to nearest even (finite x)
+  return static_cast<unsigned short>(u >> 16);
+}
+
+template <int D, int NH, int NT>
+__global__ void __launch_bounds__(kBlock, 4) attend_union_mfma_kernel(
+    const uint16_t* __restrict__ rest, const uint16_t* __restrict__ val,
+    const float* __restrict__ qrot, const float* __restrict__ scores,
+    const unsigned* __restrict__ bits, float* __restrict__ part, float* __restrict__ out, int Hq,
+    int Hkv, int d, int S, int S_max, int R, int nsplit, float scale_log2) {
+  using Gm = Geo<BF16, D>;
+  constexpr int VEC = 8;
+  constexpr int LPV = Gm::LPV;     // lanes per value row
+  constexpr int GPW = 64 / LPV;    // value-row groups per wave
+  constexpr int TILE = 16;         // union tokens per wave step (MFMA N)
+  constexpr int US = TILE / GPW;   // value-row steps per tile
+  static_assert(NH <= 4, "the heads occupy rows 0..3 of the MFMA output");
+  __shared__ UnionSmem<D, NH, Gm::NG> sm;
+
+  const int bg = blockIdx.x, split = blockIdx.y;
+  const int b = bg / Hkv, g = bg % Hkv;
+  const int h0 = g * NH;
+  const int j0 = split * R;
+  const int n = max(0, min(S, j0 + R) - j0);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int mc = lane >> 4;   // MFMA lane group: dims 8*mc.. of each 32-dim step
+  const int mn = lane & 15;   // MFMA column (token of the tile) / row (head)
+  const int Dr = D - d;
+
+  // A operands: q' rest dims 32t + 8mc + 4hf + i of head mn (rows >= NH zero)
+  bf16x4 ahi[NT][2], alo[NT][2];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const int dim = 32 * t + 8 * mc + 4 * hf;  // 4 dims, 16-byte aligned (d % 8 == 0)
+      const float4 x4 =
+          (mn < NH && dim < Dr)
+              ? *reinterpret_cast<const float4*>(
+                    qrot + (static_cast<int64_t>(b) * Hq + h0 + mn) * D + d + dim)
+              : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float xs[4] = {x4.x, x4.y, x4.z, x4.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const unsigned short hi = f32_to_bf16_bits(xs[i]);
+        const float xl = xs[i] - __uint_as_float(static_cast<uint32_t>(hi) << 16);
+        ahi[t][hf][i] = static_cast<short>(hi);
+        alo[t][hf][i] = static_cast<short>(f32_to_bf16_bits(xl));
+      }
+    }
+
+  const int nw = (S + 31) >> 5;
+  const int ucnt = union_compact<NH>(
+      bits + (static_cast<int64_t>(b) * Hq + h0) * nw + (j0 >> 5), nw, j0, n, sm.g);
+
+  const int64_t bgo = static_cast<int64_t>(b) * Hkv + g;
+  const Region gr = make_region(rest ? rest + bgo * S_max * Dr : val, 0x7fffffffu);
+  const Region gv = make_region(val + bgo * S_max * D, 0x7fffffffu);
+  const float* srow = scores + (static_cast<int64_t>(b) * Hq + h0) * S;
+  const int r = lane % LPV, gw = lane / LPV;
+  const uint32_t vcol = static_cast<uint32_t>(r * VEC) * 2u;
+
+  Acc<VEC> st[NH];
+#pragma unroll
+  for (int h = 0; h < NH; ++h) acc_init(st[h]);
+
+  for (int t0 = wave * TILE; t0 < ucnt; t0 += 4 * TILE) {
+    // this lane's MFMA token and the value-row tokens of its group
+    const int tn = t0 + mn;
+    const unsigned en = tn < ucnt ? sm.g.ulist[tn] : 0u;
+    const int jn = tn < ucnt ? static_cast<int>(en & 0xffffffu) : -1;
+    Chunk rc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int dim = 32 * t + 8 * mc;
+      rc[t] = (jn >= 0 && dim < Dr)
+                  ? ld16_region(gr, static_cast<uint32_t>(jn) * Dr * 2u + dim * 2u)
+                  : zero_chunk();
+    }
+    Chunk vc[US];
+#pragma unroll
+    for (int u = 0; u < US; ++u) {
+      const int tv = t0 + u * GPW + gw;
+      vc[u] = tv < ucnt ? ld16_region(gv, (sm.g.ulist[tv] & 0xffffffu) * (D * 2u) + vcol)
+                        : zero_chunk();
+    }
+    float sv[NH];
+#pragma unroll
+    for (int h = 0; h < NH; ++h)
+      sv[h] = (mc == 0 && jn >= 0 && ((en >> (24 + h)) & 1u))
+                  ? srow[static_cast<int64_t>(h) * S + jn]
+                  : 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const u32x2 w = hf == 0 ? u32x2{rc[t].u.x, rc[t].u.y} : u32x2{rc[t].u.z, rc[t].u.w};
+        const bf16x4 bop = __builtin_bit_cast(bf16x4, w);
+        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ahi[t][hf], bop, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(alo[t][hf], bop, acc, 0, 0, 0);
+      }
+    // logits of token mn in lanes 0..15 (row h of the output = head h)
+    float e[NH];
+#pragma unroll
+    for (int h = 0; h < NH; ++h)
+      e[h] = (mc == 0 && jn >= 0 && ((en >> (24 + h)) & 1u)) ? (acc[h] + sv[h]) * scale_log2
+                                                                 : -INFINITY;
+    float p[NH];
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+      float mx = e[h];
+      mx = fmaxf(mx, dpp_f<0xB1>(mx));
+      mx = fmaxf(mx, dpp_f<0x4E>(mx));
+      mx = fmaxf(mx, dpp_f<0x141>(mx));
+      mx = fmaxf(mx, dpp_f<0x140>(mx));
+      mx = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mx), 0));
+      const float mnew = fmaxf(st[h].m, mx);
+      const float c = (st[h].m == mnew) ? 1.f : fast_exp2(st[h].m - mnew);
+      st[h].m = mnew;
+      st[h].l *= c;
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) st[h].a[v] *= c;
+      p[h] = (e[h] == -INFINITY) ? 0.f : fast_exp2(e[h] - mnew);
+    }
+#pragma unroll
+    for (int u = 0; u < US; ++u) {
+      const int src = u * GPW + gw;  // lane holding this group's token's logits
+      float vf[VEC];
+      unpack<BF16>(vc[u], vf);
+#pragma unroll
+      for (int h = 0; h < NH; ++h) {
+        const float w = __shfl(p[h], src, 64);
+        st[h].l += w;
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) st[h].a[v] = fmaf(w, vf[v], st[h].a[v]);
+      }
+    }
+  }
+  __syncthreads();  // the merge buffer aliases the token list
+
+  merge_groups<BF16, D, NH>(st, sm.m, [&](int h, int dim, float M, float L, float A) {
     const int64_t row = static_cast<int64_t>(b) * Hq + h0 + h;
     if (nsplit == 1) {
       out[row * D + dim] = A / L;
@@ -668,6 +856,27 @@ hipError_t union_t(const DecodeArgs& a, const float* qrot, const float* scores,
   if (R > kUnionMax) return hipErrorInvalidValue;
   dim3 grid(a.B * a.Hkv, nsplit);
   const int G = a.Hq / a.Hkv;
+  const int Dr = D - a.d;
+  if constexpr (std::is_same_v<E, BF16>) {
+    const int nt = (Dr + 31) / 32;
+    if (Dr > 0 && nt <= 3) {  // key products on the matrix cores
+      auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, grid, dim3(kBlock), 0, a.stream, cptr<E>(a.k_rest),
+                           cptr<E>(a.v), qrot, scores, bits, part, a.out, a.Hq, a.Hkv, a.d, a.S,
+                           a.S_max, R, nsplit, scale_log2);
+      };
+      if (G == 4) {
+        if (nt == 1) go(attend_union_mfma_kernel<D, 4, 1>);
+        else if (nt == 2) go(attend_union_mfma_kernel<D, 4, 2>);
+        else if constexpr (D > 64) go(attend_union_mfma_kernel<D, 4, 3>);
+      } else {
+        if (nt == 1) go(attend_union_mfma_kernel<D, 2, 1>);
+        else if (nt == 2) go(attend_union_mfma_kernel<D, 2, 2>);
+        else if constexpr (D > 64) go(attend_union_mfma_kernel<D, 2, 3>);
+      }
+      return combine(a, part, nsplit);
+    }
+  }
   if (G == 4)
     hipLaunchKernelGGL((attend_union_kernel<E, D, 4>), grid, dim3(kBlock), 0, a.stream,
                        cptr<E>(a.k_slab), cptr<E>(a.k_rest), cptr<E>(a.v), qrot, scores, bits, part,
