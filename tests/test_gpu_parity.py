@@ -35,6 +35,8 @@ SMALL = {
     "f32_D128": (synth.custom("f32_D128", 111, B=2, Hq=2, Hkv=2, S=600, dtype="f32", d=16), 600, 640),
     "gqa4_f32": (synth.custom("gqa4_f32", 112, B=2, Hq=8, Hkv=2, D=64, d=16, S=900, dtype="f32",
                               tau=8.0), 900, 960),
+    # bf16 with d < 32 at D = 128: the union gather takes its VALU kernel
+    "gqa4_d16": (synth.custom("gqa4_d16", 113, B=2, Hq=8, Hkv=2, d=16, S=700), 700, 720),
 }
 
 
