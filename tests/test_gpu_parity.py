@@ -426,3 +426,18 @@ def test_split_paths_ignore_stale_workspace(lib, path):
         res.append((out.cpu().numpy(), idx.cpu().numpy()))
     assert np.array_equal(res[0][1], res[1][1])
     assert np.array_equal(res[0][0].view(np.uint32), res[1][0].view(np.uint32))
+
+
+def test_per_layer_slab_width(lib):
+    """Per-layer d (the pages' ablation over d): one cache per layer, each
+    with its own slab width, decoded one after another with the same query
+    heads and each checked against the oracle at its own d."""
+    import torch
+    for layer, d in enumerate((8, 16, 40, 64, 128)):
+        w = synth.custom(f"layer{layer}", 500 + layer, B=2, Hq=8, Hkv=2, d=d, S=900)
+        c = make_case(w)
+        cache = device_cache(lib, c)
+        out, idx = lib.decode(_q(c), cache, _P(c), c.k)
+        ref_out, ref_idx, ref_s = oracle.decode(c.q, c.slab, c.rest, c.v, c.P, c.k, w.dtype, S=c.S)
+        check_decode(w.dtype, c.k, out.cpu().numpy(), idx.cpu().numpy(), ref_out, ref_idx, ref_s,
+                     all_pairs(w))
