@@ -508,19 +508,22 @@ __global__ void __launch_bounds__(kBlock, 4) attend_union_kernel(
   });
 }
 
-// Union gather with the key products on the matrix cores (bf16 caches).
-// The VALU union gather spends most of its issue slots on the G heads' key
-// dot products and their lane reductions; here each wave takes the union
-// tokens 16 at a time and forms the rest-dims products of all G heads for the
-// 16 tokens with 16x16x16 bf16 MFMAs: A = q' (heads x dims; q' split into bf16
-// high and low parts, so the products keep ~16 bits of q' beyond bf16 and
-// float32 accumulation), B = the tokens' rest rows (dims x tokens, each lane
-// loading 16 bytes of one token's row), D = heads x tokens in float32.  Lane
-// l (< 16) then holds the G logits of token l; the softmax statistics are
-// taken per wave and tile, and the value rows are accumulated on the VALU by
-// groups of LPV lanes per token as in attend_loop, each group fetching its
-// token's weights from the logit lanes.  NT = ceil((D - d) / 32) chunk steps
-// of the rest row per lane.
+// Union gather on the matrix cores (bf16 caches).  Each wave takes the union
+// tokens 16 at a time (a tile) and runs both products of all G = NH heads as
+// 16x16x16 bf16 MFMAs:
+//   logits  S[h][t] = q'_rest[h] . rest[t]: A = q' (heads x dims, rows past G
+//           zero), B = the tile's rest rows (dims x tokens; each lane loads 16
+//           bytes of one token's row), so lane t < 16 receives token t's G
+//           logits;
+//   values  O[h][:] += P[h][t] V[t][:]: A = the softmax weights (heads x
+//           tokens), B = the tile's value rows (tokens x dims), read from LDS
+//           transposed (the rows are staged there as loaded, with a pad of 16
+//           bytes per row so the four lane groups read different banks).
+// q' and the weights are split into bf16 high and low parts (two MFMAs per
+// step), which keeps about 16 bits beyond bf16 with float32 accumulation.
+// Softmax statistics are kept per wave (a DPP max and sum over the 16 logit
+// lanes per tile); the waves' states are merged in LDS at the end.  NT =
+// ceil((D - d) / 32) 32-dim steps of the rest row.
 typedef short bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
@@ -531,20 +534,47 @@ __device__ __forceinline__ unsigned short f32_to_bf16_bits(float x) {
   return static_cast<unsigned short>(u >> 16);
 }
 
+// x = hi + lo with hi, lo bf16, for four values (high and low parts of an
+// MFMA operand)
+__device__ __forceinline__ void split_bf16(const float4& x, bf16x4& hi, bf16x4& lo) {
+  const float xs[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const unsigned short h = f32_to_bf16_bits(xs[i]);
+    hi[i] = static_cast<short>(h);
+    lo[i] = static_cast<short>(
+        f32_to_bf16_bits(xs[i] - __uint_as_float(static_cast<uint32_t>(h) << 16)));
+  }
+}
+
+template <int D, int NH>
+union UnionMfmaSmem {
+  struct {
+    UnionList<NH> list;
+    alignas(16) uint16_t vt[kBlock / 64][16][D + 8];  // per wave: the tile's value rows
+    alignas(16) float pt[kBlock / 64][16][20];  // per wave: weights by head row (rows >= NH zero)
+  } g;
+  struct {
+    float m[NH][kBlock / 64], l[NH][kBlock / 64];
+    float a[NH][kBlock / 64][D];
+  } mrg;
+};
+
 template <int D, int NH, int NT>
 __global__ void __launch_bounds__(kBlock, 4) attend_union_mfma_kernel(
     const uint16_t* __restrict__ rest, const uint16_t* __restrict__ val,
     const float* __restrict__ qrot, const float* __restrict__ scores,
     const unsigned* __restrict__ bits, float* __restrict__ part, float* __restrict__ out, int Hq,
     int Hkv, int d, int S, int S_max, int R, int nsplit, float scale_log2) {
-  using Gm = Geo<BF16, D>;
   constexpr int VEC = 8;
-  constexpr int LPV = Gm::LPV;     // lanes per value row
-  constexpr int GPW = 64 / LPV;    // value-row groups per wave
-  constexpr int TILE = 16;         // union tokens per wave step (MFMA N)
-  constexpr int US = TILE / GPW;   // value-row steps per tile
-  static_assert(NH <= 4, "the heads occupy rows 0..3 of the MFMA output");
-  __shared__ UnionSmem<D, NH, Gm::NG> sm;
+  constexpr int LPV = D / VEC;     // lanes per value row
+  constexpr int GPW = 64 / LPV;    // value rows per wave load
+  constexpr int TILE = 16;         // union tokens per wave step
+  constexpr int US = TILE / GPW;   // value-row loads per lane per tile
+  constexpr int NDB = D / 16;      // 16-dim output blocks
+  constexpr int NW = kBlock / 64;
+  static_assert(NH <= 4, "the heads occupy rows 0..3 of the MFMA outputs");
+  __shared__ UnionMfmaSmem<D, NH> sm;
 
   const int bg = blockIdx.x, split = blockIdx.y;
   const int b = bg / Hkv, g = bg % Hkv;
@@ -553,11 +583,11 @@ __global__ void __launch_bounds__(kBlock, 4) attend_union_mfma_kernel(
   const int n = max(0, min(S, j0 + R) - j0);
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int mc = lane >> 4;   // MFMA lane group: dims 8*mc.. of each 32-dim step
-  const int mn = lane & 15;   // MFMA column (token of the tile) / row (head)
+  const int mc = lane >> 4;   // MFMA lane group
+  const int mn = lane & 15;   // MFMA row / column index of this lane
   const int Dr = D - d;
 
-  // A operands: q' rest dims 32t + 8mc + 4hf + i of head mn (rows >= NH zero)
+  // logits A operand: q' rest dims 32t + 8mc + 4hf + i of head mn
   bf16x4 ahi[NT][2], alo[NT][2];
 #pragma unroll
   for (int t = 0; t < NT; ++t)
@@ -569,19 +599,15 @@ __global__ void __launch_bounds__(kBlock, 4) attend_union_mfma_kernel(
               ? *reinterpret_cast<const float4*>(
                     qrot + (static_cast<int64_t>(b) * Hq + h0 + mn) * D + d + dim)
               : make_float4(0.f, 0.f, 0.f, 0.f);
-      const float xs[4] = {x4.x, x4.y, x4.z, x4.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const unsigned short hi = f32_to_bf16_bits(xs[i]);
-        const float xl = xs[i] - __uint_as_float(static_cast<uint32_t>(hi) << 16);
-        ahi[t][hf][i] = static_cast<short>(hi);
-        alo[t][hf][i] = static_cast<short>(f32_to_bf16_bits(xl));
-      }
+      split_bf16(x4, ahi[t][hf], alo[t][hf]);
     }
+  // weight rows past the heads stay zero
+  for (int i = lane; i < 16 * 20; i += 64)
+    if (i / 20 >= NH) sm.g.pt[wave][i / 20][i % 20] = 0.f;
 
   const int nw = (S + 31) >> 5;
   const int ucnt = union_compact<NH>(
-      bits + (static_cast<int64_t>(b) * Hq + h0) * nw + (j0 >> 5), nw, j0, n, sm.g);
+      bits + (static_cast<int64_t>(b) * Hq + h0) * nw + (j0 >> 5), nw, j0, n, sm.g.list);
 
   const int64_t bgo = static_cast<int64_t>(b) * Hkv + g;
   const Region gr = make_region(rest ? rest + bgo * S_max * Dr : val, 0x7fffffffu);
@@ -590,14 +616,19 @@ __global__ void __launch_bounds__(kBlock, 4) attend_union_mfma_kernel(
   const int r = lane % LPV, gw = lane / LPV;
   const uint32_t vcol = static_cast<uint32_t>(r * VEC) * 2u;
 
-  Acc<VEC> st[NH];
+  float m[NH], l[NH];
 #pragma unroll
-  for (int h = 0; h < NH; ++h) acc_init(st[h]);
+  for (int h = 0; h < NH; ++h) {
+    m[h] = -INFINITY;
+    l[h] = 0.f;
+  }
+  f32x4 o[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int t0 = wave * TILE; t0 < ucnt; t0 += 4 * TILE) {
-    // this lane's MFMA token and the value-row tokens of its group
+  for (int t0 = wave * TILE; t0 < ucnt; t0 += NW * TILE) {  // wave-uniform
     const int tn = t0 + mn;
-    const unsigned en = tn < ucnt ? sm.g.ulist[tn] : 0u;
+    const unsigned en = tn < ucnt ? sm.g.list.ulist[tn] : 0u;
     const int jn = tn < ucnt ? static_cast<int>(en & 0xffffffu) : -1;
     Chunk rc[NT];
 #pragma unroll
@@ -611,7 +642,7 @@ __global__ void __launch_bounds__(kBlock, 4) attend_union_mfma_kernel(
 #pragma unroll
     for (int u = 0; u < US; ++u) {
       const int tv = t0 + u * GPW + gw;
-      vc[u] = tv < ucnt ? ld16_region(gv, (sm.g.ulist[tv] & 0xffffffu) * (D * 2u) + vcol)
+      vc[u] = tv < ucnt ? ld16_region(gv, (sm.g.list.ulist[tv] & 0xffffffu) * (D * 2u) + vcol)
                         : zero_chunk();
     }
     float sv[NH];
@@ -630,46 +661,110 @@ __global__ void __launch_bounds__(kBlock, 4) attend_union_mfma_kernel(
         acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ahi[t][hf], bop, acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(alo[t][hf], bop, acc, 0, 0, 0);
       }
-    // logits of token mn in lanes 0..15 (row h of the output = head h)
+    // logits of token mn in lanes 0..15.  The wave's reference maximum m[h]
+    // only moves when a logit exceeds it by more than kSlack (weights stay
+    // below 2^kSlack), so most tiles need no reduction; l[h] is kept per lane
+    // (lanes 0..15, their own tokens) and summed at the end.
+    constexpr float kSlack = 8.f;
     float e[NH];
+    bool above = false;
 #pragma unroll
-    for (int h = 0; h < NH; ++h)
+    for (int h = 0; h < NH; ++h) {
       e[h] = (mc == 0 && jn >= 0 && ((en >> (24 + h)) & 1u)) ? (acc[h] + sv[h]) * scale_log2
-                                                                 : -INFINITY;
+                                                              : -INFINITY;
+      above |= e[h] > m[h] + kSlack;
+    }
+    if (__ballot(above)) {  // wave-uniform: move the reference maxima
+#pragma unroll
+      for (int h = 0; h < NH; ++h) {
+        float mx = e[h];
+        mx = fmaxf(mx, dpp_f<0xB1>(mx));
+        mx = fmaxf(mx, dpp_f<0x4E>(mx));
+        mx = fmaxf(mx, dpp_f<0x141>(mx));
+        mx = fmaxf(mx, dpp_f<0x140>(mx));
+        mx = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mx), 0));
+        const float mnew = fmaxf(m[h], mx);
+        const float c = (m[h] == mnew) ? 1.f : fast_exp2(m[h] - mnew);
+        m[h] = mnew;
+        l[h] *= c;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) o[db][h] *= c;
+      }
+    }
     float p[NH];
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
-      float mx = e[h];
-      mx = fmaxf(mx, dpp_f<0xB1>(mx));
-      mx = fmaxf(mx, dpp_f<0x4E>(mx));
-      mx = fmaxf(mx, dpp_f<0x141>(mx));
-      mx = fmaxf(mx, dpp_f<0x140>(mx));
-      mx = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mx), 0));
-      const float mnew = fmaxf(st[h].m, mx);
-      const float c = (st[h].m == mnew) ? 1.f : fast_exp2(st[h].m - mnew);
-      st[h].m = mnew;
-      st[h].l *= c;
+      p[h] = (e[h] == -INFINITY) ? 0.f : fast_exp2(e[h] - m[h]);
+      l[h] += p[h];
+    }
+    // stage the weights (head rows) and the value rows of the tile
+    if (mc == 0) {
 #pragma unroll
-      for (int v = 0; v < VEC; ++v) st[h].a[v] *= c;
-      p[h] = (e[h] == -INFINITY) ? 0.f : fast_exp2(e[h] - mnew);
+      for (int h = 0; h < NH; ++h) sm.g.pt[wave][h][mn] = p[h];
     }
 #pragma unroll
-    for (int u = 0; u < US; ++u) {
-      const int src = u * GPW + gw;  // lane holding this group's token's logits
-      float vf[VEC];
-      unpack<BF16>(vc[u], vf);
+    for (int u = 0; u < US; ++u)
+      *reinterpret_cast<uint4*>(&sm.g.vt[wave][u * GPW + gw][r * VEC]) = vc[u].u;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // values A operand: weights of head mn for tokens 4mc .. 4mc+3
+    const float4 pw = *reinterpret_cast<const float4*>(&sm.g.pt[wave][mn][4 * mc]);
+    bf16x4 phi, plo;
+    split_bf16(pw, phi, plo);
 #pragma unroll
-      for (int h = 0; h < NH; ++h) {
-        const float w = __shfl(p[h], src, 64);
-        st[h].l += w;
+    for (int db = 0; db < NDB; ++db) {
+      bf16x4 bv;
 #pragma unroll
-        for (int v = 0; v < VEC; ++v) st[h].a[v] = fmaf(w, vf[v], st[h].a[v]);
-      }
+      for (int i = 0; i < 4; ++i)
+        bv[i] = static_cast<short>(sm.g.vt[wave][4 * mc + i][16 * db + mn]);
+      o[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi, bv, o[db], 0, 0, 0);
+      o[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo, bv, o[db], 0, 0, 0);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();  // the stages are rewritten by the next tile
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+  // the wave's weight sums: lanes 0..15 hold their own tokens' partial sums
+#pragma unroll
+  for (int h = 0; h < NH; ++h) {
+    float sum = l[h];
+    sum += dpp_f<0xB1>(sum);
+    sum += dpp_f<0x4E>(sum);
+    sum += dpp_f<0x141>(sum);
+    sum += dpp_f<0x140>(sum);
+    l[h] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sum), 0));
+  }
+  __syncthreads();  // the merge buffer aliases the token list and the stages
+
+  // lanes 0..15 hold O[h][16 db + lane]; merge the waves' states
+  if (mc == 0) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int h = 0; h < NH; ++h) sm.mrg.a[h][wave][16 * db + mn] = o[db][h];
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+      sm.mrg.m[h][wave] = m[h];
+      sm.mrg.l[h][wave] = l[h];
     }
   }
-  __syncthreads();  // the merge buffer aliases the token list
-
-  merge_groups<BF16, D, NH>(st, sm.m, [&](int h, int dim, float M, float L, float A) {
+  __syncthreads();
+  for (int oi = tid; oi < NH * D; oi += kBlock) {
+    const int h = oi / D, dim = oi % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm.mrg.m[h][w]);
+    float L = 0.f, A = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float mw = sm.mrg.m[h][w];
+      const float wt = (mw == -INFINITY) ? 0.f : fast_exp2(mw - M);
+      L = fmaf(sm.mrg.l[h][w], wt, L);
+      A = fmaf(sm.mrg.a[h][w][dim], wt, A);
+    }
     const int64_t row = static_cast<int64_t>(b) * Hq + h0 + h;
     if (nsplit == 1) {
       out[row * D + dim] = A / L;
@@ -681,7 +776,7 @@ __global__ void __launch_bounds__(kBlock, 4) attend_union_mfma_kernel(
         pp[D + 1] = L;
       }
     }
-  });
+  }
 }
 
 // Log-sum-exp merge of the nsplit slices of each row (a separate launch:
