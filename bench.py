@@ -212,7 +212,7 @@ def main():
     achieved = step_bytes / (step_avg_ms * 1e-3) / 1e9
     khash = kernel_source_hash()
     path_name = {1: "fused", 2: "split", 3: "union"}[
-        loki.decode_path(w.B, w.Hq, w.Hkv, w.D, w.d, S, k, args.path)]
+        loki.decode_path(w.B, w.Hq, w.Hkv, w.D, w.d, S, k, w.dtype, args.path)]
     traffic = measured_traffic(khash, args.config) if "fused" in path_name else None
 
     result = {
@@ -261,16 +261,19 @@ def main():
         result["roofline"]["frac_of_measured_stream_read"] = achieved / best
         log(f"streaming-read probe {best:.0f} GB/s; step at {achieved / best:.3f} of it")
 
-    # ---- grouped-query shapes: the union gather on the same caches
-    if w.Hq // w.Hkv in (2, 4) and path_name != "union":
-        uni_plans = [loki.DecodePlan(qs[i % R], caches[i % L], Pd, k, S=S, out=out, idx=idx,
-                                     workspace=ws, path=loki.PATH_UNION) for i in range(n_plans)]
+    # ---- grouped-query shapes: the other gather (union / per-head) on the
+    # same caches
+    if w.Hq // w.Hkv in (2, 4) and path_name in ("split", "union"):
+        other, key = ((loki.PATH_UNION, "union_gather") if path_name == "split"
+                      else (loki.PATH_SPLIT, "per_head_gather"))
+        alt_plans = [loki.DecodePlan(qs[i % R], caches[i % L], Pd, k, S=S, out=out, idx=idx,
+                                     workspace=ws, path=other) for i in range(n_plans)]
         for i in range(args.warmup):
-            uni_plans[i % n_plans]()
-        _, ums = timed(lambda i: uni_plans[i % n_plans](), args.steps)
-        result["union_gather"] = {"avg_ms": ums, "head_queries_per_s": hq / (ums * 1e-3),
-                                  "vs_decode_only": dec_avg_ms / ums}
-        log(f"union gather decode {ums * 1e3:.1f} us/launch")
+            alt_plans[i % n_plans]()
+        _, ams = timed(lambda i: alt_plans[i % n_plans](), args.steps)
+        result[key] = {"avg_ms": ams, "head_queries_per_s": hq / (ams * 1e-3),
+                       "vs_decode_only": dec_avg_ms / ams}
+        log(f"{key.replace('_', ' ')} decode {ams * 1e3:.1f} us/launch")
 
     # ---- same-GPU dense baseline on the same caches
     if not args.no_dense:

@@ -63,19 +63,22 @@ typedef enum {
 
 typedef enum { LOKI_F32 = 0, LOKI_BF16 = 1 } loki_dtype;
 
-/* Execution path of loki_decode_ex.  AUTO picks FUSED or SPLIT by shape.
- * FUSED runs one kernel per (sequence, query head) that scores, selects and
- * attends with the scores held in LDS (requires (D + S + min(k, S)) * 4 bytes
- * <= 56 KiB).  SPLIT runs separate rotation, score, selection and attention
- * kernels through the workspace; its attention reads each query head's kept
- * rows, with the query heads of one KV head scheduled together so that rows
- * several of them kept are served from cache.  UNION is SPLIT with a
- * grouped-query gather (Hq/Hkv of 2 or 4, S <= 131072, else
- * LOKI_EUNSUPPORTED): per KV head and position range, the union of its query
- * heads' kept tokens is loaded once and each head attends over its own
- * tokens in it.  It moves fewer bytes but computes every head on every union
- * token, so it pays off when the heads' selections overlap strongly; AUTO
- * never picks it.  All paths compute the same function. */
+/* Execution path of loki_decode_ex.  AUTO picks one by shape and dtype
+ * (loki_decode_path reports which).  FUSED runs one kernel per (sequence,
+ * query head) that scores, selects and attends with the scores held in LDS
+ * (requires (D + S + min(k, S)) * 4 bytes <= 56 KiB); AUTO takes it for one
+ * query head per KV head and at least 256 (sequence, head) rows.  SPLIT runs
+ * separate score, selection and attention kernels through the workspace; its
+ * attention reads each query head's kept rows, with the query heads of one
+ * KV head scheduled together so that rows several of them kept are served
+ * from cache.  UNION is SPLIT with a grouped-query gather (Hq/Hkv of 2 or 4,
+ * S <= 131072, else LOKI_EUNSUPPORTED): per KV head and position range, the
+ * union of its query heads' kept tokens is loaded once and all heads'
+ * products are formed over it (on the matrix cores for bf16 caches).  AUTO
+ * takes it for bf16 caches with d >= D - 96 when, even for independently
+ * selecting heads, the union, a fraction 1 - (1 - k/S)^G of the positions,
+ * is at most 3/4 of the G*k/S per-head reads.  All paths compute the same
+ * function. */
 typedef enum {
   LOKI_PATH_AUTO = 0,
   LOKI_PATH_FUSED = 1,
@@ -163,12 +166,12 @@ int loki_decode_step(const void* q, const void* k_new, const void* v_new, const 
                      float* out, int32_t* idx, void* workspace, size_t workspace_bytes,
                      int32_t path, void* stream);
 
-/* The path loki_decode_ex would take for these sizes with `path`: the
- * resolved loki_path (FUSED, SPLIT or UNION), or a negative status for
- * invalid sizes or a FUSED / UNION request these sizes do not allow.  Host
- * only. */
+/* The path loki_decode_ex would take for these sizes, cache dtype and
+ * `path`: the resolved loki_path (FUSED, SPLIT or UNION), or a negative
+ * status for invalid sizes or a FUSED / UNION request these sizes do not
+ * allow.  Host only. */
 int loki_decode_path(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t d, int32_t S,
-                     int32_t k, int32_t path);
+                     int32_t k, int32_t dtype, int32_t path);
 
 /* The ranking pass alone: scores [B, Hq, S] float32 (device) receives s_j as
  * defined for loki_decode.  Same workspace rule. */

@@ -35,7 +35,7 @@ _SIGS = {
                                       _P, _P, _P, ctypes.c_size_t, _I, _P]),
     "loki_decode_step": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I,
                                         _I, _I, _P, _P, _P, ctypes.c_size_t, _I, _P]),
-    "loki_decode_path": (ctypes.c_int, [_I, _I, _I, _I, _I, _I, _I, _I]),
+    "loki_decode_path": (ctypes.c_int, [_I, _I, _I, _I, _I, _I, _I, _I, _I]),
     "loki_scores": (ctypes.c_int, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P,
                                    ctypes.c_size_t, _P]),
     "loki_topk": (ctypes.c_int, [_P, _I, _I, _I, _I, _P, _P]),
@@ -230,10 +230,11 @@ def decode_step(q, k_new, v_new, cache: KVCache, P, k: int, pos: int | None = No
     return out, idx
 
 
-def decode_path(B, Hq, Hkv, D, d, S, k, path=PATH_AUTO) -> int:
+def decode_path(B, Hq, Hkv, D, d, S, k, dtype="bf16", path=PATH_AUTO) -> int:
     """The path (PATH_FUSED, PATH_SPLIT or PATH_UNION) loki_decode_ex takes
-    for these sizes."""
-    st = load().loki_decode_path(B, Hq, Hkv, D, d, S, k, path)
+    for these sizes and cache dtype ("bf16" or "f32")."""
+    code = {"bf16": LOKI_BF16, "f32": LOKI_F32}[dtype]
+    st = load().loki_decode_path(B, Hq, Hkv, D, d, S, k, code, path)
     if st < 0:
         raise LokiError(st, "loki_decode_path")
     return st

@@ -3,6 +3,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <cmath>
 
 #include "loki.h"
 #include "launch.hpp"
@@ -11,7 +12,7 @@ using loki::DecodeArgs;
 
 namespace {
 
-constexpr int kAbiVersion = 1;
+constexpr int kAbiVersion = 2;
 constexpr int kTargetWorkgroups = 1024;  // about four per compute unit
 constexpr int kAttendStageTok = 2048;    // must match the attend kernel's LDS stage
 
@@ -150,6 +151,26 @@ bool auto_fused(int B, int Hq, int Hkv, int D, int S, int kk) {
   return Hq == Hkv && static_cast<int64_t>(B) * Hq >= 256 && fused_fits(D, S, kk);
 }
 
+// The union gather is chosen (bf16 caches, where its products run on the
+// matrix cores) when, even for query heads that select independently of
+// each other, the union of their kept tokens, a fraction 1 - (1 - k/S)^G of
+// the positions, is at most 3/4 of the G*k/S per-head reads: at k = S/4 and
+// G = 4 (68% against 100%) it measures faster than the per-head gather, at
+// k = S/8 (41% against 50%) slower.  Heads whose selections overlap only
+// favour it more.
+bool auto_union(int Hq, int Hkv, int D, int d, int S, int kk, int dtype) {
+  if (!union_ok(Hq, Hkv, S) || dtype != LOKI_BF16 || d >= D || (D - d + 31) / 32 > 3) return false;
+  const int G = Hq / Hkv;
+  const double f = static_cast<double>(kk) / S;
+  return 1.0 - std::pow(1.0 - f, G) <= 0.75 * G * f;
+}
+
+// The path AUTO resolves to.
+int auto_path(int B, int Hq, int Hkv, int D, int d, int S, int kk, int dtype) {
+  if (auto_fused(B, Hq, Hkv, D, S, kk)) return LOKI_PATH_FUSED;
+  return auto_union(Hq, Hkv, D, d, S, kk, dtype) ? LOKI_PATH_UNION : LOKI_PATH_SPLIT;
+}
+
 }  // namespace
 
 extern "C" {
@@ -192,8 +213,8 @@ size_t loki_decode_workspace_size(int32_t B, int32_t Hq, int32_t D, int32_t S_ma
 }
 
 int loki_decode_path(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t d, int32_t S,
-                     int32_t k, int32_t path) {
-  int st = check_shape(B < 1 ? 1 : B, Hq, Hkv, D, d, S, S, LOKI_BF16);
+                     int32_t k, int32_t dtype, int32_t path) {
+  int st = check_shape(B < 1 ? 1 : B, Hq, Hkv, D, d, S, S, dtype);
   if (st != LOKI_OK) return st;
   if (k < 1) return LOKI_EINVAL;
   const int kk = std::min(k, S);
@@ -201,7 +222,7 @@ int loki_decode_path(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t d, i
   if (path == LOKI_PATH_FUSED) return fused_fits(D, S, kk) ? LOKI_PATH_FUSED : LOKI_EUNSUPPORTED;
   if (path == LOKI_PATH_UNION) return union_ok(Hq, Hkv, S) ? LOKI_PATH_UNION : LOKI_EUNSUPPORTED;
   if (path != LOKI_PATH_AUTO) return LOKI_EINVAL;
-  return auto_fused(B, Hq, Hkv, D, S, kk) ? LOKI_PATH_FUSED : LOKI_PATH_SPLIT;
+  return auto_path(B, Hq, Hkv, D, d, S, kk, dtype);
 }
 
 int loki_decode_ex(const void* q, const void* k_slab, const void* k_rest, const void* v,
@@ -212,6 +233,8 @@ int loki_decode_ex(const void* q, const void* k_slab, const void* k_rest, const 
   if (st != LOKI_OK) return st;
   if (k < 1) return LOKI_EINVAL;
   if (!valid_path(path)) return LOKI_EINVAL;
+  const int kk = std::min(k, S);
+  if (path == LOKI_PATH_AUTO) path = auto_path(B, Hq, Hkv, D, d, S, kk, dtype);
   const bool uni = path == LOKI_PATH_UNION;
   if (uni && !union_ok(Hq, Hkv, S)) return LOKI_EUNSUPPORTED;
   if (B == 0) return LOKI_OK;
@@ -219,12 +242,9 @@ int loki_decode_ex(const void* q, const void* k_slab, const void* k_rest, const 
   st = check_cache_ptrs(k_slab, k_rest, v, P, D, d);
   if (st != LOKI_OK) return st;
   if (!aligned16(out) || (reinterpret_cast<uintptr_t>(idx) & 3u)) return LOKI_EINVAL;
-  const int kk = std::min(k, S);
-  const bool fused = path == LOKI_PATH_FUSED ||
-                     (path == LOKI_PATH_AUTO && auto_fused(B, Hq, Hkv, D, S, kk));
   DecodeArgs a = make_args(q, k_slab, k_rest, v, P, B, Hq, Hkv, D, d, S, S_max, dtype, out, idx,
                            stream);
-  if (fused) {
+  if (path == LOKI_PATH_FUSED) {
     if (!fused_fits(D, S, kk)) return LOKI_EUNSUPPORTED;
     return status_of(loki::launch_fused(a, kk));
   }
@@ -257,6 +277,8 @@ int loki_decode_step(const void* q, const void* k_new, const void* v_new, const 
   if (st != LOKI_OK) return st;
   if (k < 1) return LOKI_EINVAL;
   if (!valid_path(path)) return LOKI_EINVAL;
+  const int kk = std::min(k, S);
+  if (path == LOKI_PATH_AUTO) path = auto_path(B, Hq, Hkv, D, d, S, kk, dtype);
   const bool uni = path == LOKI_PATH_UNION;
   if (uni && !union_ok(Hq, Hkv, S)) return LOKI_EUNSUPPORTED;
   if (B == 0) return LOKI_OK;
@@ -264,12 +286,9 @@ int loki_decode_step(const void* q, const void* k_new, const void* v_new, const 
   st = check_cache_ptrs(k_slab, k_rest, v, P, D, d);
   if (st != LOKI_OK) return st;
   if (!aligned16(out) || (reinterpret_cast<uintptr_t>(idx) & 3u)) return LOKI_EINVAL;
-  const int kk = std::min(k, S);
-  const bool fused = path == LOKI_PATH_FUSED ||
-                     (path == LOKI_PATH_AUTO && auto_fused(B, Hq, Hkv, D, S, kk));
   DecodeArgs a = make_args(q, k_slab, k_rest, v, P, B, Hq, Hkv, D, d, S, S_max, dtype, out, idx,
                            stream);
-  if (fused) {
+  if (path == LOKI_PATH_FUSED) {
     if (!fused_fits(D, S, kk)) return LOKI_EUNSUPPORTED;
     return status_of(loki::launch_fused_step(a, k_new, v_new, pos, kk));
   }

@@ -43,7 +43,7 @@ def test_header_declarations_exported(L):
 
 def test_version_and_status_strings(L):
     lib = L.load()
-    assert lib.loki_abi_version() == 1
+    assert lib.loki_abi_version() == 2
     for st in (0, -1, -2, -3, -4, 7):
         assert lib.loki_status_string(st)
     assert L.status_string(-2).startswith("LOKI_EWORKSPACE")
@@ -79,24 +79,27 @@ def test_decode_fused_rejects_when_lds_too_small(L):
     # q' + scores + kept ids over 56 KiB cannot take the fused path
     assert _decode(L.load(), path=1, S=20000, S_max=20000, k=5000) == -4
     lib = L.load()
-    assert lib.loki_decode_path(1, 4, 4, 128, 32, 20000, 5000, 1) == -4
-    assert lib.loki_decode_path(16, 40, 40, 128, 32, 3584, 896, 0) == 1   # auto -> fused
-    assert lib.loki_decode_path(8, 32, 8, 128, 32, 8192, 2048, 0) == 2    # GQA -> split
-    assert lib.loki_decode_path(1, 32, 32, 128, 32, 4096, 1024, 0) == 2   # few heads -> split
-    assert lib.loki_decode_path(1, 4, 4, 128, 32, 100, 25, 2) == 2
-    assert lib.loki_decode_path(1, 4, 4, 128, 32, 100, 25, 1) == 1
-    assert lib.loki_decode_path(1, 4, 4, 128, 33, 100, 25, 0) == -4
+    assert lib.loki_decode_path(1, 4, 4, 128, 32, 20000, 5000, 1, 1) == -4
+    assert lib.loki_decode_path(16, 40, 40, 128, 32, 3584, 896, 1, 0) == 1   # auto -> fused
+    assert lib.loki_decode_path(8, 32, 8, 128, 32, 8192, 2048, 1, 0) == 3    # GQA, k = S/4 -> union
+    assert lib.loki_decode_path(8, 32, 8, 128, 32, 8192, 2048, 0, 0) == 2    # ... float32 cache -> split
+    assert lib.loki_decode_path(4, 32, 8, 128, 64, 32768, 4096, 1, 0) == 2   # GQA, k = S/8 -> split
+    assert lib.loki_decode_path(8, 32, 8, 128, 16, 8192, 2048, 1, 0) == 2    # d < D - 96 -> split
+    assert lib.loki_decode_path(1, 32, 32, 128, 32, 4096, 1024, 1, 0) == 2   # few heads -> split
+    assert lib.loki_decode_path(1, 4, 4, 128, 32, 100, 25, 1, 2) == 2
+    assert lib.loki_decode_path(1, 4, 4, 128, 32, 100, 25, 1, 1) == 1
+    assert lib.loki_decode_path(1, 4, 4, 128, 33, 100, 25, 1, 0) == -4
 
 
 def test_union_path_only_for_two_or_four_heads_per_kv_head(L):
     lib = L.load()
-    assert lib.loki_decode_path(8, 32, 8, 128, 32, 8192, 2048, 3) == 3    # G = 4
-    assert lib.loki_decode_path(2, 8, 4, 128, 32, 700, 100, 3) == 3       # G = 2
-    assert lib.loki_decode_path(2, 8, 8, 128, 32, 700, 100, 3) == -4      # G = 1
-    assert lib.loki_decode_path(2, 16, 2, 128, 32, 700, 100, 3) == -4     # G = 8
-    assert lib.loki_decode_path(1, 4, 1, 128, 32, 1 << 17, 100, 3) == 3
-    assert lib.loki_decode_path(1, 4, 1, 128, 32, (1 << 17) + 1, 100, 3) == -4
-    assert lib.loki_decode_path(1, 4, 1, 128, 32, 100, 10, 4) == -1       # no such path
+    assert lib.loki_decode_path(8, 32, 8, 128, 32, 8192, 2048, 1, 3) == 3    # G = 4
+    assert lib.loki_decode_path(2, 8, 4, 128, 32, 700, 100, 1, 3) == 3       # G = 2
+    assert lib.loki_decode_path(2, 8, 8, 128, 32, 700, 100, 1, 3) == -4      # G = 1
+    assert lib.loki_decode_path(2, 16, 2, 128, 32, 700, 100, 1, 3) == -4     # G = 8
+    assert lib.loki_decode_path(1, 4, 1, 128, 32, 1 << 17, 100, 1, 3) == 3
+    assert lib.loki_decode_path(1, 4, 1, 128, 32, (1 << 17) + 1, 100, 1, 3) == -4
+    assert lib.loki_decode_path(1, 4, 1, 128, 32, 100, 10, 1, 4) == -1       # no such path
     # rejected before any pointer is looked at
     assert _decode(lib, Hq=4, Hkv=4, path=3) == -4
     assert _decode(lib, path=4) == -1
