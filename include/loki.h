@@ -89,7 +89,11 @@ typedef enum {
 /* Human-readable name of a status code.  Never NULL. */
 const char* loki_status_string(int status);
 
-/* ABI revision of this header (incremented on any signature change). */
+/* ABI revision of this header, incremented on any signature change; a caller
+ * compares it with loki_abi_version() of the library it loaded. */
+#define LOKI_ABI_VERSION 2
+
+/* ABI revision the library was built with (LOKI_ABI_VERSION of its header). */
 int loki_abi_version(void);
 
 /* Offline PCA of sample keys (host only, no device work).  The pages state

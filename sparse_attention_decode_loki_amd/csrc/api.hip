@@ -12,7 +12,7 @@ using loki::DecodeArgs;
 
 namespace {
 
-constexpr int kAbiVersion = 2;
+constexpr int kAbiVersion = LOKI_ABI_VERSION;
 constexpr int kTargetWorkgroups = 1024;  // about four per compute unit
 constexpr int kAttendStageTok = 2048;    // must match the attend kernel's LDS stage
 

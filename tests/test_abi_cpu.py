@@ -43,7 +43,9 @@ def test_header_declarations_exported(L):
 
 def test_version_and_status_strings(L):
     lib = L.load()
-    assert lib.loki_abi_version() == 2
+    with open(os.path.join(ROOT, "include", "loki.h")) as fh:
+        header = int(re.search(r"#define LOKI_ABI_VERSION (\d+)", fh.read()).group(1))
+    assert lib.loki_abi_version() == header == 2
     for st in (0, -1, -2, -3, -4, 7):
         assert lib.loki_status_string(st)
     assert L.status_string(-2).startswith("LOKI_EWORKSPACE")
