@@ -441,3 +441,42 @@ def test_per_layer_slab_width(lib):
         ref_out, ref_idx, ref_s = oracle.decode(c.q, c.slab, c.rest, c.v, c.P, c.k, w.dtype, S=c.S)
         check_decode(w.dtype, c.k, out.cpu().numpy(), idx.cpu().numpy(), ref_out, ref_idx, ref_s,
                      all_pairs(w))
+
+
+# ------------------------------------------------------------ graph capture --
+
+@pytest.mark.parametrize("path", [1, 2, 3], ids=["fused", "split", "union"])
+def test_decode_replays_from_a_captured_graph(lib, path):
+    """Each path launches only kernels (no allocation, no memset), so a decode
+    captured into a HIP graph replays correctly: three replays, with eager
+    work and synchronisation between them, each equal to the eager call."""
+    import torch
+    c = case("sinks")  # G = 4: every path applies
+    cache = device_cache(lib, c)
+    q = _q(c)
+    P = _P(c)
+    ws = lib.alloc_workspace(c.w.B, c.w.Hq, c.w.D, c.S_max, c.k, torch.device("cuda"))
+    out = torch.empty((c.w.B, c.w.Hq, c.w.D), dtype=torch.float32, device="cuda")
+    idx = torch.empty((c.w.B, c.w.Hq, c.k), dtype=torch.int32, device="cuda")
+    ref_out, ref_idx = lib.decode(q, cache, P, c.k, workspace=ws, path=path)
+    ref_out, ref_idx = ref_out.cpu().numpy(), ref_idx.cpu().numpy()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):  # warm up on the capture stream
+        lib.decode(q, cache, P, c.k, out=out, idx=idx, workspace=ws, path=path)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        lib.decode(q, cache, P, c.k, out=out, idx=idx, workspace=ws, path=path)
+    for rep in range(3):
+        out.fill_(float("nan"))
+        idx.fill_(-1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(idx.cpu().numpy(), ref_idx), f"replay {rep}"
+        assert np.array_equal(out.cpu().numpy().view(np.uint32), ref_out.view(np.uint32)), rep
+        # eager work between replays
+        lib.decode(q, cache, P, 7, workspace=ws, path=path)
+        torch.cuda.synchronize()
