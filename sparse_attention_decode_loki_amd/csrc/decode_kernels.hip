@@ -560,12 +560,16 @@ union UnionMfmaSmem {
   } mrg;
 };
 
-template <int D, int NH, int NT>
+// DENSE: the same kernel as the grouped-query dense baseline: every position
+// of the range, every head, and the logits over all D dims (NTS 32-dim steps
+// of the slab row, then NT of the rest row), with no ranking scores.
+template <int D, int NH, int NT, int NTS, bool DENSE>
 __global__ void __launch_bounds__(kBlock, 4) attend_union_mfma_kernel(
-    const uint16_t* __restrict__ rest, const uint16_t* __restrict__ val,
-    const float* __restrict__ qrot, const float* __restrict__ scores,
-    const unsigned* __restrict__ bits, float* __restrict__ part, float* __restrict__ out, int Hq,
-    int Hkv, int d, int S, int S_max, int R, int nsplit, float scale_log2) {
+    const uint16_t* __restrict__ slab, const uint16_t* __restrict__ rest,
+    const uint16_t* __restrict__ val, const float* __restrict__ qrot,
+    const float* __restrict__ scores, const unsigned* __restrict__ bits,
+    float* __restrict__ part, float* __restrict__ out, int Hq, int Hkv, int d, int S, int S_max,
+    int R, int nsplit, float scale_log2) {
   constexpr int VEC = 8;
   constexpr int LPV = D / VEC;     // lanes per value row
   constexpr int GPW = 64 / LPV;    // value rows per wave load
@@ -573,7 +577,9 @@ __global__ void __launch_bounds__(kBlock, 4) attend_union_mfma_kernel(
   constexpr int US = TILE / GPW;   // value-row loads per lane per tile
   constexpr int NDB = D / 16;      // 16-dim output blocks
   constexpr int NW = kBlock / 64;
+  constexpr int NTS1 = NTS > 0 ? NTS : 1;
   static_assert(NH <= 4, "the heads occupy rows 0..3 of the MFMA outputs");
+  static_assert(DENSE || NTS == 0, "slab steps only for the dense kernel");
   __shared__ UnionMfmaSmem<D, NH> sm;
 
   const int bg = blockIdx.x, split = blockIdx.y;
@@ -601,18 +607,41 @@ __global__ void __launch_bounds__(kBlock, 4) attend_union_mfma_kernel(
               : make_float4(0.f, 0.f, 0.f, 0.f);
       split_bf16(x4, ahi[t][hf], alo[t][hf]);
     }
+  // DENSE: the slab dims 32t + 8mc + 4hf + i as well
+  bf16x4 shi[NTS1][2], slo[NTS1][2];
+  if constexpr (DENSE) {
+#pragma unroll
+    for (int t = 0; t < NTS; ++t)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const int dim = 32 * t + 8 * mc + 4 * hf;
+        const float4 x4 =
+            (mn < NH && dim < d)
+                ? *reinterpret_cast<const float4*>(
+                      qrot + (static_cast<int64_t>(b) * Hq + h0 + mn) * D + dim)
+                : make_float4(0.f, 0.f, 0.f, 0.f);
+        split_bf16(x4, shi[t][hf], slo[t][hf]);
+      }
+  }
   // weight rows past the heads stay zero
   for (int i = lane; i < 16 * 20; i += 64)
     if (i / 20 >= NH) sm.g.pt[wave][i / 20][i % 20] = 0.f;
 
-  const int nw = (S + 31) >> 5;
-  const int ucnt = union_compact<NH>(
-      bits + (static_cast<int64_t>(b) * Hq + h0) * nw + (j0 >> 5), nw, j0, n, sm.g.list);
+  int ucnt;
+  if constexpr (DENSE) {
+    ucnt = n;
+    __syncthreads();
+  } else {
+    const int nw = (S + 31) >> 5;
+    ucnt = union_compact<NH>(bits + (static_cast<int64_t>(b) * Hq + h0) * nw + (j0 >> 5), nw,
+                             j0, n, sm.g.list);
+  }
 
   const int64_t bgo = static_cast<int64_t>(b) * Hkv + g;
+  const Region gs = make_region(DENSE ? slab + bgo * S_max * d : val, 0x7fffffffu);
   const Region gr = make_region(rest ? rest + bgo * S_max * Dr : val, 0x7fffffffu);
   const Region gv = make_region(val + bgo * S_max * D, 0x7fffffffu);
-  const float* srow = scores + (static_cast<int64_t>(b) * Hq + h0) * S;
+  const float* srow = DENSE ? nullptr : scores + (static_cast<int64_t>(b) * Hq + h0) * S;
   const int r = lane % LPV, gw = lane / LPV;
   const uint32_t vcol = static_cast<uint32_t>(r * VEC) * 2u;
 
@@ -628,8 +657,20 @@ __global__ void __launch_bounds__(kBlock, 4) attend_union_mfma_kernel(
 
   for (int t0 = wave * TILE; t0 < ucnt; t0 += NW * TILE) {  // wave-uniform
     const int tn = t0 + mn;
-    const unsigned en = tn < ucnt ? sm.g.list.ulist[tn] : 0u;
+    const unsigned en = tn >= ucnt ? 0u
+                        : DENSE    ? static_cast<unsigned>(j0 + tn) | (0xfu << 24)
+                                   : sm.g.list.ulist[tn];
     const int jn = tn < ucnt ? static_cast<int>(en & 0xffffffu) : -1;
+    Chunk sc[NTS1];
+    if constexpr (DENSE) {
+#pragma unroll
+      for (int t = 0; t < NTS; ++t) {
+        const int dim = 32 * t + 8 * mc;
+        sc[t] = (jn >= 0 && dim < d)
+                    ? ld16_region(gs, static_cast<uint32_t>(jn) * d * 2u + dim * 2u)
+                    : zero_chunk();
+      }
+    }
     Chunk rc[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
@@ -642,16 +683,27 @@ __global__ void __launch_bounds__(kBlock, 4) attend_union_mfma_kernel(
 #pragma unroll
     for (int u = 0; u < US; ++u) {
       const int tv = t0 + u * GPW + gw;
-      vc[u] = tv < ucnt ? ld16_region(gv, (sm.g.list.ulist[tv] & 0xffffffu) * (D * 2u) + vcol)
-                        : zero_chunk();
+      const uint32_t jv = DENSE ? static_cast<uint32_t>(j0 + tv) : (sm.g.list.ulist[tv] & 0xffffffu);
+      vc[u] = tv < ucnt ? ld16_region(gv, jv * (D * 2u) + vcol) : zero_chunk();
     }
     float sv[NH];
 #pragma unroll
     for (int h = 0; h < NH; ++h)
-      sv[h] = (mc == 0 && jn >= 0 && ((en >> (24 + h)) & 1u))
+      sv[h] = (!DENSE && mc == 0 && jn >= 0 && ((en >> (24 + h)) & 1u))
                   ? srow[static_cast<int64_t>(h) * S + jn]
                   : 0.f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (DENSE) {
+#pragma unroll
+      for (int t = 0; t < NTS; ++t)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const u32x2 w = hf == 0 ? u32x2{sc[t].u.x, sc[t].u.y} : u32x2{sc[t].u.z, sc[t].u.w};
+          const bf16x4 bop = __builtin_bit_cast(bf16x4, w);
+          acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(shi[t][hf], bop, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(slo[t][hf], bop, acc, 0, 0, 0);
+        }
+    }
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -924,6 +976,40 @@ hipError_t attend_t(const DecodeArgs& a, const float* qrot, const float* scores,
                        nsplit, 1, scale_log2);
   } else {
     const int G = a.Hq / a.Hkv;
+    if constexpr (std::is_same_v<E, BF16>) {
+      // grouped-query dense attention on the matrix cores: the union
+      // kernel over every position of its range
+      const int nts = (a.d + 31) / 32, nt = (D - a.d + 31) / 32;
+      if ((G == 2 || G == 4) && a.d < D && nts + nt <= 4) {
+        const int R = (a.S + nsplit - 1) / nsplit;
+        dim3 grid(a.B * a.Hkv, nsplit);
+        auto go = [&](auto kern) {
+          hipLaunchKernelGGL(kern, grid, dim3(kBlock), 0, a.stream, sl, rs, vv, qrot, nullptr,
+                             nullptr, part, a.out, a.Hq, a.Hkv, a.d, a.S, a.S_max, R, nsplit,
+                             scale_log2);
+        };
+        if constexpr (D == 128) {
+          if (G == 4)
+            nts == 1 ? go(attend_union_mfma_kernel<D, 4, 3, 1, true>)
+            : nts == 2 ? go(attend_union_mfma_kernel<D, 4, 2, 2, true>)
+                       : go(attend_union_mfma_kernel<D, 4, 1, 3, true>);
+          else
+            nts == 1 ? go(attend_union_mfma_kernel<D, 2, 3, 1, true>)
+            : nts == 2 ? go(attend_union_mfma_kernel<D, 2, 2, 2, true>)
+                       : go(attend_union_mfma_kernel<D, 2, 1, 3, true>);
+        } else {
+          if (G == 4)
+            nts == 2 ? go(attend_union_mfma_kernel<D, 4, 1, 2, true>)
+            : nt == 2 ? go(attend_union_mfma_kernel<D, 4, 2, 1, true>)
+                      : go(attend_union_mfma_kernel<D, 4, 1, 1, true>);
+          else
+            nts == 2 ? go(attend_union_mfma_kernel<D, 2, 1, 2, true>)
+            : nt == 2 ? go(attend_union_mfma_kernel<D, 2, 2, 1, true>)
+                      : go(attend_union_mfma_kernel<D, 2, 1, 1, true>);
+        }
+        return combine(a, part, nsplit);
+      }
+    }
     const int nh = G >= 4 ? 4 : (G >= 2 ? 2 : 1);
     const int nhb = (G + nh - 1) / nh;
     dim3 grid(a.B * a.Hkv * nhb, nsplit);
@@ -956,18 +1042,18 @@ hipError_t union_t(const DecodeArgs& a, const float* qrot, const float* scores,
     const int nt = (Dr + 31) / 32;
     if (Dr > 0 && nt <= 3) {  // key products on the matrix cores
       auto go = [&](auto kern) {
-        hipLaunchKernelGGL(kern, grid, dim3(kBlock), 0, a.stream, cptr<E>(a.k_rest),
-                           cptr<E>(a.v), qrot, scores, bits, part, a.out, a.Hq, a.Hkv, a.d, a.S,
-                           a.S_max, R, nsplit, scale_log2);
+        hipLaunchKernelGGL(kern, grid, dim3(kBlock), 0, a.stream, cptr<E>(a.k_slab),
+                           cptr<E>(a.k_rest), cptr<E>(a.v), qrot, scores, bits, part, a.out, a.Hq,
+                           a.Hkv, a.d, a.S, a.S_max, R, nsplit, scale_log2);
       };
       if (G == 4) {
-        if (nt == 1) go(attend_union_mfma_kernel<D, 4, 1>);
-        else if (nt == 2) go(attend_union_mfma_kernel<D, 4, 2>);
-        else if constexpr (D > 64) go(attend_union_mfma_kernel<D, 4, 3>);
+        if (nt == 1) go(attend_union_mfma_kernel<D, 4, 1, 0, false>);
+        else if (nt == 2) go(attend_union_mfma_kernel<D, 4, 2, 0, false>);
+        else if constexpr (D > 64) go(attend_union_mfma_kernel<D, 4, 3, 0, false>);
       } else {
-        if (nt == 1) go(attend_union_mfma_kernel<D, 2, 1>);
-        else if (nt == 2) go(attend_union_mfma_kernel<D, 2, 2>);
-        else if constexpr (D > 64) go(attend_union_mfma_kernel<D, 2, 3>);
+        if (nt == 1) go(attend_union_mfma_kernel<D, 2, 1, 0, false>);
+        else if (nt == 2) go(attend_union_mfma_kernel<D, 2, 2, 0, false>);
+        else if constexpr (D > 64) go(attend_union_mfma_kernel<D, 2, 3, 0, false>);
       }
       return combine(a, part, nsplit);
     }

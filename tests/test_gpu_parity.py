@@ -234,7 +234,8 @@ def test_append_matches_oracle(lib, w, pos, T):
 
 # ------------------------------------------------------------------- dense --
 
-@pytest.mark.parametrize("name", ["tiny", "ragged_gqa2", "gqa8", "gqa5", "full_rank_f32", "long_5000"])
+@pytest.mark.parametrize("name", ["tiny", "ragged_gqa2", "gqa8", "gqa5", "full_rank_f32", "long_5000",
+                                  "sinks", "long_20000", "d64_D64_bf16", "gqa4_d16", "gqa4_f32"])
 def test_dense_matches_oracle(lib, name):
     c = case(name)
     cache = device_cache(lib, c)
