@@ -5,21 +5,28 @@
 // project the query onto the calibrated PCA basis, score every cached token
 // with the leading d rotated dimensions, keep the top k, and run exact
 // softmax attention over the kept tokens.  Every stage is bound by HBM
-// bandwidth (about 1 flop per byte), so the kernels use the vector ALU with
-// wide coalesced loads and no matrix cores.
+// bandwidth (about 1 flop per byte), so the kernels use wide coalesced loads
+// and the vector ALU; only where G query heads share each loaded row (the
+// grouped-query union gather and dense baseline) would the G heads' products
+// saturate the vector ALU, and there they run as small MFMA tiles.
 //
 // Kernels:
 //   rotate_kernel   q' = q . P[g] for all query heads of one KV head (dense
 //                   baseline)
 //   score_kernel    q' and s_j over a chunk of the key slab for up to 4 query
 //                   heads; chunk 0 also stores q' for the attention kernels
-//   topk_kernel     exact top-k of one score row, ascending indices
+//   topk_kernel     exact top-k of one score row, ascending indices (and the
+//                   kept-position bitmap for the union gather)
 //   attend_kernel   gather + online softmax over a slice of the kept tokens
 //                   (also the dense baseline, with all tokens)
 //   attend_union_kernel  the grouped-query variant: the union of the G query
-//                   heads' kept tokens is gathered once per KV head
+//                   heads' kept tokens is gathered once per KV head (VALU)
+//   attend_union_mfma_kernel  the same on the matrix cores for bf16 caches;
+//                   also the grouped-query dense baseline
 //   combine_kernel  log-sum-exp merge of the slices
 // The single-kernel path (fused_kernel) is in fused_kernels.hip.
+#include <type_traits>
+
 #include "launch.hpp"
 #include "attend.hpp"
 #include "score.hpp"
