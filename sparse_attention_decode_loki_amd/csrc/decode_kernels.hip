@@ -99,8 +99,10 @@ __global__ void __launch_bounds__(kBlock) rotate_kernel(const typename E::T* __r
 // Tokens per score workgroup: the largest of 1024, 512, 256 that still gives
 // about four workgroups per CU (the rotation at the start of each workgroup
 // is amortised over its chunk).
+constexpr int kScoreChunkMax = 1024;
+
 int score_chunk(int units, int S) {
-  for (int c = 1024; c > 256; c >>= 1)
+  for (int c = kScoreChunkMax; c > 256; c >>= 1)
     if (static_cast<int64_t>(units) * ((S + c - 1) / c) >= 1024) return c;
   return 256;
 }
@@ -129,6 +131,8 @@ __global__ void __launch_bounds__(kBlock) score_kernel(const typename E::T* __re
   __shared__ float qin[NH][D];
   __shared__ float red[NRB][NH][D];
   __shared__ float qr[NH][D];
+  // this chunk's scores; the pad puts the heads of one token in different banks
+  __shared__ __align__(16) float ssc[NH][kScoreChunkMax + 16];
   const int G = Hq / Hkv;
   const int bg = blockIdx.x / nhb;
   const int hb = blockIdx.x % nhb;
@@ -189,10 +193,67 @@ __global__ void __launch_bounds__(kBlock) score_kernel(const typename E::T* __re
 #pragma unroll
     for (int v = 0; v < VEC; ++v)
       qf[h][v] = (part * VEC < d) ? qr[h][part * VEC + v] : 0.f;
-  float* srow = scores + (static_cast<int64_t>(b) * Hq + h0) * S;
-  score_loop<E, LPS, NH, 4>(sl, d, j0, j1, qf, [&](int h, int j, float s) {
-    if (h < nh) srow[static_cast<int64_t>(h) * S + j] = s;
-  }, c);
+
+  // The stream: the loads and dot products of the fused kernel's ranking
+  // pass (same lanes, same order), but every lane of a token's lane group
+  // ends with the group's sums, so lane `part` keeps heads part, part + LPS,
+  // ...  The scores collect in LDS and are stored row by row afterwards: the
+  // loop issues no global stores, which on this chip would share the loads'
+  // completion counter and stall each wait for the next batch.
+  {
+    constexpr int TPI = kBlock / LPS;
+    constexpr int U = 4;
+    constexpr int RND = (NH + LPS - 1) / LPS;
+    const int tk = threadIdx.x / LPS;
+    const bool active = part * VEC < d;
+    const Region gs = make_region(sl, 0x7fffffffu);
+    const uint32_t rowb = static_cast<uint32_t>(d) * E::BYTES;
+    for (int jb = j0 + tk; jb < j1; jb += TPI * U) {
+      if (jb != j0 + tk) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int j = jb + TPI * u;
+          c[u] = (active && j < j1) ? ld16_region(gs, static_cast<uint32_t>(j) * rowb + part * 16u)
+                                    : zero_chunk();
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        float x[VEC];
+        unpack<E>(c[u], x);
+        const int j = jb + TPI * u;
+        float dots[NH];
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
+          float dot = 0.f;
+#pragma unroll
+          for (int v = 0; v < VEC; ++v) dot = fmaf(qf[h][v], x[v], dot);
+          dots[h] = group_sum<LPS>(dot);
+        }
+#pragma unroll
+        for (int r = 0; r < RND; ++r) {
+          const int hh = r * LPS + part;
+          float val = dots[0];
+#pragma unroll
+          for (int h = 1; h < NH; ++h) val = (h == hh) ? dots[h] : val;
+          if (hh < NH && j < j1) ssc[hh][j - j0] = val;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  const int n = j1 - j0;
+  float* srow = scores + (static_cast<int64_t>(b) * Hq + h0) * S + j0;
+  if ((S & 3) == 0 && (reinterpret_cast<uintptr_t>(scores) & 15) == 0) {
+    // rows start 16-byte aligned (chunks are multiples of 256 tokens)
+    for (int h = 0; h < nh; ++h)
+      for (int i = threadIdx.x; 4 * i < n; i += kBlock)
+        *reinterpret_cast<float4*>(srow + static_cast<int64_t>(h) * S + 4 * i) =
+            *reinterpret_cast<const float4*>(&ssc[h][4 * i]);
+  } else {
+    for (int h = 0; h < nh; ++h)
+      for (int i = threadIdx.x; i < n; i += kBlock) srow[static_cast<int64_t>(h) * S + i] = ssc[h][i];
+  }
 }
 
 // -------------------------------------------------------------------- topk --

@@ -144,13 +144,6 @@ def all_pairs(w):
     return [(b, h) for b in range(w.B) for h in range(w.Hq)]
 
 
-def sample_pairs(w, n=16, seed=0):
-    rng = np.random.default_rng(seed)
-    allp = all_pairs(w)
-    pick = rng.choice(len(allp), size=min(n, len(allp)), replace=False)
-    return sorted(allp[i] for i in pick)
-
-
 def ulp_diff_bf16(a: np.ndarray, b: np.ndarray) -> np.ndarray:
     """|a - b| in units of bf16 steps for same-sign finite bf16 patterns
     (ordered integer distance of the bit patterns)."""

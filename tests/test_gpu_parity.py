@@ -13,7 +13,7 @@ import pytest
 import oracle
 import synth
 from gpu_cases import (TOL, all_pairs, check_decode, device_cache, make_case, out_error,
-                       sample_pairs, to_dev, to_host, ulp_diff_bf16, ulp_diff_f32)
+                       to_dev, to_host, ulp_diff_bf16, ulp_diff_f32)
 
 pytestmark = pytest.mark.gpu
 
@@ -114,6 +114,57 @@ def test_topk_all_equal_and_negative_zero(lib):
     idx = lib.topk(torch.from_numpy(host).cuda(), 1000).cpu().numpy()
     for r in range(3):
         assert idx[r].tolist() == list(range(1000))
+
+
+def _crossing_bin_row(rng, S, k, n, kept, values):
+    """A float32 row whose k-th largest value lies in one first-digit bin
+    (sign, exponent and the top two mantissa bits of the order key) holding
+    exactly n scores, `kept` of which are selected: k - kept scores far
+    above, n in [1, 1.25) drawn from `values`, the rest below."""
+    row = np.empty(S, np.float32)
+    row[:] = rng.uniform(-4.0, 0.5, S)
+    pos = rng.permutation(S)
+    row[pos[:k - kept]] = rng.uniform(100.0, 1000.0, k - kept)
+    row[pos[k - kept:k - kept + n]] = rng.choice(values, n)
+    return row
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 64, 255, 256, 257, 600])
+@pytest.mark.parametrize("ties", [False, True])
+def test_topk_crossing_bin_sizes(lib, n, ties):
+    """Rows whose k-th largest score sits in a first-digit bin of n scores
+    (the bin the selection resolves further, or ranks directly when small),
+    with and without repeated values inside it, give the oracle's set."""
+    import torch
+    rng = np.random.default_rng(7 * n + ties)
+    S, k = 4096, 1024
+    values = (np.float32(1.0) + np.arange(4, dtype=np.float32) / 32) if ties else \
+        rng.uniform(1.0, 1.2, 4096).astype(np.float32)
+    rows = [_crossing_bin_row(rng, S, k, n, kept, values)
+            for kept in sorted({1, (n + 1) // 2, n})]
+    host = np.stack(rows)
+    idx = lib.topk(torch.from_numpy(host).cuda(), k).cpu().numpy()
+    for r in range(host.shape[0]):
+        want = oracle.select_topk(host[r].astype(np.float64), k)
+        assert np.array_equal(idx[r].astype(np.int64), want), f"row {r}"
+
+
+def test_topk_crossing_bin_of_signed_zeros(lib):
+    """A crossing bin made of +0.0 and -0.0 only: they rank equal, so the
+    lowest indices among them are kept."""
+    import torch
+    rng = np.random.default_rng(11)
+    S, k = 3000, 1000
+    host = rng.uniform(-3.0, -1.0, (2, S)).astype(np.float32)
+    for r, nz in enumerate((100, 300)):
+        pos = rng.permutation(S)
+        host[r, pos[:976]] = 5.0
+        zeros = pos[976:976 + nz]
+        host[r, zeros] = np.where(rng.random(nz) < 0.5, np.float32(-0.0), np.float32(0.0))
+    idx = lib.topk(torch.from_numpy(host).cuda(), k).cpu().numpy()
+    for r in range(2):
+        want = oracle.select_topk(host[r].astype(np.float64), k)
+        assert np.array_equal(idx[r].astype(np.int64), want), f"row {r}"
 
 
 # --------------------------------------------------- attention over given ids --
@@ -255,16 +306,16 @@ FULL = ["l2_7b", "l2_13b_run", "l3_8b_gqa", "mistral_32k"]
 def test_full_size_decode_sampled(lib, name, path):
     """Full benchmark shapes, launched exactly as the benchmark launches them
     (AUTO path; also the gather AUTO does not take for the grouped-query
-    shapes); 16 sampled (sequence, head) pairs checked against the oracle,
-    plus properties that hold for every pair."""
+    shapes); every (sequence, head) pair checked against the oracle, with at
+    most 1 in 100 near-tie swaps (at least one allowed)."""
     w = synth.WORKLOADS[name]
     c = make_case(w)
     cache = device_cache(lib, c)
     out, idx = lib.decode(_q(c), cache, _P(c), w.k, path=path)
     out, idx = out.cpu().numpy(), idx.cpu().numpy()
-    pairs = sample_pairs(w, 16, seed=w.wid)
+    pairs = all_pairs(w)
     ref_out, ref_idx, ref_s = oracle.decode(c.q, c.slab, c.rest, c.v, c.P, w.k, w.dtype, heads=pairs)
-    check_decode(w.dtype, w.k, out, idx, ref_out, ref_idx, ref_s, pairs, max_swaps=1)
+    check_decode(w.dtype, w.k, out, idx, ref_out, ref_idx, ref_s, pairs)
     # every row: k distinct ascending ids in range, finite outputs
     assert np.all(np.diff(idx.astype(np.int64), axis=-1) > 0)
     assert idx.min() >= 0 and idx.max() < w.S
