@@ -16,11 +16,11 @@
 
 namespace loki {
 
-template <class E, int D>
+template <class E, int D, int NT = kBlock>
 struct Geo {
   static constexpr int VEC = E::VEC;
-  static constexpr int LPV = D / VEC;      // lanes per token row
-  static constexpr int NG = kBlock / LPV;  // token groups per workgroup
+  static constexpr int LPV = D / VEC;   // lanes per token row
+  static constexpr int NG = NT / LPV;   // token groups of an NT-thread workgroup
   static_assert(LPV >= 1 && LPV <= 64 && (LPV & (LPV - 1)) == 0, "row must map to 2^n lanes");
 };
 
@@ -54,7 +54,7 @@ struct NoMask {
   __device__ __forceinline__ unsigned operator()(int) const { return 0xffffffffu; }
 };
 
-template <class E, int D, int NH, bool SPARSE, int U, class GetJ, class GetS,
+template <class E, int D, int NH, bool SPARSE, int U, int NT = kBlock, class GetJ, class GetS,
           class GetMask = NoMask>
 __device__ __forceinline__ void attend_loop(GetJ get_j, GetS get_s, int t0, int t1,
                                             const typename E::T* __restrict__ slab,
@@ -65,7 +65,7 @@ __device__ __forceinline__ void attend_loop(GetJ get_j, GetS get_s, int t0, int 
                                             const typename E::T* ko = nullptr,
                                             const typename E::T* vo = nullptr,
                                             GetMask get_mask = GetMask()) {
-  using G = Geo<E, D>;
+  using G = Geo<E, D, NT>;
   constexpr int VEC = G::VEC;
   constexpr int LPV = G::LPV;
   constexpr int NG = G::NG;
@@ -166,12 +166,12 @@ struct MergeSmem {
 };
 
 // Merge the group states.  Afterwards thread t handles outputs o = t,
-// t + kBlock, ... < NH*D (head o / D, dim o % D) and `fin(h, dim, M, L, A)`
+// t + NT, ... < NH*D (head o / D, dim o % D) and `fin(h, dim, M, L, A)`
 // is called with the merged max M, sum L and accumulator A.
-template <class E, int D, int NH, class Fin>
+template <class E, int D, int NH, int NT = kBlock, class Fin>
 __device__ __forceinline__ void merge_groups(const Acc<E::VEC> (&st)[NH],
-                                             MergeSmem<D, NH, Geo<E, D>::NG>& sm, Fin fin) {
-  using G = Geo<E, D>;
+                                             MergeSmem<D, NH, Geo<E, D, NT>::NG>& sm, Fin fin) {
+  using G = Geo<E, D, NT>;
   constexpr int VEC = G::VEC;
   constexpr int LPV = G::LPV;
   constexpr int NG = G::NG;
@@ -187,7 +187,7 @@ __device__ __forceinline__ void merge_groups(const Acc<E::VEC> (&st)[NH],
     for (int v = 0; v < VEC; ++v) sm.a[h][grp][r * VEC + v] = st[h].a[v];
   }
   __syncthreads();
-  for (int o = threadIdx.x; o < NH * D; o += kBlock) {
+  for (int o = threadIdx.x; o < NH * D; o += NT) {
     const int h = o / D, dim = o % D;
     float M = -INFINITY;
 #pragma unroll

@@ -33,12 +33,21 @@ struct FusedArgs {
   float scale_log2;
 };
 
-// SMALL: S <= 16 * kBlock, so the selection keeps 16 keys per thread.
+// Eight waves per row: the slab stream and the gather each keep twice the
+// bytes in flight of a four-wave workgroup, which is what bounds both.
+constexpr int kFusedBlock = 512;
+constexpr int kFusedKeys = 8;  // keys per thread of the SMALL selection
+
+// SMALL: S <= kFusedKeys * kFusedBlock, so the selection keeps the scores as
+// register keys with a first-digit histogram counted during the stream.
 template <class E, int D, int LPS, bool SMALL, bool STEP>
-__global__ void __launch_bounds__(kBlock) fused_kernel(FusedArgs a) {
+__global__ void __launch_bounds__(kFusedBlock) fused_kernel(FusedArgs a) {
   using T = typename E::T;
-  using Gm = Geo<E, D>;
+  constexpr int NT = kFusedBlock;
+  using Gm = Geo<E, D, NT>;
   constexpr int VEC = E::VEC;
+  // the rotation is formed by kBlock threads with the partition of
+  // rotate_kernel and score_kernel, so every path ranks with the same q'
   constexpr int CQ = D / 4;         // column quads of P
   constexpr int NRB = kBlock / CQ;  // row blocks of P
   constexpr int RB = D / NRB;       // rows per block
@@ -48,7 +57,7 @@ __global__ void __launch_bounds__(kBlock) fused_kernel(FusedArgs a) {
   };
   constexpr int CAP = 64;  // crossing bins up to this size are ranked directly
   struct Sel {
-    SelectSmemAny<kBlock> s;
+    SelectSmemAny<NT> s;
     uint32_t cand[CAP];
   };
   union Scratch {
@@ -78,7 +87,7 @@ __global__ void __launch_bounds__(kBlock) fused_kernel(FusedArgs a) {
   const T* vv = static_cast<const T*>(a.val) + bgo * a.S_max * D;
 
   if (SMALL)
-    for (int i = threadIdx.x; i < kSelBins; i += kBlock) hist0[i] = 0u;
+    for (int i = threadIdx.x; i < kSelBins; i += NT) hist0[i] = 0u;
 
   // 1. q' = q . P[g] (and, for STEP, k' = k_new . P[g] in float64): thread
   //    (cq, rb) adds rows [rb*RB, rb*RB + RB) for columns 4*cq .. 4*cq + 3,
@@ -90,7 +99,7 @@ __global__ void __launch_bounds__(kBlock) fused_kernel(FusedArgs a) {
           ld_elem<E>(static_cast<const T*>(a.k_new), bgo * D + threadIdx.x);
   }
   __syncthreads();
-  {
+  if (threadIdx.x < kBlock) {
     const int cq = threadIdx.x % CQ, rb = threadIdx.x / CQ;
     const float* Pg = a.P + static_cast<int64_t>(g) * D * D;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -151,11 +160,11 @@ __global__ void __launch_bounds__(kBlock) fused_kernel(FusedArgs a) {
     float qf[1][VEC];
 #pragma unroll
     for (int v = 0; v < VEC; ++v) qf[0][v] = (part * VEC < d) ? qs[part * VEC + v] : 0.f;
-    constexpr int US = 8;
+    constexpr int US = 4;  // 16-byte slab loads in flight per lane (8 waves)
     Chunk c[US];
-    score_first<E, LPS, US>(sl, d, 0, S, c);
+    score_first<E, LPS, US, NT>(sl, d, 0, S, c);
     // the selection's first radix digit is counted here, under the stream
-    score_loop<E, LPS, 1, US>(sl, d, 0, S, qf, [&](int, int j, float s) {
+    score_loop<E, LPS, 1, US, NT>(sl, d, 0, S, qf, [&](int, int j, float s) {
       sb[j] = s;
       if (SMALL) atomicAdd(&hist0[first_digit(order_key(s))], 1u);
     }, c);
@@ -191,10 +200,10 @@ __global__ void __launch_bounds__(kBlock) fused_kernel(FusedArgs a) {
       irow[p] = j;
     };
     if (SMALL)
-      block_select_topk_hist<kBlock, 16, CAP>([&](int j) { return sb[j]; }, S, kk, hist0, emit,
-                                              sc.sel.s.reg, sc.sel.cand);
+      block_select_topk_hist<NT, kFusedKeys, CAP>([&](int j) { return sb[j]; }, S, kk, hist0,
+                                                  emit, sc.sel.s.reg, sc.sel.cand);
     else
-      block_select_topk_any<kBlock>([&](int j) { return sb[j]; }, S, kk, emit, sc.sel.s);
+      block_select_topk_any<NT>([&](int j) { return sb[j]; }, S, kk, emit, sc.sel.s);
   }
   __syncthreads();
 
@@ -206,11 +215,11 @@ __global__ void __launch_bounds__(kBlock) fused_kernel(FusedArgs a) {
   for (int v = 0; v < VEC; ++v) qf[0][v] = (kd0 >= d) ? qs[kd0 + v] : 0.f;
   Acc<VEC> st[1];
   acc_init(st[0]);
-  attend_loop<E, D, 1, true, 4>([&](int t) { return ib[t]; },
+  attend_loop<E, D, 1, true, 4, NT>([&](int t) { return ib[t]; },
                                 [&](int, int, int j) { return sb[j]; }, 0, kk, sl, rs, vv, d,
                                 qf, a.scale_log2, st, STEP ? a.pos : -1, kslot, vslot);
   __syncthreads();  // the merge scratch aliases the selection scratch
-  merge_groups<E, D, 1>(st, sc.mrg, [&](int, int dim, float, float Ls, float A) {
+  merge_groups<E, D, 1, NT>(st, sc.mrg, [&](int, int dim, float, float Ls, float A) {
     a.out[row * D + dim] = A / Ls;
   });
 }
@@ -221,10 +230,12 @@ namespace {
 
 template <class E, int D, int LPS, bool STEP>
 hipError_t fused_t(const FusedArgs& fa, size_t lds, hipStream_t stream, int grid) {
-  if (fa.S <= 16 * kBlock)
-    hipLaunchKernelGGL((fused_kernel<E, D, LPS, true, STEP>), dim3(grid), dim3(kBlock), lds, stream, fa);
+  if (fa.S <= kFusedKeys * kFusedBlock)
+    hipLaunchKernelGGL((fused_kernel<E, D, LPS, true, STEP>), dim3(grid), dim3(kFusedBlock), lds,
+                       stream, fa);
   else
-    hipLaunchKernelGGL((fused_kernel<E, D, LPS, false, STEP>), dim3(grid), dim3(kBlock), lds, stream, fa);
+    hipLaunchKernelGGL((fused_kernel<E, D, LPS, false, STEP>), dim3(grid), dim3(kFusedBlock), lds,
+                       stream, fa);
   return hipGetLastError();
 }
 

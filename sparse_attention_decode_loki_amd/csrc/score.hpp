@@ -22,11 +22,11 @@ __device__ __forceinline__ int xcd_logical(int bid, int n) {
 // streamed with fully coalesced 16-byte loads.  score_first issues the first
 // batch of loads, which do not depend on the query, so a caller can start
 // them before the query is rotated.
-template <class E, int LPS, int U>
+template <class E, int LPS, int U, int NT = kBlock>
 __device__ __forceinline__ void score_first(const typename E::T* __restrict__ slab, int d, int j0,
                                             int j1, Chunk (&c)[U]) {
   constexpr int VEC = E::VEC;
-  constexpr int TPI = kBlock / LPS;
+  constexpr int TPI = NT / LPS;
   const int part = threadIdx.x % LPS;
   const int tk = threadIdx.x / LPS;
   const bool active = part * VEC < d;
@@ -41,12 +41,12 @@ __device__ __forceinline__ void score_first(const typename E::T* __restrict__ sl
 }
 
 // c holds the first batch (from score_first).
-template <class E, int LPS, int NH, int U, class Write>
+template <class E, int LPS, int NH, int U, int NT = kBlock, class Write>
 __device__ __forceinline__ void score_loop(const typename E::T* __restrict__ slab, int d, int j0,
                                            int j1, const float (&qf)[NH][E::VEC], Write write,
                                            Chunk (&c)[U]) {
   constexpr int VEC = E::VEC;
-  constexpr int TPI = kBlock / LPS;
+  constexpr int TPI = NT / LPS;
   const int part = threadIdx.x % LPS;
   const int tk = threadIdx.x / LPS;
   const bool active = part * VEC < d;
