@@ -303,10 +303,10 @@ __global__ void __launch_bounds__(BLOCK) topk_kernel(const float* __restrict__ s
     }
     for (int i = (n4 << 2) + threadIdx.x; i < S; i += BLOCK) sbuf[i + (i >> 5)] = s[i];
     __syncthreads();
-    block_select_topk_any<BLOCK>([&](int j) { return sbuf[j + (j >> 5)]; }, S, k, emit, sm);
+    block_select_topk_any<BLOCK, true>([&](int j) { return sbuf[j + (j >> 5)]; }, S, k, emit, sm);
   } else {
     __syncthreads();
-    block_select_topk_any<BLOCK>([&](int j) { return s[j]; }, S, k, emit, sm);
+    block_select_topk_any<BLOCK, true>([&](int j) { return s[j]; }, S, k, emit, sm);
   }
   if (stage_out) {
     __syncthreads();

@@ -124,7 +124,21 @@ namespace loki {
 // radix select uses three digits (11, 11 and 10 bits) on one shared LDS
 // histogram, and the compaction needs a single block-wide scan because each
 // thread's elements are consecutive in index order.  Requires S <= BLOCK*EMAX.
+//
+// With LIN, a first pass bins the values linearly between the row's minimum
+// and maximum.  The leading radix digit (sign, exponent, two mantissa bits)
+// puts most of a bell-shaped row into a dozen bins, whose LDS atomics then
+// serialise and whose crossing bin still holds a few percent of the row;
+// linear bins spread the same row evenly, so the bin that holds the k-th
+// value usually has only tens of scores, which are ranked against each other
+// directly.  The bin of a value is a monotone function of it (a subtraction
+// and a multiplication, each rounded, then a truncation clamped to the end
+// bins), so every value in a higher bin is larger than every value in a
+// lower one.  When the crossing bin holds more than kLinCap scores (heavy
+// ties, or outliers spread over the row) the radix passes run as without
+// LIN.
 constexpr int kSelBins = 2048;
+constexpr int kLinCap = 128;
 
 template <int BLOCK>
 struct SelectSmemR {
@@ -132,7 +146,33 @@ struct SelectSmemR {
   unsigned hist[kSelBins];
   unsigned wsum[2][NW];
   unsigned bin, above, cnt;
+  uint32_t wmin[NW], wmax[NW];
+  __attribute__((aligned(16))) uint32_t cand[kLinCap];
 };
+
+// The value an order key stands for (+0.0 for the key of both zeros).
+__device__ __forceinline__ float key_value(uint32_t key) {
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
+}
+
+// Minimum and maximum over the 64 lanes of a wave, returned to every lane:
+// a DPP butterfly within each row of 16 lanes, then the four rows' results
+// read as scalars.
+__device__ __forceinline__ void wave_minmax(uint32_t& mn, uint32_t& mx) {
+  mn = min(mn, dpp_u<0xB1>(mn));
+  mx = max(mx, dpp_u<0xB1>(mx));
+  mn = min(mn, dpp_u<0x4E>(mn));
+  mx = max(mx, dpp_u<0x4E>(mx));
+  mn = min(mn, dpp_u<0x141>(mn));
+  mx = max(mx, dpp_u<0x141>(mx));
+  mn = min(mn, dpp_u<0x140>(mn));
+  mx = max(mx, dpp_u<0x140>(mx));
+  const auto rl = [](uint32_t v, int l) {
+    return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), l));
+  };
+  mn = min(min(rl(mn, 0), rl(mn, 16)), min(rl(mn, 32), rl(mn, 48)));
+  mx = max(max(rl(mx, 0), rl(mx, 16)), max(rl(mx, 32), rl(mx, 48)));
+}
 
 // Exclusive prefix over the block of one value per thread; returns it and
 // the block total in `total`.  Contains one barrier; `buf` selects one of two
@@ -196,10 +236,156 @@ __device__ __forceinline__ void emit_kept(const uint32_t (&key)[EMAX], int nvali
   }
 }
 
-template <int BLOCK, int EMAX, class Src, class Emit>
+// Crossing bin of the kSelBins-bin histogram `hist` for the krem-th largest
+// key, scanned top-down (thread t owns bins [kSelBins - PER*(t+1), kSelBins -
+// PER*t)): sets sm.bin, sm.above (keys in higher bins), sm.cnt (keys in the
+// bin); ends with a barrier.
+template <int BLOCK>
+__device__ __forceinline__ void crossing_bin(const unsigned* hist, int krem, SelectSmemR<BLOCK>& sm,
+                                             int& buf) {
+  constexpr int PER = kSelBins / BLOCK;
+  const int hi = kSelBins - PER * static_cast<int>(threadIdx.x);
+  unsigned c[PER];
+  unsigned local = 0u;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    c[i] = hist[hi - 1 - i];
+    local += c[i];
+  }
+  unsigned total;
+  unsigned above = block_excl_scan<BLOCK>(local, total, sm, buf);
+  buf ^= 1;
+  if (above < static_cast<unsigned>(krem) && static_cast<unsigned>(krem) <= above + local) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      if (above < static_cast<unsigned>(krem) && static_cast<unsigned>(krem) <= above + c[i]) {
+        sm.bin = static_cast<unsigned>(hi - 1 - i);
+        sm.above = above;
+        sm.cnt = c[i];
+      }
+      above += c[i];
+    }
+  }
+  __syncthreads();
+}
+
+// The linear first pass of block_select_topk_reg<..., LIN>.  Returns true
+// and sets prefix (the k-th largest key), mask (all ones) and krem (how many
+// keys equal to it are kept) when the crossing bin holds at most kLinCap
+// keys; returns false (nothing decided) otherwise.
+template <int BLOCK, int EMAX>
+__device__ __forceinline__ bool linear_select(const uint32_t (&key)[EMAX], int nvalid, int k,
+                                              SelectSmemR<BLOCK>& sm, int& buf, uint32_t& prefix,
+                                              uint32_t& mask, int& krem) {
+  constexpr int NW = BLOCK / 64;
+  static_assert(EMAX <= 32, "one member bit per key");
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // row minimum and maximum (as keys: the order map is monotone)
+  uint32_t kmin = 0xffffffffu, kmax = 0u;
+#pragma unroll
+  for (int e = 0; e < EMAX; ++e)
+    if (e < nvalid) {
+      kmin = min(kmin, key[e]);
+      kmax = max(kmax, key[e]);
+    }
+  wave_minmax(kmin, kmax);
+  if (lane == 0) {
+    sm.wmin[wave] = kmin;
+    sm.wmax[wave] = kmax;
+  }
+  for (int i = tid; i < kSelBins; i += BLOCK) sm.hist[i] = 0u;
+  __syncthreads();
+  // The bins span the second-smallest to the second-largest wave extreme,
+  // values beyond them going to the end bins: a few outliers in one wave (the
+  // attention sinks of a cache's first tokens) then do not squeeze the rest
+  // of the row into a few bins.
+  static_assert(NW >= 2, "two waves at least");
+  uint32_t min1 = 0xffffffffu, min2 = 0xffffffffu, max1 = 0u, max2 = 0u;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const uint32_t a = sm.wmin[w], b = sm.wmax[w];
+    min2 = a < min1 ? min1 : min(min2, a);
+    min1 = min(min1, a);
+    max2 = b > max1 ? max1 : max(max2, b);
+    max1 = max(max1, b);
+  }
+  kmin = min2;
+  kmax = max2;
+  const float lo = key_value(kmin);
+  const float range = key_value(kmax) - lo;
+  const float scale = static_cast<float>(kSelBins) / range;
+  // a zero, overflowing or denormal range leaves the radix passes to decide
+  if (!(range > 0.f && range < INFINITY && scale < INFINITY)) return false;
+  auto bin_of = [&](uint32_t kk) -> int {
+    const float f = (key_value(kk) - lo) * scale;
+    return f >= static_cast<float>(kSelBins - 1) ? kSelBins - 1 : (f > 0.f ? static_cast<int>(f) : 0);
+  };
+  // each key's bin, kept in registers two to a word
+  uint32_t bins[(EMAX + 1) / 2];
+#pragma unroll
+  for (int i = 0; i < (EMAX + 1) / 2; ++i) bins[i] = 0u;
+#pragma unroll
+  for (int e = 0; e < EMAX; ++e)
+    if (e < nvalid) {
+      const int bn = bin_of(key[e]);
+      bins[e >> 1] |= static_cast<uint32_t>(bn) << (16 * (e & 1));
+      atomicAdd(&sm.hist[bn], 1u);
+    }
+  __syncthreads();
+  crossing_bin<BLOCK>(sm.hist, k, sm, buf);
+  const uint32_t bstar = sm.bin;
+  const int above = static_cast<int>(sm.above);
+  const int nbin = static_cast<int>(sm.cnt);
+  if (nbin > kLinCap) return false;  // (uniform: every thread read the same values)
+  // collect the crossing bin's keys (the scan's barrier also ends every
+  // thread's reads of sm.bin / sm.above / sm.cnt above), then rank them
+  uint32_t member = 0u;
+#pragma unroll
+  for (int e = 0; e < EMAX; ++e)
+    member |= static_cast<uint32_t>(e < nvalid && ((bins[e >> 1] >> (16 * (e & 1))) & 0xffffu) == bstar)
+              << e;
+  unsigned total;
+  unsigned at = block_excl_scan<BLOCK>(static_cast<unsigned>(__popc(member)), total, sm, buf);
+  buf ^= 1;
+  if (member) {
+#pragma unroll
+    for (int e = 0; e < EMAX; ++e)
+      if ((member >> e) & 1u) sm.cand[at++] = key[e];
+  }
+  __syncthreads();
+  const int kin = k - above;  // 1 <= kin <= nbin
+  if (tid < nbin) {
+    const uint32_t x = sm.cand[tid];
+    int gt = 0, ge = 0;
+    const int n4 = nbin & ~3;
+    for (int m = 0; m < n4; m += 4) {
+      const uint4 y = *reinterpret_cast<const uint4*>(&sm.cand[m]);
+      gt += (y.x > x) + (y.y > x) + (y.z > x) + (y.w > x);
+      ge += (y.x >= x) + (y.y >= x) + (y.z >= x) + (y.w >= x);
+    }
+    for (int m = n4; m < nbin; ++m) {
+      const uint32_t y = sm.cand[m];
+      gt += y > x;
+      ge += y >= x;
+    }
+    // the k-th key: every thread holding its value writes the same result
+    if (gt < kin && kin <= ge) {
+      sm.bin = x;
+      sm.above = static_cast<unsigned>(gt);
+    }
+  }
+  __syncthreads();
+  prefix = sm.bin;
+  mask = 0xffffffffu;
+  krem = kin - static_cast<int>(sm.above);
+  return true;
+}
+
+template <int BLOCK, int EMAX, bool LIN = false, class Src, class Emit>
 __device__ void block_select_topk_reg(Src src, int S, int k, Emit emit, SelectSmemR<BLOCK>& sm) {
   constexpr int PER = kSelBins / BLOCK;  // histogram bins owned per thread in the scan
   static_assert(kSelBins % BLOCK == 0, "bins must split evenly");
+  static_assert(!LIN || BLOCK >= kLinCap, "one thread per ranked key");
   const int tid = threadIdx.x;
   const int E = (S + BLOCK - 1) / BLOCK;
   const int j0 = tid * E;
@@ -215,7 +401,7 @@ __device__ void block_select_topk_reg(Src src, int S, int k, Emit emit, SelectSm
   uint32_t prefix = 0u, mask = 0u;
   int krem = k;
   int buf = 0;
-  if (k < S) {
+  if (k < S && !(LIN && linear_select<BLOCK, EMAX>(key, nvalid, k, sm, buf, prefix, mask, krem))) {
     const int shifts[3] = {21, 10, 0};
     const int widths[3] = {11, 11, 10};
     for (int pass = 0; pass < 3; ++pass) {
@@ -273,13 +459,16 @@ union SelectSmemAny {
 };
 
 // Top-k with the register-resident select when each thread's share fits in
-// 32 registers, else the LDS/global-resident one.
-template <int BLOCK, class Src, class Emit>
+// 32 registers, else the LDS/global-resident one.  LIN asks for the linear
+// first pass where each thread holds at most 16 keys (a 4096-score row: 8.3
+// -> 7.7 us for 32 rows); at 32 keys per thread its extra per-key work costs
+// more than the radix passes it saves.
+template <int BLOCK, bool LIN = false, class Src, class Emit>
 __device__ __forceinline__ void block_select_topk_any(Src src, int S, int k, Emit emit,
                                                       SelectSmemAny<BLOCK>& sm) {
   if (S <= BLOCK * 16)
-    block_select_topk_reg<BLOCK, 16>(src, S, k, emit, sm.reg);
-  else if (S <= BLOCK * 32)
+    block_select_topk_reg<BLOCK, 16, LIN>(src, S, k, emit, sm.reg);
+  else if (S <= BLOCK * 32)  // the linear pass does not pay at 32 keys per thread
     block_select_topk_reg<BLOCK, 32>(src, S, k, emit, sm.reg);
   else
     block_select_topk<BLOCK>(src, S, k, emit, sm.lds);

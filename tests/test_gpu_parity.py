@@ -149,6 +149,37 @@ def test_topk_crossing_bin_sizes(lib, n, ties):
         assert np.array_equal(idx[r].astype(np.int64), want), f"row {r}"
 
 
+@pytest.mark.parametrize("kind", ["denormal", "huge_range", "outliers", "two_values", "tiny_range"])
+def test_topk_extreme_value_ranges(lib, kind):
+    """Rows whose value range is zero, denormal, beyond float32 (max - min
+    overflows) or dominated by a few outliers: selections whose first pass
+    cannot bin linearly, or whose crossing bin is crowded, still match the
+    oracle."""
+    import torch
+    rng = np.random.default_rng(["denormal", "huge_range", "outliers", "two_values",
+                                 "tiny_range"].index(kind) + 500)
+    S, k = 5000, 1234
+    if kind == "denormal":
+        row = (rng.integers(1, 1 << 20, S) * np.float32(1e-45)).astype(np.float32)
+    elif kind == "huge_range":
+        row = rng.standard_normal(S).astype(np.float32)
+        row[rng.integers(0, S, 3)] = np.float32(3e38)
+        row[rng.integers(0, S, 3)] = np.float32(-3e38)
+    elif kind == "outliers":
+        row = rng.standard_normal(S).astype(np.float32)
+        row[:4] = np.float32(1e6)
+    elif kind == "two_values":
+        row = np.where(rng.random(S) < 0.5, np.float32(2.0), np.float32(-7.0)).astype(np.float32)
+    else:
+        row = (np.float32(1.0) + rng.integers(0, 64, S).astype(np.float32) * np.float32(2 ** -23))
+    host = np.stack([row, row[::-1].copy()])
+    assert np.all(np.isfinite(host))
+    idx = lib.topk(torch.from_numpy(host).cuda(), k).cpu().numpy()
+    for r in range(2):
+        want = oracle.select_topk(host[r].astype(np.float64), k)
+        assert np.array_equal(idx[r].astype(np.int64), want), f"row {r}"
+
+
 def test_topk_crossing_bin_of_signed_zeros(lib):
     """A crossing bin made of +0.0 and -0.0 only: they rank equal, so the
     lowest indices among them are kept."""
