@@ -35,7 +35,14 @@ is listed in the design notes):
      sign fixed so that its largest-magnitude entry (lowest index among equal
      magnitudes) is positive; cached keys are rotated without subtracting the
      mean;
-  J  query head h reads KV head floor(h / (Hq / Hkv)).
+  J  query head h reads KV head floor(h / (Hq / Hkv));
+  R  (RoPE variant) keys carry the rotary position embedding of their cache
+     position and the query that of its own position, applied before the PCA
+     rotation; dims i and i + D/2 are rotated together by the angle
+     pos * base^(-2i/D).  Attention always uses embedded keys; "pre-rotary"
+     and "post-rotary" differ only in whether P is calibrated from keys before
+     or after the embedding [summary: Measured effects (pre-rotary ablation);
+     Surprising findings].
 
 Every function here computes in float64 from the exact values of its inputs
 (bf16 and float32 values are exactly representable in float64).
@@ -123,6 +130,29 @@ def calibrate(keys: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
     return V, w
 
 
+# -------------------------------------------------------------------- RoPE --
+
+
+def rope_embed(x: np.ndarray, pos, base: float) -> np.ndarray:
+    """Rotary position embedding of row vectors (the rotation the pages list
+    Loki as building on [summary: "Builds on"]; reading R).
+
+    x [..., D] with D even; pos a scalar or an array broadcasting against
+    x[..., 0] (one position per row).  For i < D/2 the pair (x_i, x_{i+D/2})
+    is rotated by the angle pos * base^(-2i/D):
+        x_i       -> x_i cos - x_{i+D/2} sin
+        x_{i+D/2} -> x_{i+D/2} cos + x_i sin
+    """
+    x = np.asarray(x, dtype=np.float64)
+    D = x.shape[-1]
+    h = D // 2
+    theta = float(base) ** (-2.0 * np.arange(h, dtype=np.float64) / D)
+    ang = np.asarray(pos, dtype=np.float64)[..., None] * theta
+    c, s = np.cos(ang), np.sin(ang)
+    a, b = x[..., :h], x[..., h:]
+    return np.concatenate([a * c - b * s, b * c + a * s], axis=-1)
+
+
 # ------------------------------------------------------------------ append --
 
 
@@ -131,14 +161,19 @@ def rotate(x: np.ndarray, P: np.ndarray) -> np.ndarray:
     return np.asarray(x, dtype=np.float64) @ np.asarray(P, dtype=np.float64)
 
 
-def append(k_new: np.ndarray, v_new: np.ndarray, P: np.ndarray, d: int, dtype: str):
+def append(k_new: np.ndarray, v_new: np.ndarray, P: np.ndarray, d: int, dtype: str,
+           rope_base: float | None = None, pos: int = 0):
     """Cache entries for new tokens: keys rotated into the PCA basis and split
     into the leading-d slab and the remaining D-d columns; values unchanged.
 
-    k_new, v_new: [..., T, D] exact float64 values; P [D, D].
+    k_new, v_new: [..., T, D] exact float64 values; P [D, D].  With
+    rope_base, token t is first embedded at position pos + t (reading R).
     Returns (slab [..., T, d], rest [..., T, D-d], v [..., T, D]) rounded to
     `dtype` to nearest even.
     """
+    if rope_base is not None:
+        T = np.asarray(k_new).shape[-2]
+        k_new = rope_embed(k_new, pos + np.arange(T), rope_base)
     kp = rotate(k_new, P)
     return (from_f64(kp[..., :d], dtype), from_f64(kp[..., d:], dtype),
             from_f64(v_new, dtype))
@@ -217,15 +252,16 @@ def kv_head(h: int, Hq: int, Hkv: int) -> int:
     return h // (Hq // Hkv)
 
 
-def decode(q, kslab, krest, v, P, k, dtype, S=None, heads=None):
+def decode(q, kslab, krest, v, P, k, dtype, S=None, heads=None, rope=None):
     """Decode step for a batch (the oracle of loki_decode).
 
     q [B, Hq, D], kslab [B, Hkv, S_max, d], krest [B, Hkv, S_max, D-d],
     v [B, Hkv, S_max, D] in storage form (`dtype` "bf16" bits, "f32", "f64");
     P [Hkv, D, D].  Only the first S cached positions are read.
     heads: optional iterable of (b, h) pairs to compute (others are left NaN /
-    -1).  Returns (out [B, Hq, D] float64, idx [B, Hq, min(k,S)] int64,
-    s [B, Hq, S] float64).
+    -1).  rope: optional (base, q_pos), the query's embedding (reading R; the
+    cache then holds embedded keys).  Returns (out [B, Hq, D] float64,
+    idx [B, Hq, min(k,S)] int64, s [B, Hq, S] float64).
     """
     B, Hq, D = q.shape
     Hkv = kslab.shape[1]
@@ -243,7 +279,10 @@ def decode(q, kslab, krest, v, P, k, dtype, S=None, heads=None):
             cache[(b, g)] = (to_f64(kslab[b, g, :S], dtype), to_f64(krest[b, g, :S], dtype),
                              to_f64(v[b, g, :S], dtype))
         ks, kr, vv = cache[(b, g)]
-        o, i, sc = decode_head(to_f64(q[b, h], dtype), np.asarray(P[g], np.float64), ks, kr, vv, kk)
+        qv = to_f64(q[b, h], dtype)
+        if rope is not None:
+            qv = rope_embed(qv, rope[1], rope[0])
+        o, i, sc = decode_head(qv, np.asarray(P[g], np.float64), ks, kr, vv, kk)
         out[b, h], idx[b, h], s[b, h] = o, i, sc
     return out, idx, s
 
@@ -279,9 +318,9 @@ def dense_attention(q: np.ndarray, K: np.ndarray, V: np.ndarray) -> np.ndarray:
     return w @ V
 
 
-def dense_decode(q, kslab, krest, v, P, dtype, S=None, heads=None):
+def dense_decode(q, kslab, krest, v, P, dtype, S=None, heads=None, rope=None):
     """Full attention over all S cached tokens of the rotated cache: the
-    oracle of loki_dense_decode.  Same layouts as decode()."""
+    oracle of loki_dense_decode.  Same layouts (and rope) as decode()."""
     B, Hq, D = q.shape
     Hkv = kslab.shape[1]
     S = kslab.shape[2] if S is None else S
@@ -290,7 +329,10 @@ def dense_decode(q, kslab, krest, v, P, dtype, S=None, heads=None):
     for b, h in pairs:
         g = kv_head(h, Hq, Hkv)
         K = np.concatenate([to_f64(kslab[b, g, :S], dtype), to_f64(krest[b, g, :S], dtype)], axis=-1)
-        qp = rotate(to_f64(q[b, h], dtype), np.asarray(P[g], np.float64))
+        qv = to_f64(q[b, h], dtype)
+        if rope is not None:
+            qv = rope_embed(qv, rope[1], rope[0])
+        qp = rotate(qv, np.asarray(P[g], np.float64))
         out[b, h] = dense_attention(qp, K, to_f64(v[b, g, :S], dtype))
     return out
 

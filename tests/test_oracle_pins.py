@@ -344,3 +344,91 @@ def test_append_bf16_within_half_ulp():
     got = np.concatenate([oracle.bf16_to_f64(slab), oracle.bf16_to_f64(rest)], axis=1)
     _, e = np.frexp(exact)
     assert np.all(np.abs(got - exact) <= np.ldexp(1.0, e - 9) * (1 + 1e-12))
+
+
+# ------------------------------------------------------------------- RoPE --
+
+def test_rope_closed_form_on_basis_vectors():
+    # D = 4, base 10000: pair (0, 2) turns by pos, pair (1, 3) by pos / 100
+    p = 3.0
+    e0, e1, e2 = np.eye(4)[0], np.eye(4)[1], np.eye(4)[2]
+    assert np.allclose(oracle.rope_embed(e0, p, 10000.0), [math.cos(p), 0, math.sin(p), 0],
+                       rtol=0, atol=1e-15)
+    assert np.allclose(oracle.rope_embed(e1, p, 10000.0),
+                       [0, math.cos(p / 100), 0, math.sin(p / 100)], rtol=0, atol=1e-15)
+    # the second member of a pair turns the same way: (0, 1) -> (-sin, cos)
+    assert np.allclose(oracle.rope_embed(e2, p, 10000.0), [-math.sin(p), 0, math.cos(p), 0],
+                       rtol=0, atol=1e-15)
+    # D = 8, base 4: theta_i = 4^(-i/4) = 2^(-i/2)
+    x = np.zeros(8)
+    x[3] = 1.0
+    got = oracle.rope_embed(x, 2.0, 4.0)
+    ang = 2.0 * 2.0 ** -1.5
+    want = np.zeros(8)
+    want[3], want[7] = math.cos(ang), math.sin(ang)
+    assert np.allclose(got, want, rtol=0, atol=1e-15)
+
+
+def test_rope_position_zero_identity_norms_and_composition():
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((5, 16))
+    assert np.array_equal(oracle.rope_embed(x, 0, 10000.0), x)
+    y = oracle.rope_embed(x, 37, 10000.0)
+    # every (i, i + D/2) pair keeps its length
+    assert np.allclose(x[:, :8] ** 2 + x[:, 8:] ** 2, y[:, :8] ** 2 + y[:, 8:] ** 2, rtol=1e-13)
+    # turning by a then by b is turning by a + b; by -a undoes a
+    assert np.allclose(oracle.rope_embed(y, 5, 10000.0), oracle.rope_embed(x, 42, 10000.0),
+                       rtol=0, atol=1e-12)
+    assert np.allclose(oracle.rope_embed(y, -37, 10000.0), x, rtol=0, atol=1e-12)
+
+
+def test_rope_scores_depend_on_relative_position_only():
+    # <R_m q, R_n k> = <R_(m-n) q, k>: the property rotary embedding is built for
+    rng = np.random.default_rng(12)
+    q, K = rng.standard_normal(32), rng.standard_normal((6, 32))
+    n = np.array([0, 3, 10, 100, 4000, 32767])
+    m = 32767
+    lhs = oracle.rope_embed(K, n, 500000.0) @ oracle.rope_embed(q, m, 500000.0)
+    rhs = np.array([oracle.rope_embed(q, m - nj, 500000.0) @ K[j] for j, nj in enumerate(n)])
+    assert np.allclose(lhs, rhs, rtol=0, atol=1e-9)
+
+
+def test_rope_per_row_positions_match_scalar_calls():
+    rng = np.random.default_rng(13)
+    K = rng.standard_normal((4, 8))
+    pos = np.array([0, 1, 7, 1000])
+    rows = np.stack([oracle.rope_embed(K[i], pos[i], 10000.0) for i in range(4)])
+    assert np.array_equal(oracle.rope_embed(K, pos, 10000.0), rows)
+
+
+def test_rope_append_embeds_each_token_at_its_slot():
+    rng = np.random.default_rng(14)
+    D, d, T, pos = 8, 3, 5, 20
+    P = _haar(rng, D)
+    K, V = rng.standard_normal((T, D)), rng.standard_normal((T, D))
+    slab, rest, vv = oracle.append(K, V, P, d, "f64", rope_base=10000.0, pos=pos)
+    want = np.stack([oracle.rope_embed(K[t], pos + t, 10000.0) for t in range(T)]) @ P
+    assert np.allclose(np.concatenate([slab, rest], axis=-1), want, rtol=0, atol=1e-13)
+    assert np.array_equal(vv, V)
+
+
+def test_rope_decode_full_budget_is_dense_attention_on_embedded_keys():
+    # d = D, k = S with embedded keys and query: softmax((R_m q).(R_j k_j)/sqrt(D)).V
+    rng = np.random.default_rng(15)
+    S, D, m, base = 30, 8, 29, 10000.0
+    P = _haar(rng, D)
+    K, V, q = rng.standard_normal((S, D)), rng.standard_normal((S, D)), rng.standard_normal(D)
+    slab, rest, vv = oracle.append(K, V, P, D, "f64", rope_base=base, pos=0)
+    out, idx, _ = oracle.decode(q[None, None], slab[None, None], rest[None, None], vv[None, None],
+                                P[None], S, "f64", rope=(base, m))
+    Ke = oracle.rope_embed(K, np.arange(S), base)
+    want = oracle.dense_attention(oracle.rope_embed(q, m, base), Ke, V)
+    assert idx[0, 0].tolist() == list(range(S))
+    assert np.allclose(out[0, 0], want, rtol=0, atol=1e-12)
+    dense = oracle.dense_decode(q[None, None], slab[None, None], rest[None, None], vv[None, None],
+                                P[None], "f64", rope=(base, m))
+    assert np.allclose(dense[0, 0], want, rtol=0, atol=1e-12)
+    # without the query's embedding the result differs: the option is applied
+    plain, _, _ = oracle.decode(q[None, None], slab[None, None], rest[None, None],
+                                vv[None, None], P[None], S, "f64")
+    assert not np.allclose(plain[0, 0], want, atol=1e-6)
