@@ -91,7 +91,7 @@ const char* loki_status_string(int status);
 
 /* ABI revision of this header, incremented on any signature change; a caller
  * compares it with loki_abi_version() of the library it loaded. */
-#define LOKI_ABI_VERSION 2
+#define LOKI_ABI_VERSION 3
 
 /* ABI revision the library was built with (LOKI_ABI_VERSION of its header). */
 int loki_abi_version(void);
@@ -210,6 +210,51 @@ int loki_dense_decode(const void* q, const void* k_slab, const void* k_rest, con
                       const float* P, int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t d,
                       int32_t S, int32_t S_max, int32_t dtype, float* out,
                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---- Rotary position embedding (RoPE) variant ----------------------------
+ *
+ * The pages evaluate Loki on models whose attention uses rotary position
+ * embeddings, and find a basis calibrated on keys before the embedding
+ * ("pre-rotary") better than one calibrated after it, although attention
+ * uses the embedded keys either way ("Measured effects", "Surprising
+ * findings").  These entry points apply the embedding inside the library:
+ * each key is embedded at its cache position before its PCA rotation, and
+ * the query at q_pos before its own.  Pre- or post-rotary is only a choice of
+ * the keys given to loki_calibrate.  The embedding turns dims i and i + D/2
+ * together by the angle pos * rope_base^(-2i/D), computed in float64 (the
+ * pages name RoPE but not its form; this is the Llama-family pairing).
+ * rope_base must be finite and > 0 (10000 for Llama2, 500000 for Llama3) and
+ * q_pos >= 0, else LOKI_EINVAL.  A cache must be filled with the _rope
+ * append (same base) for these decodes to mean attention over embedded
+ * keys; the library cannot tell. */
+
+/* loki_kv_append, embedding new token t at position pos + t first. */
+int loki_kv_append_rope(const void* k_new, const void* v_new, const float* P,
+                        void* k_slab, void* k_rest, void* v,
+                        int32_t B, int32_t Hkv, int32_t D, int32_t d, int32_t S_max,
+                        int32_t pos, int32_t T, int32_t dtype, double rope_base, void* stream);
+
+/* loki_decode_ex with the query embedded at position q_pos (usually S - 1,
+ * the position of the token being generated). */
+int loki_decode_rope(const void* q, const void* k_slab, const void* k_rest, const void* v,
+                     const float* P, int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t d,
+                     int32_t S, int32_t S_max, int32_t k, int32_t dtype, int32_t q_pos,
+                     double rope_base, float* out, int32_t* idx, void* workspace,
+                     size_t workspace_bytes, int32_t path, void* stream);
+
+/* loki_decode_step with the new key and the query both embedded at pos. */
+int loki_decode_step_rope(const void* q, const void* k_new, const void* v_new, const float* P,
+                          void* k_slab, void* k_rest, void* v, int32_t B, int32_t Hq,
+                          int32_t Hkv, int32_t D, int32_t d, int32_t pos, int32_t S_max,
+                          int32_t k, int32_t dtype, double rope_base, float* out, int32_t* idx,
+                          void* workspace, size_t workspace_bytes, int32_t path, void* stream);
+
+/* loki_dense_decode with the query embedded at position q_pos. */
+int loki_dense_decode_rope(const void* q, const void* k_slab, const void* k_rest, const void* v,
+                           const float* P, int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                           int32_t d, int32_t S, int32_t S_max, int32_t dtype, int32_t q_pos,
+                           double rope_base, float* out, void* workspace,
+                           size_t workspace_bytes, void* stream);
 
 /* Measurement helper, not part of the method: reads `bytes` of device memory
  * at buf (16-byte aligned, bytes a multiple of 16) with nontemporal 16-byte

@@ -23,6 +23,7 @@ PATH_AUTO, PATH_FUSED, PATH_SPLIT, PATH_UNION = 0, 1, 2, 3
 # name -> (restype, argtypes); mirrors include/loki.h
 _P = ctypes.c_void_p
 _I = ctypes.c_int32
+_F64 = ctypes.c_double
 _SIGS = {
     "loki_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "loki_abi_version": (ctypes.c_int, []),
@@ -44,6 +45,15 @@ _SIGS = {
     "loki_dense_decode": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P,
                                          _P, ctypes.c_size_t, _P]),
     "loki_stream_read": (ctypes.c_int, [_P, ctypes.c_size_t, _P, _I, _P]),
+    "loki_kv_append_rope": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I,
+                                           _F64, _P]),
+    "loki_decode_rope": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I,
+                                        _F64, _P, _P, _P, ctypes.c_size_t, _I, _P]),
+    "loki_decode_step_rope": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I,
+                                             _I, _I, _I, _F64, _P, _P, _P, ctypes.c_size_t, _I,
+                                             _P]),
+    "loki_dense_decode_rope": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I,
+                                              _I, _F64, _P, _P, ctypes.c_size_t, _P]),
 }
 
 _lib = None
@@ -149,18 +159,24 @@ def calibrate(keys: np.ndarray):
     return P, ev
 
 
-def append(cache: KVCache, k_new, v_new, P, pos: int | None = None):
+def append(cache: KVCache, k_new, v_new, P, pos: int | None = None,
+           rope_base: float | None = None):
     """Rotate and store k_new/v_new [B, Hkv, T, D] at positions pos..pos+T-1
-    (default: the cache's current length, which then advances)."""
+    (default: the cache's current length, which then advances).  With
+    rope_base, each key is first given the rotary embedding of its position
+    (loki_kv_append_rope)."""
     lib = load()
     _need(k_new, "k_new", cache.dtype)
     _need(v_new, "v_new", cache.dtype)
     _need(P, "P", _torch().float32)
     B, Hkv, T, D = k_new.shape
     at = cache.length if pos is None else pos
-    st = lib.loki_kv_append(_ptr(k_new), _ptr(v_new), _ptr(P), _ptr(cache.k_slab),
-                            _ptr(cache.k_rest), _ptr(cache.v), B, Hkv, D, cache.d, cache.S_max,
-                            at, T, _dtype_code(k_new), _stream(k_new))
+    args = (_ptr(k_new), _ptr(v_new), _ptr(P), _ptr(cache.k_slab), _ptr(cache.k_rest),
+            _ptr(cache.v), B, Hkv, D, cache.d, cache.S_max, at, T, _dtype_code(k_new))
+    if rope_base is None:
+        st = lib.loki_kv_append(*args, _stream(k_new))
+    else:
+        st = lib.loki_kv_append_rope(*args, float(rope_base), _stream(k_new))
     _check(st, "loki_kv_append")
     if pos is None or at + T > cache.length:
         cache.length = max(cache.length, at + T)
@@ -177,9 +193,12 @@ def alloc_workspace(B, Hq, D, S_max, k_max, device="cuda"):
 
 
 def decode(q, cache: KVCache, P, k: int, S: int | None = None, out=None, idx=None,
-           workspace=None, path: int = PATH_AUTO):
+           workspace=None, path: int = PATH_AUTO, rope_base: float | None = None,
+           q_pos: int | None = None):
     """One Loki decode step.  q [B, Hq, D] -> (out [B, Hq, D] float32,
-    idx [B, Hq, min(k, S)] int32 ascending)."""
+    idx [B, Hq, min(k, S)] int32 ascending).  With rope_base the query is
+    given the rotary embedding of position q_pos (default S - 1) first
+    (loki_decode_rope; the cache must hold embedded keys)."""
     torch = _torch()
     lib = load()
     _need(q, "q", cache.dtype)
@@ -194,17 +213,24 @@ def decode(q, cache: KVCache, P, k: int, S: int | None = None, out=None, idx=Non
     if workspace is None and path != PATH_FUSED:
         workspace = alloc_workspace(B, Hq, D, cache.S_max, kk, q.device)
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib.loki_decode_ex(_ptr(q), _ptr(cache.k_slab), _ptr(cache.k_rest), _ptr(cache.v), _ptr(P),
-                            B, Hq, cache.Hkv, D, cache.d, S, cache.S_max, k, _dtype_code(q),
-                            _ptr(out), _ptr(idx), _ptr(workspace), wsb, path, _stream(q))
+    head = (_ptr(q), _ptr(cache.k_slab), _ptr(cache.k_rest), _ptr(cache.v), _ptr(P),
+            B, Hq, cache.Hkv, D, cache.d, S, cache.S_max, k, _dtype_code(q))
+    tail = (_ptr(out), _ptr(idx), _ptr(workspace), wsb, path, _stream(q))
+    if rope_base is None:
+        st = lib.loki_decode_ex(*head, *tail)
+    else:
+        st = lib.loki_decode_rope(*head, S - 1 if q_pos is None else q_pos, float(rope_base),
+                                  *tail)
     _check(st, "loki_decode")
     return out, idx
 
 
 def decode_step(q, k_new, v_new, cache: KVCache, P, k: int, pos: int | None = None, out=None,
-                idx=None, workspace=None, path: int = PATH_AUTO):
+                idx=None, workspace=None, path: int = PATH_AUTO, rope_base: float | None = None):
     """Append k_new/v_new [B, Hkv, D] at `pos` (default: the cache length) and
-    decode over pos + 1 tokens, in one call.  Returns (out, idx)."""
+    decode over pos + 1 tokens, in one call.  With rope_base the new key and
+    the query are both embedded at pos (loki_decode_step_rope).  Returns
+    (out, idx)."""
     torch = _torch()
     lib = load()
     _need(q, "q", cache.dtype)
@@ -221,10 +247,13 @@ def decode_step(q, k_new, v_new, cache: KVCache, P, k: int, pos: int | None = No
     if workspace is None and path != PATH_FUSED:
         workspace = alloc_workspace(B, Hq, D, cache.S_max, kk, q.device)
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib.loki_decode_step(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(P), _ptr(cache.k_slab),
-                              _ptr(cache.k_rest), _ptr(cache.v), B, Hq, cache.Hkv, D, cache.d, at,
-                              cache.S_max, k, _dtype_code(q), _ptr(out), _ptr(idx),
-                              _ptr(workspace), wsb, path, _stream(q))
+    head = (_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(P), _ptr(cache.k_slab), _ptr(cache.k_rest),
+            _ptr(cache.v), B, Hq, cache.Hkv, D, cache.d, at, cache.S_max, k, _dtype_code(q))
+    tail = (_ptr(out), _ptr(idx), _ptr(workspace), wsb, path, _stream(q))
+    if rope_base is None:
+        st = lib.loki_decode_step(*head, *tail)
+    else:
+        st = lib.loki_decode_step_rope(*head, float(rope_base), *tail)
     _check(st, "loki_decode_step")
     cache.length = max(cache.length, at + 1)
     return out, idx
@@ -292,8 +321,10 @@ def attend_indices(q, cache: KVCache, P, idx, S: int | None = None, out=None, wo
     return out
 
 
-def dense_decode(q, cache: KVCache, P, S: int | None = None, out=None, workspace=None):
-    """Dense attention over all S tokens of the same rotated cache."""
+def dense_decode(q, cache: KVCache, P, S: int | None = None, out=None, workspace=None,
+                 rope_base: float | None = None, q_pos: int | None = None):
+    """Dense attention over all S tokens of the same rotated cache (the query
+    embedded at q_pos, default S - 1, when rope_base is given)."""
     torch = _torch()
     lib = load()
     B, Hq, D = q.shape
@@ -302,10 +333,14 @@ def dense_decode(q, cache: KVCache, P, S: int | None = None, out=None, workspace
         out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
     if workspace is None:
         workspace = alloc_workspace(B, Hq, D, cache.S_max, 1, q.device)
-    st = lib.loki_dense_decode(_ptr(q), _ptr(cache.k_slab), _ptr(cache.k_rest), _ptr(cache.v),
-                               _ptr(P), B, Hq, cache.Hkv, D, cache.d, S, cache.S_max,
-                               _dtype_code(q), _ptr(out), _ptr(workspace), workspace.numel(),
-                               _stream(q))
+    head = (_ptr(q), _ptr(cache.k_slab), _ptr(cache.k_rest), _ptr(cache.v), _ptr(P), B, Hq,
+            cache.Hkv, D, cache.d, S, cache.S_max, _dtype_code(q))
+    tail = (_ptr(out), _ptr(workspace), workspace.numel(), _stream(q))
+    if rope_base is None:
+        st = lib.loki_dense_decode(*head, *tail)
+    else:
+        st = lib.loki_dense_decode_rope(*head, S - 1 if q_pos is None else q_pos,
+                                        float(rope_base), *tail)
     _check(st, "loki_dense_decode")
     return out
 
@@ -332,7 +367,8 @@ class DecodePlan:
     place between calls).  The stream is the current stream at creation."""
 
     def __init__(self, q, cache: KVCache, P, k: int, S: int | None = None, out=None, idx=None,
-                 workspace=None, path: int = PATH_AUTO):
+                 workspace=None, path: int = PATH_AUTO, rope_base: float | None = None,
+                 q_pos: int | None = None):
         torch = _torch()
         _need(q, "q", cache.dtype)
         _need(P, "P", torch.float32)
@@ -345,10 +381,15 @@ class DecodePlan:
             workspace = alloc_workspace(B, Hq, D, cache.S_max, kk, q.device)
         self._keep = (q, cache, P, workspace)
         wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
-        self._fn = load().loki_decode_ex
-        self._args = (_ptr(q), _ptr(cache.k_slab), _ptr(cache.k_rest), _ptr(cache.v), _ptr(P),
-                      B, Hq, cache.Hkv, D, cache.d, S, cache.S_max, k, _dtype_code(q),
-                      _ptr(self.out), _ptr(self.idx), _ptr(workspace), wsb, path, _stream(q))
+        head = (_ptr(q), _ptr(cache.k_slab), _ptr(cache.k_rest), _ptr(cache.v), _ptr(P),
+                B, Hq, cache.Hkv, D, cache.d, S, cache.S_max, k, _dtype_code(q))
+        tail = (_ptr(self.out), _ptr(self.idx), _ptr(workspace), wsb, path, _stream(q))
+        if rope_base is None:
+            self._fn = load().loki_decode_ex
+            self._args = head + tail
+        else:
+            self._fn = load().loki_decode_rope
+            self._args = head + (S - 1 if q_pos is None else q_pos, float(rope_base)) + tail
 
     def __call__(self):
         st = self._fn(*self._args)
@@ -360,16 +401,20 @@ class DecodePlan:
 class AppendPlan:
     """An append call marshalled once (fixed source buffers and position)."""
 
-    def __init__(self, cache: KVCache, k_new, v_new, P, pos: int):
+    def __init__(self, cache: KVCache, k_new, v_new, P, pos: int, rope_base: float | None = None):
         _need(k_new, "k_new", cache.dtype)
         _need(v_new, "v_new", cache.dtype)
         _need(P, "P", _torch().float32)
         B, Hkv, T, D = k_new.shape
         self._keep = (cache, k_new, v_new, P)
-        self._fn = load().loki_kv_append
-        self._args = (_ptr(k_new), _ptr(v_new), _ptr(P), _ptr(cache.k_slab), _ptr(cache.k_rest),
-                      _ptr(cache.v), B, Hkv, D, cache.d, cache.S_max, pos, T,
-                      _dtype_code(k_new), _stream(k_new))
+        args = (_ptr(k_new), _ptr(v_new), _ptr(P), _ptr(cache.k_slab), _ptr(cache.k_rest),
+                _ptr(cache.v), B, Hkv, D, cache.d, cache.S_max, pos, T, _dtype_code(k_new))
+        if rope_base is None:
+            self._fn = load().loki_kv_append
+            self._args = args + (_stream(k_new),)
+        else:
+            self._fn = load().loki_kv_append_rope
+            self._args = args + (float(rope_base), _stream(k_new))
 
     def __call__(self):
         st = self._fn(*self._args)
@@ -380,7 +425,8 @@ class AppendPlan:
 class DensePlan:
     """A dense-baseline call marshalled once."""
 
-    def __init__(self, q, cache: KVCache, P, S: int | None = None, out=None, workspace=None):
+    def __init__(self, q, cache: KVCache, P, S: int | None = None, out=None, workspace=None,
+                 rope_base: float | None = None, q_pos: int | None = None):
         torch = _torch()
         _need(q, "q", cache.dtype)
         _need(P, "P", torch.float32)
@@ -390,10 +436,16 @@ class DensePlan:
         if workspace is None:
             workspace = alloc_workspace(B, Hq, D, cache.S_max, 1, q.device)
         self._keep = (q, cache, P, workspace)
-        self._fn = load().loki_dense_decode
-        self._args = (_ptr(q), _ptr(cache.k_slab), _ptr(cache.k_rest), _ptr(cache.v), _ptr(P),
-                      B, Hq, cache.Hkv, D, cache.d, S, cache.S_max, _dtype_code(q), _ptr(self.out),
-                      _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(q))
+        head = (_ptr(q), _ptr(cache.k_slab), _ptr(cache.k_rest), _ptr(cache.v), _ptr(P),
+                B, Hq, cache.Hkv, D, cache.d, S, cache.S_max, _dtype_code(q))
+        tail = (_ptr(self.out), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                _stream(q))
+        if rope_base is None:
+            self._fn = load().loki_dense_decode
+            self._args = head + tail
+        else:
+            self._fn = load().loki_dense_decode_rope
+            self._args = head + (S - 1 if q_pos is None else q_pos, float(rope_base)) + tail
 
     def __call__(self):
         st = self._fn(*self._args)
@@ -407,7 +459,7 @@ class StepPlan:
     marshalled once."""
 
     def __init__(self, q, k_new, v_new, cache: KVCache, P, k: int, pos: int, out=None, idx=None,
-                 workspace=None, path: int = PATH_AUTO):
+                 workspace=None, path: int = PATH_AUTO, rope_base: float | None = None):
         torch = _torch()
         _need(q, "q", cache.dtype)
         _need(k_new, "k_new", cache.dtype)
@@ -421,11 +473,16 @@ class StepPlan:
             workspace = alloc_workspace(B, Hq, D, cache.S_max, kk, q.device)
         wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
         self._keep = (q, k_new, v_new, cache, P, workspace)
-        self._fn = load().loki_decode_step
-        self._args = (_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(P), _ptr(cache.k_slab),
-                      _ptr(cache.k_rest), _ptr(cache.v), B, Hq, cache.Hkv, D, cache.d, pos,
-                      cache.S_max, k, _dtype_code(q), _ptr(self.out), _ptr(self.idx),
-                      _ptr(workspace), wsb, path, _stream(q))
+        head = (_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(P), _ptr(cache.k_slab),
+                _ptr(cache.k_rest), _ptr(cache.v), B, Hq, cache.Hkv, D, cache.d, pos,
+                cache.S_max, k, _dtype_code(q))
+        tail = (_ptr(self.out), _ptr(self.idx), _ptr(workspace), wsb, path, _stream(q))
+        if rope_base is None:
+            self._fn = load().loki_decode_step
+            self._args = head + tail
+        else:
+            self._fn = load().loki_decode_step_rope
+            self._args = head + (float(rope_base),) + tail
 
     def __call__(self):
         st = self._fn(*self._args)

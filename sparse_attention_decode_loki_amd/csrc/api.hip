@@ -117,6 +117,8 @@ int check_cache_ptrs(const void* k_slab, const void* k_rest, const void* v, cons
 
 int status_of(hipError_t e) { return e == hipSuccess ? LOKI_OK : LOKI_EDEVICE; }
 
+bool rope_ok(double base) { return std::isfinite(base) && base > 0.0; }
+
 DecodeArgs make_args(const void* q, const void* k_slab, const void* k_rest, const void* v,
                      const float* P, int B, int Hq, int Hkv, int D, int d, int S, int S_max,
                      int dtype, float* out, int32_t* idx, void* stream) {
@@ -188,9 +190,13 @@ const char* loki_status_string(int status) {
 
 int loki_abi_version(void) { return kAbiVersion; }
 
-int loki_kv_append(const void* k_new, const void* v_new, const float* P, void* k_slab,
-                   void* k_rest, void* v, int32_t B, int32_t Hkv, int32_t D, int32_t d,
-                   int32_t S_max, int32_t pos, int32_t T, int32_t dtype, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int append_impl(const void* k_new, const void* v_new, const float* P, void* k_slab, void* k_rest,
+                void* v, int32_t B, int32_t Hkv, int32_t D, int32_t d, int32_t S_max, int32_t pos,
+                int32_t T, int32_t dtype, double rope_base, void* stream) {
   if (dtype != LOKI_F32 && dtype != LOKI_BF16) return LOKI_EINVAL;
   if (B < 0 || Hkv < 1 || D < 1 || d < 1 || d > D || S_max < 1 || pos < 0 || T < 0)
     return LOKI_EINVAL;
@@ -204,7 +210,27 @@ int loki_kv_append(const void* k_new, const void* v_new, const float* P, void* k
   if (Hkv > 65535 || static_cast<int64_t>(B) * T > (1LL << 30)) return LOKI_EUNSUPPORTED;
   return status_of(loki::launch_append(k_new, v_new, P, k_slab, d < D ? k_rest : nullptr, v, B,
                                        Hkv, D, d, S_max, pos, T, dtype,
-                                       static_cast<hipStream_t>(stream)));
+                                       static_cast<hipStream_t>(stream), rope_base));
+}
+
+}  // namespace
+
+extern "C" {
+
+int loki_kv_append(const void* k_new, const void* v_new, const float* P, void* k_slab,
+                   void* k_rest, void* v, int32_t B, int32_t Hkv, int32_t D, int32_t d,
+                   int32_t S_max, int32_t pos, int32_t T, int32_t dtype, void* stream) {
+  return append_impl(k_new, v_new, P, k_slab, k_rest, v, B, Hkv, D, d, S_max, pos, T, dtype, 0.0,
+                     stream);
+}
+
+int loki_kv_append_rope(const void* k_new, const void* v_new, const float* P, void* k_slab,
+                        void* k_rest, void* v, int32_t B, int32_t Hkv, int32_t D, int32_t d,
+                        int32_t S_max, int32_t pos, int32_t T, int32_t dtype, double rope_base,
+                        void* stream) {
+  if (!rope_ok(rope_base)) return LOKI_EINVAL;
+  return append_impl(k_new, v_new, P, k_slab, k_rest, v, B, Hkv, D, d, S_max, pos, T, dtype,
+                     rope_base, stream);
 }
 
 size_t loki_decode_workspace_size(int32_t B, int32_t Hq, int32_t D, int32_t S_max, int32_t k_max) {
@@ -225,10 +251,14 @@ int loki_decode_path(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t d, i
   return auto_path(B, Hq, Hkv, D, d, S, kk, dtype);
 }
 
-int loki_decode_ex(const void* q, const void* k_slab, const void* k_rest, const void* v,
-                   const float* P, int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t d,
-                   int32_t S, int32_t S_max, int32_t k, int32_t dtype, float* out, int32_t* idx,
-                   void* workspace, size_t ws_bytes, int32_t path, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int decode_impl(const void* q, const void* k_slab, const void* k_rest, const void* v,
+                const float* P, int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t d,
+                int32_t S, int32_t S_max, int32_t k, int32_t dtype, float* out, int32_t* idx,
+                void* workspace, size_t ws_bytes, int32_t path, loki::Rope rope, void* stream) {
   int st = check_shape(B, Hq, Hkv, D, d, S, S_max, dtype);
   if (st != LOKI_OK) return st;
   if (k < 1) return LOKI_EINVAL;
@@ -244,6 +274,7 @@ int loki_decode_ex(const void* q, const void* k_slab, const void* k_rest, const 
   if (!aligned16(out) || (reinterpret_cast<uintptr_t>(idx) & 3u)) return LOKI_EINVAL;
   DecodeArgs a = make_args(q, k_slab, k_rest, v, P, B, Hq, Hkv, D, d, S, S_max, dtype, out, idx,
                            stream);
+  a.rope = rope;
   if (path == LOKI_PATH_FUSED) {
     if (!fused_fits(D, S, kk)) return LOKI_EUNSUPPORTED;
     return status_of(loki::launch_fused(a, kk));
@@ -266,11 +297,10 @@ int loki_decode_ex(const void* q, const void* k_slab, const void* k_rest, const 
   return status_of(e);
 }
 
-int loki_decode_step(const void* q, const void* k_new, const void* v_new, const float* P,
-                     void* k_slab, void* k_rest, void* v, int32_t B, int32_t Hq, int32_t Hkv,
-                     int32_t D, int32_t d, int32_t pos, int32_t S_max, int32_t k, int32_t dtype,
-                     float* out, int32_t* idx, void* workspace, size_t ws_bytes, int32_t path,
-                     void* stream) {
+int step_impl(const void* q, const void* k_new, const void* v_new, const float* P, void* k_slab,
+              void* k_rest, void* v, int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t d,
+              int32_t pos, int32_t S_max, int32_t k, int32_t dtype, float* out, int32_t* idx,
+              void* workspace, size_t ws_bytes, int32_t path, double rope_base, void* stream) {
   if (pos < 0) return LOKI_EINVAL;
   const int S = pos + 1;
   int st = check_shape(B, Hq, Hkv, D, d, S, S_max, dtype);
@@ -288,6 +318,10 @@ int loki_decode_step(const void* q, const void* k_new, const void* v_new, const 
   if (!aligned16(out) || (reinterpret_cast<uintptr_t>(idx) & 3u)) return LOKI_EINVAL;
   DecodeArgs a = make_args(q, k_slab, k_rest, v, P, B, Hq, Hkv, D, d, S, S_max, dtype, out, idx,
                            stream);
+  loki::Rope rope;  // the query and the new key sit at position pos
+  rope.base = rope_base;
+  rope.pos = pos;
+  a.rope = rope;
   if (path == LOKI_PATH_FUSED) {
     if (!fused_fits(D, S, kk)) return LOKI_EUNSUPPORTED;
     return status_of(loki::launch_fused_step(a, k_new, v_new, pos, kk));
@@ -295,10 +329,80 @@ int loki_decode_step(const void* q, const void* k_new, const void* v_new, const 
   const Layout L = split_layout(B, Hq, Hkv, D, S, S_max, kk, uni);
   if (!workspace || ws_bytes < L.total || !aligned16(workspace)) return LOKI_EWORKSPACE;
   hipError_t e = loki::launch_append(k_new, v_new, P, k_slab, d < D ? k_rest : nullptr, v, B, Hkv,
-                                     D, d, S_max, pos, 1, dtype, a.stream);
+                                     D, d, S_max, pos, 1, dtype, a.stream, rope_base);
   if (e != hipSuccess) return LOKI_EDEVICE;
-  return loki_decode_ex(q, k_slab, k_rest, v, P, B, Hq, Hkv, D, d, S, S_max, k, dtype, out, idx,
-                        workspace, ws_bytes, uni ? LOKI_PATH_UNION : LOKI_PATH_SPLIT, stream);
+  return decode_impl(q, k_slab, k_rest, v, P, B, Hq, Hkv, D, d, S, S_max, k, dtype, out, idx,
+                     workspace, ws_bytes, uni ? LOKI_PATH_UNION : LOKI_PATH_SPLIT, rope, stream);
+}
+
+int dense_impl(const void* q, const void* k_slab, const void* k_rest, const void* v,
+               const float* P, int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t d, int32_t S,
+               int32_t S_max, int32_t dtype, float* out, void* workspace, size_t ws_bytes,
+               loki::Rope rope, void* stream) {
+  int st = check_shape(B, Hq, Hkv, D, d, S, S_max, dtype);
+  if (st != LOKI_OK) return st;
+  if (B == 0) return LOKI_OK;
+  if (!q || !out) return LOKI_EINVAL;
+  st = check_cache_ptrs(k_slab, k_rest, v, P, D, d);
+  if (st != LOKI_OK) return st;
+  if (!aligned16(out)) return LOKI_EINVAL;
+  const int nsplit = dense_nsplit(B, Hq, Hkv, S);
+  const Layout L = layout(B, Hq, D, S_max, nsplit);
+  if (!workspace || ws_bytes < L.total || !aligned16(workspace)) return LOKI_EWORKSPACE;
+  DecodeArgs a = make_args(q, k_slab, k_rest, v, P, B, Hq, Hkv, D, d, S, S_max, dtype, out,
+                           nullptr, stream);
+  a.rope = rope;
+  char* ws = static_cast<char*>(workspace);
+  float* qrot = reinterpret_cast<float*>(ws + L.qrot);
+  float* part = reinterpret_cast<float*>(ws + L.part);
+  hipError_t e = loki::launch_rotate(a, qrot);
+  if (e == hipSuccess)
+    e = loki::launch_attend(a, qrot, nullptr, nullptr, S, part, nsplit, false);
+  return status_of(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+int loki_decode_ex(const void* q, const void* k_slab, const void* k_rest, const void* v,
+                   const float* P, int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t d,
+                   int32_t S, int32_t S_max, int32_t k, int32_t dtype, float* out, int32_t* idx,
+                   void* workspace, size_t ws_bytes, int32_t path, void* stream) {
+  return decode_impl(q, k_slab, k_rest, v, P, B, Hq, Hkv, D, d, S, S_max, k, dtype, out, idx,
+                     workspace, ws_bytes, path, loki::Rope(), stream);
+}
+
+int loki_decode_rope(const void* q, const void* k_slab, const void* k_rest, const void* v,
+                     const float* P, int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t d,
+                     int32_t S, int32_t S_max, int32_t k, int32_t dtype, int32_t q_pos,
+                     double rope_base, float* out, int32_t* idx, void* workspace,
+                     size_t ws_bytes, int32_t path, void* stream) {
+  if (!rope_ok(rope_base) || q_pos < 0) return LOKI_EINVAL;
+  loki::Rope rope;
+  rope.base = rope_base;
+  rope.pos = q_pos;
+  return decode_impl(q, k_slab, k_rest, v, P, B, Hq, Hkv, D, d, S, S_max, k, dtype, out, idx,
+                     workspace, ws_bytes, path, rope, stream);
+}
+
+int loki_decode_step(const void* q, const void* k_new, const void* v_new, const float* P,
+                     void* k_slab, void* k_rest, void* v, int32_t B, int32_t Hq, int32_t Hkv,
+                     int32_t D, int32_t d, int32_t pos, int32_t S_max, int32_t k, int32_t dtype,
+                     float* out, int32_t* idx, void* workspace, size_t ws_bytes, int32_t path,
+                     void* stream) {
+  return step_impl(q, k_new, v_new, P, k_slab, k_rest, v, B, Hq, Hkv, D, d, pos, S_max, k, dtype,
+                   out, idx, workspace, ws_bytes, path, 0.0, stream);
+}
+
+int loki_decode_step_rope(const void* q, const void* k_new, const void* v_new, const float* P,
+                          void* k_slab, void* k_rest, void* v, int32_t B, int32_t Hq, int32_t Hkv,
+                          int32_t D, int32_t d, int32_t pos, int32_t S_max, int32_t k,
+                          int32_t dtype, double rope_base, float* out, int32_t* idx,
+                          void* workspace, size_t ws_bytes, int32_t path, void* stream) {
+  if (!rope_ok(rope_base)) return LOKI_EINVAL;
+  return step_impl(q, k_new, v_new, P, k_slab, k_rest, v, B, Hq, Hkv, D, d, pos, S_max, k, dtype,
+                   out, idx, workspace, ws_bytes, path, rope_base, stream);
 }
 
 int loki_decode(const void* q, const void* k_slab, const void* k_rest, const void* v,
@@ -367,25 +471,21 @@ int loki_dense_decode(const void* q, const void* k_slab, const void* k_rest, con
                       const float* P, int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t d,
                       int32_t S, int32_t S_max, int32_t dtype, float* out, void* workspace,
                       size_t ws_bytes, void* stream) {
-  int st = check_shape(B, Hq, Hkv, D, d, S, S_max, dtype);
-  if (st != LOKI_OK) return st;
-  if (B == 0) return LOKI_OK;
-  if (!q || !out) return LOKI_EINVAL;
-  st = check_cache_ptrs(k_slab, k_rest, v, P, D, d);
-  if (st != LOKI_OK) return st;
-  if (!aligned16(out)) return LOKI_EINVAL;
-  const int nsplit = dense_nsplit(B, Hq, Hkv, S);
-  const Layout L = layout(B, Hq, D, S_max, nsplit);
-  if (!workspace || ws_bytes < L.total || !aligned16(workspace)) return LOKI_EWORKSPACE;
-  DecodeArgs a = make_args(q, k_slab, k_rest, v, P, B, Hq, Hkv, D, d, S, S_max, dtype, out,
-                           nullptr, stream);
-  char* ws = static_cast<char*>(workspace);
-  float* qrot = reinterpret_cast<float*>(ws + L.qrot);
-  float* part = reinterpret_cast<float*>(ws + L.part);
-  hipError_t e = loki::launch_rotate(a, qrot);
-  if (e == hipSuccess)
-    e = loki::launch_attend(a, qrot, nullptr, nullptr, S, part, nsplit, false);
-  return status_of(e);
+  return dense_impl(q, k_slab, k_rest, v, P, B, Hq, Hkv, D, d, S, S_max, dtype, out, workspace,
+                    ws_bytes, loki::Rope(), stream);
+}
+
+int loki_dense_decode_rope(const void* q, const void* k_slab, const void* k_rest, const void* v,
+                           const float* P, int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                           int32_t d, int32_t S, int32_t S_max, int32_t dtype, int32_t q_pos,
+                           double rope_base, float* out, void* workspace, size_t ws_bytes,
+                           void* stream) {
+  if (!rope_ok(rope_base) || q_pos < 0) return LOKI_EINVAL;
+  loki::Rope rope;
+  rope.base = rope_base;
+  rope.pos = q_pos;
+  return dense_impl(q, k_slab, k_rest, v, P, B, Hq, Hkv, D, d, S, S_max, dtype, out, workspace,
+                    ws_bytes, rope, stream);
 }
 
 int loki_stream_read(const void* buf, size_t bytes, float* sink, int32_t workgroups,

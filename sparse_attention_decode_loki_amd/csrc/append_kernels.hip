@@ -7,7 +7,8 @@
 // The rotation is accumulated in float64 (128 FMAs per output element) and
 // rounded once to the cache type, so the stored key is the correctly rounded
 // value of x . P; append is off the decode path and float64 FMA throughput is
-// ample for it.
+// ample for it.  The RoPE variant first embeds each key at its slot's
+// position, also in float64.
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -25,10 +26,11 @@ template <class E, int D>
 __global__ void __launch_bounds__(kBlock) append_kernel(
     const typename E::T* __restrict__ k_new, const typename E::T* __restrict__ v_new,
     const float* __restrict__ P, typename E::T* __restrict__ slab, typename E::T* __restrict__ rest,
-    typename E::T* __restrict__ val, int B, int Hkv, int d, int S_max, int pos, int T) {
+    typename E::T* __restrict__ val, int B, int Hkv, int d, int S_max, int pos, int T,
+    double rope_base) {
   constexpr int NP = kBlock / D;  // partial sums per output
   constexpr int R = D / NP;       // rows of P per partial
-  __shared__ float ks[kAppendTok][D];
+  __shared__ double ks[kAppendTok][D];  // the chunk's keys (embedded when rope_base > 0)
   __shared__ double red[NP][kAppendTok][D];
   const int g = blockIdx.y;
   const int col = threadIdx.x % D;
@@ -45,10 +47,11 @@ __global__ void __launch_bounds__(kBlock) append_kernel(
     const int nt = min(kAppendTok, ntok - n0);
     for (int i = threadIdx.x; i < kAppendTok * D; i += kBlock) {
       const int tt = i / D, c = i % D;
-      float x = 0.f;
+      double x = 0.0;
       if (tt < nt) {
         const int n = n0 + tt, b = n / T, t = n % T;
-        x = ld_elem<E>(k_new, ((static_cast<int64_t>(b) * Hkv + g) * T + t) * D + c);
+        x = rope_elem<E>(k_new + ((static_cast<int64_t>(b) * Hkv + g) * T + t) * D, c, D,
+                         rope_base, pos + t);
       }
       ks[tt][c] = x;
     }
@@ -61,7 +64,7 @@ __global__ void __launch_bounds__(kBlock) append_kernel(
       const double pv = static_cast<double>(pc[r]);
 #pragma unroll
       for (int tt = 0; tt < kAppendTok; ++tt)
-        acc[tt] = fma(static_cast<double>(ks[tt][part * R + r]), pv, acc[tt]);
+        acc[tt] = fma(ks[tt][part * R + r], pv, acc[tt]);
     }
 #pragma unroll
     for (int tt = 0; tt < kAppendTok; ++tt) red[part][tt][col] = acc[tt];
@@ -87,7 +90,7 @@ namespace {
 template <class E, int D>
 hipError_t append_t(const void* k_new, const void* v_new, const float* P, void* k_slab,
                     void* k_rest, void* v, int B, int Hkv, int d, int S_max, int pos, int T,
-                    hipStream_t stream) {
+                    hipStream_t stream, double rope_base) {
   using T_ = typename E::T;
   const int64_t chunks = (static_cast<int64_t>(B) * T + kAppendTok - 1) / kAppendTok;
   // enough workgroups to fill the chip, each reusing its basis column over
@@ -98,19 +101,23 @@ hipError_t append_t(const void* k_new, const void* v_new, const float* P, void* 
   hipLaunchKernelGGL((append_kernel<E, D>), grid, dim3(kBlock), 0, stream,
                      static_cast<const T_*>(k_new), static_cast<const T_*>(v_new), P,
                      static_cast<T_*>(k_slab), static_cast<T_*>(k_rest), static_cast<T_*>(v), B,
-                     Hkv, d, S_max, pos, T);
+                     Hkv, d, S_max, pos, T, rope_base);
   return hipGetLastError();
 }
 }  // namespace
 
 hipError_t launch_append(const void* k_new, const void* v_new, const float* P, void* k_slab,
                          void* k_rest, void* v, int B, int Hkv, int D, int d, int S_max, int pos,
-                         int T, int dtype, hipStream_t stream) {
+                         int T, int dtype, hipStream_t stream, double rope_base) {
   if (dtype == kF32)
-    return D == 64 ? append_t<F32, 64>(k_new, v_new, P, k_slab, k_rest, v, B, Hkv, d, S_max, pos, T, stream)
-                   : append_t<F32, 128>(k_new, v_new, P, k_slab, k_rest, v, B, Hkv, d, S_max, pos, T, stream);
-  return D == 64 ? append_t<BF16, 64>(k_new, v_new, P, k_slab, k_rest, v, B, Hkv, d, S_max, pos, T, stream)
-                 : append_t<BF16, 128>(k_new, v_new, P, k_slab, k_rest, v, B, Hkv, d, S_max, pos, T, stream);
+    return D == 64 ? append_t<F32, 64>(k_new, v_new, P, k_slab, k_rest, v, B, Hkv, d, S_max, pos,
+                                       T, stream, rope_base)
+                   : append_t<F32, 128>(k_new, v_new, P, k_slab, k_rest, v, B, Hkv, d, S_max, pos,
+                                        T, stream, rope_base);
+  return D == 64 ? append_t<BF16, 64>(k_new, v_new, P, k_slab, k_rest, v, B, Hkv, d, S_max, pos, T,
+                                      stream, rope_base)
+                 : append_t<BF16, 128>(k_new, v_new, P, k_slab, k_rest, v, B, Hkv, d, S_max, pos,
+                                       T, stream, rope_base);
 }
 
 }  // namespace loki

@@ -46,7 +46,7 @@ template <class E, int D>
 __global__ void __launch_bounds__(kBlock) rotate_kernel(const typename E::T* __restrict__ q,
                                                         const float* __restrict__ P,
                                                         float* __restrict__ qrot, int B, int Hq,
-                                                        int Hkv) {
+                                                        int Hkv, Rope rope) {
   constexpr int CQ = D / 4;        // column quads
   constexpr int NRB = kBlock / CQ; // row blocks
   constexpr int RB = D / NRB;      // rows per block
@@ -68,7 +68,8 @@ __global__ void __launch_bounds__(kBlock) rotate_kernel(const typename E::T* __r
   for (int e = threadIdx.x; e < nq * D; e += kBlock) {
     const int r = e / D, m = e % D;
     const int n = n0 + r, b = n / G, h = g * G + n % G;
-    qsh[r][m] = ld_elem<E>(q, (static_cast<int64_t>(b) * Hq + h) * D + m);
+    qsh[r][m] = static_cast<float>(
+        rope_elem<E>(q + (static_cast<int64_t>(b) * Hq + h) * D, m, D, rope.base, rope.pos));
   }
   __syncthreads();
   for (int r = 0; r < nq; ++r) {
@@ -123,7 +124,7 @@ __global__ void __launch_bounds__(kBlock) score_kernel(const typename E::T* __re
                                                        float* __restrict__ qrot,
                                                        float* __restrict__ scores, int Hq, int Hkv,
                                                        int d, int S, int S_max, int nhb,
-                                                       int chunk) {
+                                                       int chunk, Rope rope) {
   constexpr int VEC = E::VEC;
   constexpr int CQ = D / 4;         // column quads of P
   constexpr int NRB = kBlock / CQ;  // row blocks of P
@@ -147,7 +148,9 @@ __global__ void __launch_bounds__(kBlock) score_kernel(const typename E::T* __re
 
   for (int e = threadIdx.x; e < NH * D; e += kBlock) {
     const int h = e / D, m = e % D;
-    qin[h][m] = h < nh ? ld_elem<E>(q, (static_cast<int64_t>(b) * Hq + h0 + h) * D + m) : 0.f;
+    qin[h][m] = h < nh ? static_cast<float>(rope_elem<E>(
+                             q + (static_cast<int64_t>(b) * Hq + h0 + h) * D, m, D, rope.base, rope.pos))
+                       : 0.f;
   }
   __syncthreads();
   const int ncols = blockIdx.y == 0 ? D : d;
@@ -972,7 +975,7 @@ hipError_t rotate_t(const DecodeArgs& a, float* qrot) {
   const int G = a.Hq / a.Hkv;
   dim3 grid((a.B * G + kRotQ - 1) / kRotQ, a.Hkv);
   hipLaunchKernelGGL((rotate_kernel<E, D>), grid, dim3(kBlock), 0, a.stream, cptr<E>(a.q), a.P,
-                     qrot, a.B, a.Hq, a.Hkv);
+                     qrot, a.B, a.Hq, a.Hkv, a.rope);
   return hipGetLastError();
 }
 
@@ -987,13 +990,13 @@ hipError_t score_t(const DecodeArgs& a, float* qrot, float* scores) {
   const auto* qq = cptr<E>(a.q);
   if (nh == 4)
     hipLaunchKernelGGL((score_kernel<E, D, LPS, 4>), grid, dim3(kBlock), 0, a.stream, sl, qq, a.P,
-                       qrot, scores, a.Hq, a.Hkv, a.d, a.S, a.S_max, nhb, chunk);
+                       qrot, scores, a.Hq, a.Hkv, a.d, a.S, a.S_max, nhb, chunk, a.rope);
   else if (nh == 2)
     hipLaunchKernelGGL((score_kernel<E, D, LPS, 2>), grid, dim3(kBlock), 0, a.stream, sl, qq, a.P,
-                       qrot, scores, a.Hq, a.Hkv, a.d, a.S, a.S_max, nhb, chunk);
+                       qrot, scores, a.Hq, a.Hkv, a.d, a.S, a.S_max, nhb, chunk, a.rope);
   else
     hipLaunchKernelGGL((score_kernel<E, D, LPS, 1>), grid, dim3(kBlock), 0, a.stream, sl, qq, a.P,
-                       qrot, scores, a.Hq, a.Hkv, a.d, a.S, a.S_max, nhb, chunk);
+                       qrot, scores, a.Hq, a.Hkv, a.d, a.S, a.S_max, nhb, chunk, a.rope);
   return hipGetLastError();
 }
 

@@ -116,6 +116,26 @@ __device__ __forceinline__ float ld_elem<BF16>(const uint16_t* p, int64_t i) {
   return __uint_as_float(static_cast<uint32_t>(p[i]) << 16);
 }
 
+// Element m of the D-vector x (storage type) after the rotary position
+// embedding at position pos, in float64: dims i and i + D/2 turn together by
+// the angle pos * base^(-2i/D) (the embedding of the Llama-family models the
+// pages evaluate; they name RoPE without its form).  base == 0 means no
+// embedding: the element itself.
+template <class E>
+__device__ __forceinline__ double rope_elem(const typename E::T* x, int m, int D, double base,
+                                            int pos) {
+  const double a = static_cast<double>(ld_elem<E>(x, m));
+  if (base == 0.0) return a;
+  const int h = D >> 1;
+  const bool first = m < h;
+  const int i = first ? m : m - h;
+  const double b = static_cast<double>(ld_elem<E>(x, first ? m + h : m - h));  // partner
+  double sn, cs;
+  sincos(static_cast<double>(pos) * pow(base, -2.0 * i / D), &sn, &cs);
+  // first half: x_i cos - x_{i+h} sin; second half: x_{i+h} cos + x_i sin
+  return first ? a * cs - b * sn : a * cs + b * sn;
+}
+
 // Data-parallel-primitive (DPP) lane moves.  dpp<CTRL, ROW_MASK, BANK_MASK>
 // returns, per lane, the value of the lane selected by CTRL within its row of
 // 16 lanes; lanes whose source is out of range, or that the masks disable,

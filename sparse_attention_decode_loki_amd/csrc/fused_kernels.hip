@@ -31,6 +31,7 @@ struct FusedArgs {
   int* idx;
   int B, Hq, Hkv, d, S, S_max, kk, pos;
   float scale_log2;
+  Rope rope;  // the query's embedding; STEP embeds the new key at pos
 };
 
 // Eight waves per row: the slab stream and the gather each keep twice the
@@ -67,7 +68,8 @@ __global__ void __launch_bounds__(kFusedBlock) fused_kernel(FusedArgs a) {
   };
   __shared__ Scratch sc;
   __shared__ unsigned hist0[SMALL ? kSelBins : 1];  // first-digit histogram of the scores
-  __shared__ float rin[STEP ? 2 : 1][D];  // q (and the new key) as float
+  __shared__ float rin[D];                     // q as float (embedded)
+  __shared__ double kin[STEP ? D : 1];         // STEP: the new key, float64 (embedded)
   __shared__ __align__(16) T kslot[STEP ? D : VEC];  // new key row [slab | rest], stored values
   __shared__ __align__(16) T vslot[STEP ? D : VEC];  // new value row
   extern __shared__ float dyn[];
@@ -93,10 +95,11 @@ __global__ void __launch_bounds__(kFusedBlock) fused_kernel(FusedArgs a) {
   //    (cq, rb) adds rows [rb*RB, rb*RB + RB) for columns 4*cq .. 4*cq + 3,
   //    read as 16-byte chunks; the NRB partials are added through LDS.
   if (threadIdx.x < D) {
-    rin[0][threadIdx.x] = ld_elem<E>(static_cast<const T*>(a.q), row * D + threadIdx.x);
+    rin[threadIdx.x] = static_cast<float>(rope_elem<E>(static_cast<const T*>(a.q) + row * D,
+                                                       threadIdx.x, D, a.rope.base, a.rope.pos));
     if (STEP)
-      rin[STEP ? 1 : 0][threadIdx.x] =
-          ld_elem<E>(static_cast<const T*>(a.k_new), bgo * D + threadIdx.x);
+      kin[threadIdx.x] = rope_elem<E>(static_cast<const T*>(a.k_new) + bgo * D, threadIdx.x, D,
+                                      a.rope.base, a.pos);
   }
   __syncthreads();
   if (threadIdx.x < kBlock) {
@@ -108,13 +111,13 @@ __global__ void __launch_bounds__(kFusedBlock) fused_kernel(FusedArgs a) {
     for (int rr = 0; rr < RB; ++rr) {
       const int m = rb * RB + rr;
       const float4 p = *reinterpret_cast<const float4*>(Pg + m * D + 4 * cq);
-      const float x = rin[0][m];
+      const float x = rin[m];
       acc.x = fmaf(x, p.x, acc.x);
       acc.y = fmaf(x, p.y, acc.y);
       acc.z = fmaf(x, p.z, acc.z);
       acc.w = fmaf(x, p.w, acc.w);
       if (STEP) {
-        const double xk = static_cast<double>(rin[STEP ? 1 : 0][m]);
+        const double xk = kin[STEP ? m : 0];
         kacc[0] = fma(xk, static_cast<double>(p.x), kacc[0]);
         kacc[1] = fma(xk, static_cast<double>(p.y), kacc[1]);
         kacc[2] = fma(xk, static_cast<double>(p.z), kacc[2]);
@@ -292,6 +295,7 @@ FusedArgs fused_args(const DecodeArgs& a, int kk) {
   fa.kk = kk;
   fa.pos = -1;
   fa.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(a.D)));
+  fa.rope = a.rope;
   return fa;
 }
 

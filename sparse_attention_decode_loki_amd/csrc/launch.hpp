@@ -14,6 +14,13 @@ constexpr int kBF16 = 1;
 constexpr size_t kTopkLdsMax = 136 * 1024;   // scores staged in LDS up to this size
 constexpr size_t kFusedLdsMax = 56 * 1024;   // fused path: q' + scores + kept ids (dynamic LDS)
 
+// Rotary position embedding of the query before its PCA rotation: base 0
+// means none; pos is the query's position.
+struct Rope {
+  double base = 0.0;
+  int pos = 0;
+};
+
 struct DecodeArgs {
   const void* q;
   const void* k_slab;
@@ -25,6 +32,7 @@ struct DecodeArgs {
   float* out;
   int* idx;
   hipStream_t stream;
+  Rope rope;
 };
 
 hipError_t launch_rotate(const DecodeArgs& a, float* qrot);
@@ -48,13 +56,16 @@ hipError_t launch_attend_union(const DecodeArgs& a, const float* qrot, const flo
                                const unsigned* bits, float* part, int nsplit);
 size_t fused_lds_bytes(int D, int S, int kk);
 hipError_t launch_fused(const DecodeArgs& a, int kk);
-// append (k_new, v_new [B, Hkv, D]) at pos and decode over a.S = pos + 1
+// append (k_new, v_new [B, Hkv, D]) at pos and decode over a.S = pos + 1;
+// with a.rope.base > 0 the new key is embedded at pos (the query at
+// a.rope.pos)
 hipError_t launch_fused_step(const DecodeArgs& a, const void* k_new, const void* v_new, int pos,
                              int kk);
 
+// rope_base > 0: new token t is embedded at position pos + t before rotating
 hipError_t launch_append(const void* k_new, const void* v_new, const float* P, void* k_slab,
                          void* k_rest, void* v, int B, int Hkv, int D, int d, int S_max, int pos,
-                         int T, int dtype, hipStream_t stream);
+                         int T, int dtype, hipStream_t stream, double rope_base = 0.0);
 
 // streaming read of bytes (multiple of 16) with nontemporal 16-byte loads;
 // sink receives workgroups * 256 floats

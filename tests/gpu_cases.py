@@ -52,7 +52,10 @@ def basis(w: synth.Workload) -> np.ndarray:
     return P
 
 
-def make_case(w: synth.Workload, S: int | None = None, S_max: int | None = None) -> Case:
+def make_case(w: synth.Workload, S: int | None = None, S_max: int | None = None,
+              rope_base: float | None = None) -> Case:
+    """The oracle's cache of the generator's keys and values; with rope_base
+    each key is embedded at its position before the rotation."""
     S = w.S if S is None else S
     S_max = S if S_max is None else S_max
     P = basis(w)
@@ -64,7 +67,7 @@ def make_case(w: synth.Workload, S: int | None = None, S_max: int | None = None)
     vv = np.full((w.B, w.Hkv, S_max, w.D), poison, st)
     for g in range(w.Hkv):
         s_, r_, v_ = oracle.append(oracle.to_f64(K[:, g], w.dtype), oracle.to_f64(V[:, g], w.dtype),
-                                   P[g].astype(np.float64), w.d, w.dtype)
+                                   P[g].astype(np.float64), w.d, w.dtype, rope_base=rope_base)
         slab[:, g, :S], rest[:, g, :S], vv[:, g, :S] = s_, r_, v_
     return Case(w, S, S_max, P, synth.queries(w), K, V, slab, rest, vv)
 

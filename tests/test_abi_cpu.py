@@ -45,7 +45,7 @@ def test_version_and_status_strings(L):
     lib = L.load()
     with open(os.path.join(ROOT, "include", "loki.h")) as fh:
         header = int(re.search(r"#define LOKI_ABI_VERSION (\d+)", fh.read()).group(1))
-    assert lib.loki_abi_version() == header == 2
+    assert lib.loki_abi_version() == header == 3
     for st in (0, -1, -2, -3, -4, 7):
         assert lib.loki_status_string(st)
     assert L.status_string(-2).startswith("LOKI_EWORKSPACE")
@@ -131,6 +131,42 @@ def test_append_rejects_bad_arguments(L):
     assert ap(D=96) == -4
     assert ap(d=4) == -4
     assert ap(dt=3) == -1
+
+
+@pytest.mark.parametrize("base", [0.0, -10000.0, float("nan"), float("inf")])
+def test_rope_entry_points_reject_bad_base(L, base):
+    lib = L.load()
+    assert lib.loki_kv_append_rope(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 2, 128, 32, 64, 0, 4, 1,
+                                   base, None) == -1
+    assert lib.loki_decode_rope(FAKE, FAKE, FAKE, FAKE, FAKE, 2, 4, 2, 128, 32, 100, 128, 25, 1, 99,
+                                base, FAKE, FAKE, FAKE, 1 << 40, 2, None) == -1
+    assert lib.loki_decode_step_rope(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 4, 2, 128, 32, 99,
+                                     128, 25, 1, base, FAKE, FAKE, FAKE, 1 << 40, 2, None) == -1
+    assert lib.loki_dense_decode_rope(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, 2, 128, 32, 10, 10, 1, 9,
+                                      base, FAKE, FAKE, 1 << 40, None) == -1
+
+
+def test_rope_entry_points_check_like_the_plain_ones(L):
+    lib = L.load()
+    base = 10000.0
+    dec = lambda **kw: lib.loki_decode_rope(
+        FAKE, FAKE, FAKE, FAKE, FAKE, kw.get("B", 2), 4, 2, 128, kw.get("d", 32), 100, 128, 25, 1,
+        kw.get("q_pos", 99), base, FAKE, FAKE, kw.get("ws", FAKE), kw.get("wsb", 1 << 40),
+        kw.get("path", 2), None)
+    assert dec(q_pos=-1) == -1
+    assert dec(d=20) == -4
+    assert dec(ws=None) == -2
+    assert dec(B=0) == 0                 # empty batch: nothing launched
+    assert dec(path=9) == -1
+    assert lib.loki_kv_append_rope(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 2, 128, 32, 64, 62, 4, 1,
+                                   base, None) == -1     # pos + T > S_max
+    assert lib.loki_kv_append_rope(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 2, 128, 32, 64, 0, 0, 1,
+                                   base, None) == 0      # T = 0
+    assert lib.loki_decode_step_rope(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 4, 2, 128, 32,
+                                     128, 128, 25, 1, base, FAKE, FAKE, FAKE, 1 << 40, 2,
+                                     None) == -1         # pos >= S_max
+    assert lib.loki_dense_decode_rope(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, 2, 128, 32, 10, 10, 1, -3,
+                                      base, FAKE, FAKE, 1 << 40, None) == -1
 
 
 def test_topk_and_scores_reject_bad_arguments(L):

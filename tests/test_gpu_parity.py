@@ -4,7 +4,7 @@ oracle on the same seeded inputs.
 Stages are checked one at a time (ranking scores, selection, attention over
 a given index set, append, dense baseline) and end to end (both decode
 paths), at sizes that span several tiles and ragged tails, on edge cases,
-and at the full benchmark shapes on sampled (sequence, head) pairs.
+and at the full benchmark shapes on every (sequence, head) pair.
 """
 
 import numpy as np

@@ -1,0 +1,176 @@
+"""GPU parity of the rotary-position-embedding variant (the _rope entry
+points) against the oracle: keys embedded at their cache positions before the
+PCA rotation, the query at its own position.  Caches are built by the
+oracle's float64 append with the same embedding; nothing from the GPU feeds
+the oracle."""
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_cases import (TOL, all_pairs, basis, check_decode, device_cache, make_case, out_error,
+                       to_dev, to_host, ulp_diff_bf16, ulp_diff_f32)
+
+pytestmark = pytest.mark.gpu
+
+# (workload, S, S_max, rope base)
+CASES = {
+    "rope_mha": (synth.custom("rope_mha", 601, B=2, Hq=4, Hkv=4, S=700), 700, 720, 10000.0),
+    "rope_gqa4": (synth.custom("rope_gqa4", 602, B=2, Hq=8, Hkv=2, S=1000), 1000, 1000, 500000.0),
+    "rope_f32": (synth.custom("rope_f32", 603, B=1, Hq=2, Hkv=2, D=64, d=16, S=300, dtype="f32",
+                              tau=8.0), 300, 310, 10000.0),
+    "rope_long": (synth.custom("rope_long", 604, B=1, Hq=4, Hkv=2, S=5000), 5000, 5000, 10000.0),
+}
+_cache = {}
+
+
+def case(name):
+    if name not in _cache:
+        w, S, S_max, base = CASES[name]
+        _cache[name] = (make_case(w, S, S_max, rope_base=base), base)
+    return _cache[name]
+
+
+def _paths(w):
+    paths = [2]
+    if w.Hq == w.Hkv:
+        paths.append(1)
+    if w.Hq // w.Hkv in (2, 4):
+        paths.append(3)
+    return paths
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_rope_decode_matches_oracle(lib, name):
+    c, base = case(name)
+    cache = device_cache(lib, c)
+    q = to_dev(c.q, c.w.dtype)
+    P = to_dev(c.P, "f32")
+    for q_pos in (c.S - 1, 3 * c.S + 17):  # the usual position, and one past the cache
+        ref_out, ref_idx, ref_s = oracle.decode(c.q, c.slab, c.rest, c.v, c.P, c.k, c.w.dtype,
+                                                S=c.S, rope=(base, q_pos))
+        for path in _paths(c.w):
+            out, idx = lib.decode(q, cache, P, c.k, path=path, rope_base=base, q_pos=q_pos)
+            check_decode(c.w.dtype, c.k, out.cpu().numpy(), idx.cpu().numpy(), ref_out, ref_idx,
+                         ref_s, all_pairs(c.w))
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_rope_paths_select_identically(lib, name):
+    """The embedded query is formed once per path with the same float64
+    arithmetic and rounded once, so every path ranks with the same q'."""
+    c, base = case(name)
+    cache = device_cache(lib, c)
+    q = to_dev(c.q, c.w.dtype)
+    P = to_dev(c.P, "f32")
+    res = [lib.decode(q, cache, P, c.k, path=p, rope_base=base) for p in _paths(c.w)]
+    for out, idx in res[1:]:
+        assert np.array_equal(idx.cpu().numpy(), res[0][1].cpu().numpy())
+        assert np.max(np.abs(out.cpu().numpy() - res[0][0].cpu().numpy())) < 1e-5
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_rope_dense_matches_oracle(lib, name):
+    c, base = case(name)
+    cache = device_cache(lib, c)
+    out = lib.dense_decode(to_dev(c.q, c.w.dtype), cache, to_dev(c.P, "f32"), rope_base=base,
+                           q_pos=c.S + 5).cpu().numpy()
+    ref = oracle.dense_decode(c.q, c.slab, c.rest, c.v, c.P, c.w.dtype, S=c.S, rope=(base, c.S + 5))
+    for b, h in all_pairs(c.w):
+        assert out_error(c.w.dtype, out[b, h], ref[b, h]) <= TOL[c.w.dtype]
+
+
+@pytest.mark.parametrize("wname", ["rope_mha", "rope_f32"])
+@pytest.mark.parametrize("pos,T", [(0, 1), (5, 37), (250, 50), (4000, 3)])
+def test_rope_append_matches_oracle(lib, wname, pos, T):
+    import torch
+    w, _, _, base = CASES[wname]
+    P = basis(w)
+    K, V = synth.raw_cache(w, T)
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    cache = lib.KVCache(w.B, w.Hkv, pos + T + 2, w.D, w.d, tdt)
+    lib.append(cache, to_dev(K, w.dtype), to_dev(V, w.dtype), to_dev(P, "f32"), pos=pos,
+               rope_base=base)
+    torch.cuda.synchronize()
+    slab = to_host(cache.k_slab, w.dtype)[:, :, pos:pos + T]
+    rest = to_host(cache.k_rest, w.dtype)[:, :, pos:pos + T]
+    vv = to_host(cache.v, w.dtype)[:, :, pos:pos + T]
+    for g in range(w.Hkv):
+        rs, rr, rv = oracle.append(oracle.to_f64(K[:, g], w.dtype), oracle.to_f64(V[:, g], w.dtype),
+                                   P[g].astype(np.float64), w.d, w.dtype, rope_base=base, pos=pos)
+        for a, e in ((slab[:, g], rs), (rest[:, g], rr)):
+            ud = ulp_diff_bf16(a, e) if w.dtype == "bf16" else ulp_diff_f32(a, e)
+            assert ud.max() <= 1
+            assert (ud == 0).mean() >= 0.999
+        assert np.array_equal(vv[:, g], rv)
+    # the embedding really was applied: it changes the stored keys
+    plain = oracle.append(oracle.to_f64(K[:, 0], w.dtype), oracle.to_f64(V[:, 0], w.dtype),
+                          P[0].astype(np.float64), w.d, w.dtype)[0]
+    if pos > 0:
+        assert not np.array_equal(slab[:, 0], plain)
+
+
+@pytest.mark.parametrize("path", [1, 2], ids=["fused", "split"])
+def test_rope_decode_step_matches_oracle(lib, path):
+    """Append at pos = S - 1 with the key embedded there, query embedded at
+    the same position, decode over S tokens; three steps in a row."""
+    import torch
+    w, S, S_max, base = CASES["rope_mha"]
+    c = make_case(w, S - 3, S_max, rope_base=base)
+    cache = device_cache(lib, c)
+    P = to_dev(c.P, "f32")
+    full = {nm: getattr(c, nm).copy() for nm in ("slab", "rest", "v")}
+    for step in range(3):
+        pos = S - 3 + step
+        kn, vn = synth.new_tokens(w, 40 + step)
+        for g in range(w.Hkv):
+            s_, r_, v_ = oracle.append(oracle.to_f64(kn[:, g], w.dtype), oracle.to_f64(vn[:, g], w.dtype),
+                                       c.P[g].astype(np.float64), w.d, w.dtype, rope_base=base, pos=pos)
+            full["slab"][:, g, pos], full["rest"][:, g, pos], full["v"][:, g, pos] = s_[:, 0], r_[:, 0], v_[:, 0]
+        q = synth.queries(w, step=40 + step)
+        k = w.k_at(pos + 1)
+        out, idx = lib.decode_step(to_dev(q, w.dtype), to_dev(kn[:, :, 0], w.dtype),
+                                   to_dev(vn[:, :, 0], w.dtype), cache, P, k, path=path,
+                                   rope_base=base)
+        torch.cuda.synchronize()
+        got = to_host(cache.k_slab, w.dtype)[:, :, pos]
+        assert ulp_diff_bf16(got, full["slab"][:, :, pos]).max() <= 1
+        ref_out, ref_idx, ref_s = oracle.decode(q, full["slab"], full["rest"], full["v"], c.P, k,
+                                                w.dtype, S=pos + 1, rope=(base, pos))
+        check_decode(w.dtype, k, out.cpu().numpy(), idx.cpu().numpy(), ref_out, ref_idx, ref_s,
+                     all_pairs(w))
+
+
+def test_rope_pre_and_post_rotary_bases_both_decode(lib):
+    """Pre-rotary: the basis from keys before the embedding; post-rotary: from
+    the same keys embedded at positions 0..n-1.  Either way the cache holds
+    embedded keys and the decode matches the oracle with that basis."""
+    import torch
+    w, S, S_max, base = CASES["rope_gqa4"]
+    Ks = [synth.calib_keys(w, g) for g in range(w.Hkv)]
+    pre = np.stack([lib.calibrate(K.astype(np.float32))[0] for K in Ks])
+    post = np.stack([lib.calibrate(oracle.rope_embed(K, np.arange(K.shape[0]), base)
+                                   .astype(np.float32))[0] for K in Ks])
+    assert not np.allclose(pre, post, atol=1e-3)
+    Kr, Vr = synth.raw_cache(w, S)
+    q = synth.queries(w)
+    for P in (pre, post):
+        st = np.uint16
+        slab = np.empty((w.B, w.Hkv, S, w.d), st)
+        rest = np.empty((w.B, w.Hkv, S, w.D - w.d), st)
+        vv = np.empty((w.B, w.Hkv, S, w.D), st)
+        tdt = torch.bfloat16
+        cache = lib.KVCache(w.B, w.Hkv, S, w.D, w.d, tdt)
+        lib.append(cache, to_dev(Kr, w.dtype), to_dev(Vr, w.dtype), to_dev(P, "f32"), pos=0,
+                   rope_base=base)
+        for g in range(w.Hkv):
+            slab[:, g], rest[:, g], vv[:, g] = oracle.append(
+                oracle.to_f64(Kr[:, g], w.dtype), oracle.to_f64(Vr[:, g], w.dtype),
+                P[g].astype(np.float64), w.d, w.dtype, rope_base=base, pos=0)
+        # decode from the GPU-appended cache against the oracle's own cache
+        out, idx = lib.decode(to_dev(q, w.dtype), cache, to_dev(P, "f32"), w.k, rope_base=base)
+        ref_out, ref_idx, ref_s = oracle.decode(q, slab, rest, vv, P, w.k, w.dtype, S=S,
+                                                rope=(base, S - 1))
+        check_decode(w.dtype, w.k, out.cpu().numpy(), idx.cpu().numpy(), ref_out, ref_idx, ref_s,
+                     all_pairs(w))
