@@ -85,6 +85,8 @@ def main():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-read-probe", action="store_true")
     ap.add_argument("--no-jaccard", action="store_true")
+    ap.add_argument("--rope-base", type=float, default=None,
+                    help="RoPE variant: keys embedded at their positions, the query at S-1")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="first run a plain device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -135,8 +137,9 @@ def main():
     prefill = w.prefill if w.prefill else S - 1
     K_raw, V_raw = synth.raw_cache(w, S - 1)
     log(f"generated raw cache {K_raw.shape}")
+    rb = args.rope_base
     base = loki.KVCache(w.B, w.Hkv, S, w.D, w.d, tdt, dev)
-    loki.append(base, up(K_raw), up(V_raw), Pd, pos=0)
+    loki.append(base, up(K_raw), up(V_raw), Pd, pos=0, rope_base=rb)
     R = 8
     new_k, new_v, qs = [], [], []
     for r in range(R):
@@ -144,7 +147,7 @@ def main():
         new_k.append(up(kn))
         new_v.append(up(vn))
         qs.append(up(synth.queries(w, step=r)))
-    loki.append(base, new_k[0], new_v[0], Pd, pos=S - 1)
+    loki.append(base, new_k[0], new_v[0], Pd, pos=S - 1, rope_base=rb)
     cache_bytes = sum(t.numel() * t.element_size() for t in (base.k_slab, base.k_rest, base.v)
                       if t is not None)
     if args.layers <= 0:
@@ -172,10 +175,12 @@ def main():
     new_k2 = [t[:, :, 0].contiguous() for t in new_k]
     new_v2 = [t[:, :, 0].contiguous() for t in new_v]
     step_plans = [loki.StepPlan(qs[i % R], new_k2[i % R], new_v2[i % R], caches[i % L], Pd, k,
-                                S - 1, out=out, idx=idx, workspace=ws, path=args.path)
+                                S - 1, out=out, idx=idx, workspace=ws, path=args.path,
+                                rope_base=rb)
                   for i in range(n_plans)]
     dec_plans = [loki.DecodePlan(qs[i % R], caches[i % L], Pd, k, S=S, out=out, idx=idx,
-                                 workspace=ws, path=args.path) for i in range(n_plans)]
+                                 workspace=ws, path=args.path, rope_base=rb)
+                 for i in range(n_plans)]
 
     def step(i):
         step_plans[i % n_plans]()
@@ -232,7 +237,8 @@ def main():
                    "Hkv": w.Hkv, "D": w.D, "d": w.d, "S": S, "k": k, "cache_dtype": w.dtype,
                    "step": "loki_decode_step: append 1 token/sequence at S-1 + decode over S",
                    "path": path_name,
-                   "layers_cycled": args.layers},
+                   "layers_cycled": args.layers,
+                   "rope_base": rb},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
                      "kernel": ("fused decode step (append + decode, one launch)" if "fused" in path_name
@@ -267,7 +273,8 @@ def main():
         other, key = ((loki.PATH_UNION, "union_gather") if path_name == "split"
                       else (loki.PATH_SPLIT, "per_head_gather"))
         alt_plans = [loki.DecodePlan(qs[i % R], caches[i % L], Pd, k, S=S, out=out, idx=idx,
-                                     workspace=ws, path=other) for i in range(n_plans)]
+                                     workspace=ws, path=other, rope_base=rb)
+                     for i in range(n_plans)]
         for i in range(args.warmup):
             alt_plans[i % n_plans]()
         _, ams = timed(lambda i: alt_plans[i % n_plans](), args.steps)
@@ -278,8 +285,8 @@ def main():
     # ---- same-GPU dense baseline on the same caches
     if not args.no_dense:
         dws = loki.alloc_workspace(w.B, w.Hq, w.D, S, 1, dev)
-        dense_plans = [loki.DensePlan(qs[i % R], caches[i % L], Pd, S=S, out=out, workspace=dws)
-                       for i in range(n_plans)]
+        dense_plans = [loki.DensePlan(qs[i % R], caches[i % L], Pd, S=S, out=out, workspace=dws,
+                                      rope_base=rb) for i in range(n_plans)]
         for i in range(args.warmup):
             dense_plans[i % n_plans]()
         _, dms = timed(lambda i: dense_plans[i % n_plans](), args.steps)
@@ -304,20 +311,21 @@ def main():
         ks = [w.k_at(x) for x in Ss]
         run_step = [loki.StepPlan(qs[st % R], toks[st][0], toks[st][1], run_cache, Pd, ks[st],
                                   Ss[st] - 1, out=out, idx=idx_flat[:hq * ks[st]].view(w.B, w.Hq, ks[st]),
-                                  workspace=ws, path=args.path) for st in range(w.steps)]
-        run_app = [loki.AppendPlan(run_cache, toks[st][2], toks[st][3], Pd, Ss[st] - 1)
+                                  workspace=ws, path=args.path, rope_base=rb)
+                    for st in range(w.steps)]
+        run_app = [loki.AppendPlan(run_cache, toks[st][2], toks[st][3], Pd, Ss[st] - 1, rope_base=rb)
                    for st in range(w.steps)]
         run_dec = [loki.DecodePlan(qs[st % R], run_cache, Pd, ks[st], S=Ss[st], out=out,
                                    idx=idx_flat[:hq * ks[st]].view(w.B, w.Hq, ks[st]), workspace=ws,
-                                   path=args.path) for st in range(w.steps)]
+                                   path=args.path, rope_base=rb) for st in range(w.steps)]
         n = w.steps
         run = {"prompt": w.prefill, "generated": n,
                "step_ms_total": timed(lambda i: run_step[i](), n)[1] * n,
                "append_ms_total": timed(lambda i: run_app[i](), n)[1] * n,
                "decode_ms_total": timed(lambda i: run_dec[i](), n)[1] * n}
         if not args.no_dense:
-            run_dense = [loki.DensePlan(qs[st % R], run_cache, Pd, S=Ss[st], out=out, workspace=dws)
-                         for st in range(w.steps)]
+            run_dense = [loki.DensePlan(qs[st % R], run_cache, Pd, S=Ss[st], out=out, workspace=dws,
+                                        rope_base=rb) for st in range(w.steps)]
             run["dense_ms_total"] = timed(lambda i: run_dense[i](), n)[1] * n
             run["loki_decode_speedup_vs_dense"] = run["dense_ms_total"] / run["decode_ms_total"]
         result["generation_run"] = run
@@ -330,17 +338,17 @@ def main():
     # real keys at their main settings; these keys are synthetic)
     if not args.no_jaccard:
         result["topk_agreement_vs_exact"] = topk_agreement(loki, w, S, k, K_raw, V_raw, new_k[0],
-                                                           new_v[0], qs[0], Pd, up, dev)
+                                                           new_v[0], qs[0], Pd, up, dev, rb)
         log(f"top-k Jaccard vs exact: {result['topk_agreement_vs_exact']}")
 
     # ---- CPU oracle on a bounded sample (rank 0, one GPU)
     if not args.no_cpu:
-        result["cpu_baseline"] = cpu_baseline(w, S, k, K_raw, V_raw, log)
+        result["cpu_baseline"] = cpu_baseline(w, S, k, K_raw, V_raw, log, rb)
 
     print(json.dumps(result), flush=True)
 
 
-def topk_agreement(loki, w, S, k, K_raw, V_raw, kn, vn, q, Pd, up, dev):
+def topk_agreement(loki, w, S, k, K_raw, V_raw, kn, vn, q, Pd, up, dev, rb=None):
     """Mean Jaccard similarity |A & B| / |A | B| between Loki's kept set at
     d = D/8, D/4, D/2 and the exact top-k (d = D) over every head-query."""
     import torch
@@ -349,9 +357,9 @@ def topk_agreement(loki, w, S, k, K_raw, V_raw, kn, vn, q, Pd, up, dev):
 
     def kept(d):
         c = loki.KVCache(w.B, w.Hkv, S, w.D, d, tdt, dev)
-        loki.append(c, Kd, Vd, Pd, pos=0)
-        loki.append(c, kn, vn, Pd, pos=S - 1)
-        _, idx = loki.decode(q, c, Pd, k, S=S, path=loki.PATH_SPLIT)
+        loki.append(c, Kd, Vd, Pd, pos=0, rope_base=rb)
+        loki.append(c, kn, vn, Pd, pos=S - 1, rope_base=rb)
+        _, idx = loki.decode(q, c, Pd, k, S=S, path=loki.PATH_SPLIT, rope_base=rb)
         torch.cuda.synchronize()
         out = idx.cpu().numpy().reshape(-1, k)
         del c
@@ -367,7 +375,7 @@ def topk_agreement(loki, w, S, k, K_raw, V_raw, kn, vn, q, Pd, up, dev):
     return res
 
 
-def cpu_baseline(w, S, k, K_raw, V_raw, log):
+def cpu_baseline(w, S, k, K_raw, V_raw, log, rb=None):
     """The CPU oracle, as it stands, decoding a bounded sample of the same
     workload: every query head of the first `nb` sequences at S tokens.  The
     oracle gets its own inputs (its own calibration and float64 append of the
@@ -390,14 +398,16 @@ def cpu_baseline(w, S, k, K_raw, V_raw, log):
         Vg = np.concatenate([V_raw[:nb, g], vn[:nb, g]], axis=1)
         slab[:, g], rest[:, g], vv[:, g] = oracle.append(oracle.to_f64(Kg, w.dtype),
                                                          oracle.to_f64(Vg, w.dtype),
-                                                         P32[g].astype(np.float64), w.d, w.dtype)
+                                                         P32[g].astype(np.float64), w.d, w.dtype,
+                                                         rope_base=rb)
     q = synth.queries(w)[:nb]
     pairs = [(b, h) for b in range(nb) for h in range(w.Hq)]
     reps, elapsed = 0, 0.0
     with threadpool_limits(limits=1):
         while reps < 1 or (elapsed < 10.0 and reps < 200):  # about 10 s of CPU work
             t = time.perf_counter()
-            oracle.decode(q, slab, rest, vv, P32, k, w.dtype, S=S, heads=pairs)
+            oracle.decode(q, slab, rest, vv, P32, k, w.dtype, S=S, heads=pairs,
+                          rope=None if rb is None else (rb, S - 1))
             elapsed += time.perf_counter() - t
             reps += 1
     n = reps * len(pairs)
