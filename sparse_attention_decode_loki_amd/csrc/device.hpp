@@ -121,6 +121,20 @@ __device__ __forceinline__ float ld_elem<BF16>(const uint16_t* p, int64_t i) {
 // the angle pos * base^(-2i/D) (the embedding of the Llama-family models the
 // pages evaluate; they name RoPE without its form).  base == 0 means no
 // embedding: the element itself.
+// Cosine and sine of the angle of pair i (every caller forms them with this
+// one expression, so every kernel embeds identically).
+__device__ __forceinline__ void rope_cs(int i, int D, double base, int pos, double& cs,
+                                        double& sn) {
+  sincos(static_cast<double>(pos) * pow(base, -2.0 * i / D), &sn, &cs);
+}
+
+// a = x_m, b = its partner (x_{m+D/2} for m < D/2, else x_{m-D/2}):
+// first half x_i cos - x_{i+h} sin, second half x_{i+h} cos + x_i sin.
+__device__ __forceinline__ double rope_apply(double a, double b, double cs, double sn, bool first) {
+  const double t = b * sn;  // explicit fused forms: the same rounding wherever it is inlined
+  return first ? fma(a, cs, -t) : fma(a, cs, t);
+}
+
 template <class E>
 __device__ __forceinline__ double rope_elem(const typename E::T* x, int m, int D, double base,
                                             int pos) {
@@ -128,12 +142,10 @@ __device__ __forceinline__ double rope_elem(const typename E::T* x, int m, int D
   if (base == 0.0) return a;
   const int h = D >> 1;
   const bool first = m < h;
-  const int i = first ? m : m - h;
-  const double b = static_cast<double>(ld_elem<E>(x, first ? m + h : m - h));  // partner
-  double sn, cs;
-  sincos(static_cast<double>(pos) * pow(base, -2.0 * i / D), &sn, &cs);
-  // first half: x_i cos - x_{i+h} sin; second half: x_{i+h} cos + x_i sin
-  return first ? a * cs - b * sn : a * cs + b * sn;
+  const double b = static_cast<double>(ld_elem<E>(x, first ? m + h : m - h));
+  double cs, sn;
+  rope_cs(first ? m : m - h, D, base, pos, cs, sn);
+  return rope_apply(a, b, cs, sn, first);
 }
 
 // Data-parallel-primitive (DPP) lane moves.  dpp<CTRL, ROW_MASK, BANK_MASK>

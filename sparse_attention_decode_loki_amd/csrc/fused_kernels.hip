@@ -94,12 +94,31 @@ __global__ void __launch_bounds__(kFusedBlock) fused_kernel(FusedArgs a) {
   // 1. q' = q . P[g] (and, for STEP, k' = k_new . P[g] in float64): thread
   //    (cq, rb) adds rows [rb*RB, rb*RB + RB) for columns 4*cq .. 4*cq + 3,
   //    read as 16-byte chunks; the NRB partials are added through LDS.
-  if (threadIdx.x < D) {
-    rin[threadIdx.x] = static_cast<float>(rope_elem<E>(static_cast<const T*>(a.q) + row * D,
-                                                       threadIdx.x, D, a.rope.base, a.rope.pos));
-    if (STEP)
-      kin[threadIdx.x] = rope_elem<E>(static_cast<const T*>(a.k_new) + bgo * D, threadIdx.x, D,
-                                      a.rope.base, a.pos);
+  if (a.rope.base == 0.0) {
+    if (threadIdx.x < D) {
+      rin[threadIdx.x] = ld_elem<E>(static_cast<const T*>(a.q), row * D + threadIdx.x);
+      if (STEP)
+        kin[threadIdx.x] = ld_elem<E>(static_cast<const T*>(a.k_new), bgo * D + threadIdx.x);
+    }
+  } else {
+    // RoPE: each pair's cosine and sine once, then the elements (a step
+    // places the query and the new key both at pos: a.rope.pos == a.pos)
+    __shared__ double rcs[2][D / 2];
+    if (threadIdx.x < D / 2)
+      rope_cs(threadIdx.x, D, a.rope.base, a.rope.pos, rcs[0][threadIdx.x], rcs[1][threadIdx.x]);
+    __syncthreads();
+    if (threadIdx.x < D) {
+      const int m = threadIdx.x, h = D / 2;
+      const bool first = m < h;
+      const int i = first ? m : m - h, mp = first ? m + h : m - h;
+      const T* qv = static_cast<const T*>(a.q) + row * D;
+      rin[m] = static_cast<float>(rope_apply(ld_elem<E>(qv, m), ld_elem<E>(qv, mp), rcs[0][i],
+                                             rcs[1][i], first));
+      if (STEP) {
+        const T* kv = static_cast<const T*>(a.k_new) + bgo * D;
+        kin[m] = rope_apply(ld_elem<E>(kv, m), ld_elem<E>(kv, mp), rcs[0][i], rcs[1][i], first);
+      }
+    }
   }
   __syncthreads();
   if (threadIdx.x < kBlock) {

@@ -327,6 +327,40 @@ def test_dense_matches_oracle(lib, name):
         assert out_error(c.w.dtype, out[b, h], ref[b, h]) <= TOL[c.w.dtype]
 
 
+# ------------------------------------------------------------ size limits --
+
+LIMITS = {
+    # the longest context the union gather takes (its bitmap row in LDS), and
+    # rows far beyond the top-k's LDS staging (selected from global memory)
+    "union_max_S": (synth.custom("union_max_S", 701, B=1, Hq=4, Hkv=1, S=1 << 17, k_f=0.125),
+                    [2, 3]),
+    # q' + scores + kept ids just under the fused kernel's 56 KiB of LDS
+    "fused_lds_max": (synth.custom("fused_lds_max", 702, B=1, Hq=2, Hkv=2, S=11000,
+                                   k_f=2999.5 / 11000), [1, 2]),
+}
+
+
+@pytest.mark.parametrize("name", sorted(LIMITS))
+def test_decode_at_size_limits(lib, name):
+    """Decode at the largest sizes each path accepts, every (sequence, head)
+    pair against the oracle; one past the limit is refused."""
+    w, paths = LIMITS[name]
+    c = make_case(w)
+    cache = device_cache(lib, c)
+    ref_out, ref_idx, ref_s = oracle.decode(c.q, c.slab, c.rest, c.v, c.P, c.k, w.dtype)
+    for path in paths:
+        out, idx = lib.decode(_q(c), cache, _P(c), c.k, path=path)
+        check_decode(w.dtype, c.k, out.cpu().numpy(), idx.cpu().numpy(), ref_out, ref_idx, ref_s,
+                     all_pairs(w))
+    if name == "union_max_S":
+        assert lib.decode_path(1, 4, 1, 128, 32, (1 << 17) + 1, c.k, "bf16", 0) == 2
+    else:
+        # (128 + 11000 + 3209) floats is one past 56 KiB
+        assert lib.decode_path(1, 2, 2, 128, 32, 11000, 3208, "bf16", 1) == 1
+        with pytest.raises(lib.LokiError):
+            lib.decode_path(1, 2, 2, 128, 32, 11000, 3209, "bf16", 1)
+
+
 # ------------------------------------------------------- full bench shapes --
 
 FULL = ["l2_7b", "l2_13b_run", "l3_8b_gqa", "mistral_32k"]
