@@ -173,26 +173,6 @@ int auto_path(int B, int Hq, int Hkv, int D, int d, int S, int kk, int dtype) {
   return auto_union(Hq, Hkv, D, d, S, kk, dtype) ? LOKI_PATH_UNION : LOKI_PATH_SPLIT;
 }
 
-}  // namespace
-
-extern "C" {
-
-const char* loki_status_string(int status) {
-  switch (status) {
-    case LOKI_OK: return "LOKI_OK";
-    case LOKI_EINVAL: return "LOKI_EINVAL: invalid argument";
-    case LOKI_EWORKSPACE: return "LOKI_EWORKSPACE: workspace missing or too small";
-    case LOKI_EDEVICE: return "LOKI_EDEVICE: HIP launch failed";
-    case LOKI_EUNSUPPORTED: return "LOKI_EUNSUPPORTED: unsupported shape or dtype";
-    default: return "LOKI: unknown status";
-  }
-}
-
-int loki_abi_version(void) { return kAbiVersion; }
-
-}  // extern "C"
-
-namespace {
 
 int append_impl(const void* k_new, const void* v_new, const float* P, void* k_slab, void* k_rest,
                 void* v, int32_t B, int32_t Hkv, int32_t D, int32_t d, int32_t S_max, int32_t pos,
@@ -213,47 +193,6 @@ int append_impl(const void* k_new, const void* v_new, const float* P, void* k_sl
                                        static_cast<hipStream_t>(stream), rope_base));
 }
 
-}  // namespace
-
-extern "C" {
-
-int loki_kv_append(const void* k_new, const void* v_new, const float* P, void* k_slab,
-                   void* k_rest, void* v, int32_t B, int32_t Hkv, int32_t D, int32_t d,
-                   int32_t S_max, int32_t pos, int32_t T, int32_t dtype, void* stream) {
-  return append_impl(k_new, v_new, P, k_slab, k_rest, v, B, Hkv, D, d, S_max, pos, T, dtype, 0.0,
-                     stream);
-}
-
-int loki_kv_append_rope(const void* k_new, const void* v_new, const float* P, void* k_slab,
-                        void* k_rest, void* v, int32_t B, int32_t Hkv, int32_t D, int32_t d,
-                        int32_t S_max, int32_t pos, int32_t T, int32_t dtype, double rope_base,
-                        void* stream) {
-  if (!rope_ok(rope_base)) return LOKI_EINVAL;
-  return append_impl(k_new, v_new, P, k_slab, k_rest, v, B, Hkv, D, d, S_max, pos, T, dtype,
-                     rope_base, stream);
-}
-
-size_t loki_decode_workspace_size(int32_t B, int32_t Hq, int32_t D, int32_t S_max, int32_t k_max) {
-  if (B <= 0 || Hq <= 0 || D <= 0 || S_max <= 0) return 0;
-  return workspace_bytes(B, Hq, D, S_max, k_max < 1 ? 1 : k_max);
-}
-
-int loki_decode_path(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t d, int32_t S,
-                     int32_t k, int32_t dtype, int32_t path) {
-  int st = check_shape(B < 1 ? 1 : B, Hq, Hkv, D, d, S, S, dtype);
-  if (st != LOKI_OK) return st;
-  if (k < 1) return LOKI_EINVAL;
-  const int kk = std::min(k, S);
-  if (path == LOKI_PATH_SPLIT) return LOKI_PATH_SPLIT;
-  if (path == LOKI_PATH_FUSED) return fused_fits(D, S, kk) ? LOKI_PATH_FUSED : LOKI_EUNSUPPORTED;
-  if (path == LOKI_PATH_UNION) return union_ok(Hq, Hkv, S) ? LOKI_PATH_UNION : LOKI_EUNSUPPORTED;
-  if (path != LOKI_PATH_AUTO) return LOKI_EINVAL;
-  return auto_path(B, Hq, Hkv, D, d, S, kk, dtype);
-}
-
-}  // extern "C"
-
-namespace {
 
 int decode_impl(const void* q, const void* k_slab, const void* k_rest, const void* v,
                 const float* P, int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t d,
@@ -364,6 +303,55 @@ int dense_impl(const void* q, const void* k_slab, const void* k_rest, const void
 }  // namespace
 
 extern "C" {
+
+const char* loki_status_string(int status) {
+  switch (status) {
+    case LOKI_OK: return "LOKI_OK";
+    case LOKI_EINVAL: return "LOKI_EINVAL: invalid argument";
+    case LOKI_EWORKSPACE: return "LOKI_EWORKSPACE: workspace missing or too small";
+    case LOKI_EDEVICE: return "LOKI_EDEVICE: HIP launch failed";
+    case LOKI_EUNSUPPORTED: return "LOKI_EUNSUPPORTED: unsupported shape or dtype";
+    default: return "LOKI: unknown status";
+  }
+}
+
+int loki_abi_version(void) { return kAbiVersion; }
+
+
+int loki_kv_append(const void* k_new, const void* v_new, const float* P, void* k_slab,
+                   void* k_rest, void* v, int32_t B, int32_t Hkv, int32_t D, int32_t d,
+                   int32_t S_max, int32_t pos, int32_t T, int32_t dtype, void* stream) {
+  return append_impl(k_new, v_new, P, k_slab, k_rest, v, B, Hkv, D, d, S_max, pos, T, dtype, 0.0,
+                     stream);
+}
+
+int loki_kv_append_rope(const void* k_new, const void* v_new, const float* P, void* k_slab,
+                        void* k_rest, void* v, int32_t B, int32_t Hkv, int32_t D, int32_t d,
+                        int32_t S_max, int32_t pos, int32_t T, int32_t dtype, double rope_base,
+                        void* stream) {
+  if (!rope_ok(rope_base)) return LOKI_EINVAL;
+  return append_impl(k_new, v_new, P, k_slab, k_rest, v, B, Hkv, D, d, S_max, pos, T, dtype,
+                     rope_base, stream);
+}
+
+size_t loki_decode_workspace_size(int32_t B, int32_t Hq, int32_t D, int32_t S_max, int32_t k_max) {
+  if (B <= 0 || Hq <= 0 || D <= 0 || S_max <= 0) return 0;
+  return workspace_bytes(B, Hq, D, S_max, k_max < 1 ? 1 : k_max);
+}
+
+int loki_decode_path(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t d, int32_t S,
+                     int32_t k, int32_t dtype, int32_t path) {
+  int st = check_shape(B < 1 ? 1 : B, Hq, Hkv, D, d, S, S, dtype);
+  if (st != LOKI_OK) return st;
+  if (k < 1) return LOKI_EINVAL;
+  const int kk = std::min(k, S);
+  if (path == LOKI_PATH_SPLIT) return LOKI_PATH_SPLIT;
+  if (path == LOKI_PATH_FUSED) return fused_fits(D, S, kk) ? LOKI_PATH_FUSED : LOKI_EUNSUPPORTED;
+  if (path == LOKI_PATH_UNION) return union_ok(Hq, Hkv, S) ? LOKI_PATH_UNION : LOKI_EUNSUPPORTED;
+  if (path != LOKI_PATH_AUTO) return LOKI_EINVAL;
+  return auto_path(B, Hq, Hkv, D, d, S, kk, dtype);
+}
+
 
 int loki_decode_ex(const void* q, const void* k_slab, const void* k_rest, const void* v,
                    const float* P, int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t d,
