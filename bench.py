@@ -204,6 +204,20 @@ def main():
     ms_per_step, step_avg_ms = timed(lambda i: step(args.warmup + i), args.steps)
     log(f"timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step, events {step_avg_ms * 1e3:.1f} us/launch")
 
+    # per-launch distribution: each step between its own pair of events
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for i, (a, b) in enumerate(evs):
+        a.record()
+        step(args.warmup + args.steps + i)
+        b.record()
+    torch.cuda.synchronize()
+    lat = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
+    step_latency = {"median_us": float(np.median(lat)), "p10_us": float(np.percentile(lat, 10)),
+                    "p90_us": float(np.percentile(lat, 90)), "launches": len(lat)}
+    log(f"per-launch step: median {step_latency['median_us']:.1f} us, "
+        f"p10 {step_latency['p10_us']:.1f}, p90 {step_latency['p90_us']:.1f}")
+
     # decode alone (append excluded, as the pages time it), same caches
     for i in range(args.warmup):
         dec_plans[i % n_plans]()
@@ -247,6 +261,7 @@ def main():
                      "avg_launch_ms": step_avg_ms,
                      "timing": "HIP events around the timed region's back-to-back launches",
                      "kernel_source_hash": khash},
+        "step_latency": step_latency,
         "decode_only": {"head_queries_per_s": hq / (dec_avg_ms * 1e-3), "avg_ms": dec_avg_ms,
                         "achieved_GBs": by["total"] / (dec_avg_ms * 1e-3) / 1e9},
     }
