@@ -67,7 +67,9 @@ typedef enum { LOKI_F32 = 0, LOKI_BF16 = 1 } loki_dtype;
  * (loki_decode_path reports which).  FUSED runs one kernel per (sequence,
  * query head) that scores, selects and attends with the scores held in LDS
  * (requires (D + S + min(k, S)) * 4 bytes <= 56 KiB); AUTO takes it for one
- * query head per KV head and at least 256 (sequence, head) rows.  SPLIT runs
+ * query head per KV head when rows = B * Hq satisfies rows * S + 420000 >=
+ * 190 * S (any rows for S <= 2222, at least 88 rows at S = 4096, 139 at
+ * S = 8192, never more than 190).  SPLIT runs
  * separate score, selection and attention kernels through the workspace; its
  * attention reads each query head's kept rows, with the query heads of one
  * KV head scheduled together so that rows several of them kept are served

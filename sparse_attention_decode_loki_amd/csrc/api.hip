@@ -147,10 +147,17 @@ bool fused_fits(int D, int S, int kk) {
 }
 
 // The fused kernel reads the key slab once per query head, so it is chosen
-// for one query head per KV head, when there are enough (sequence, head)
-// pairs to give every compute unit work, and when its LDS fits.
+// only for one query head per KV head, and when its LDS fits.  One
+// workgroup streams a whole row: its time grows with S but hardly with the
+// number of rows while they fit on the chip, about 8.7 + 0.0051 * S us.  The
+// split path's four launches cost about 20 us plus 2.7e-5 us per row and
+// token.  Fused is faster when rows > 190 - 420000 / S (measured, bf16,
+// D = 128, d = 32, k = S/4: split wins at 64 rows of 4096 and 128 rows of
+// 8192, fused at 96 and 192).
 bool auto_fused(int B, int Hq, int Hkv, int D, int S, int kk) {
-  return Hq == Hkv && static_cast<int64_t>(B) * Hq >= 256 && fused_fits(D, S, kk);
+  if (Hq != Hkv || !fused_fits(D, S, kk)) return false;
+  const int64_t rows = static_cast<int64_t>(B) * Hq;
+  return rows * S + 420000 >= 190LL * S;
 }
 
 // The union gather is chosen (bf16 caches, where its products run on the

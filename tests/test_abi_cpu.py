@@ -93,6 +93,19 @@ def test_decode_fused_rejects_when_lds_too_small(L):
     assert lib.loki_decode_path(1, 4, 4, 128, 33, 100, 25, 1, 0) == -4
 
 
+def test_auto_takes_fused_by_rows_and_context(L):
+    # fused when rows * S + 420000 >= 190 * S (one query head per KV head)
+    lib = L.load()
+    assert lib.loki_decode_path(1, 1, 1, 128, 32, 2222, 555, 1, 0) == 1    # short rows: any count
+    assert lib.loki_decode_path(1, 1, 1, 128, 32, 2223, 555, 1, 0) == 2
+    assert lib.loki_decode_path(1, 87, 87, 128, 32, 4096, 1024, 1, 0) == 2
+    assert lib.loki_decode_path(1, 88, 88, 128, 32, 4096, 1024, 1, 0) == 1
+    assert lib.loki_decode_path(1, 138, 138, 128, 32, 8192, 2048, 1, 0) == 2
+    assert lib.loki_decode_path(1, 139, 139, 128, 32, 8192, 2048, 1, 0) == 1
+    assert lib.loki_decode_path(1, 190, 190, 128, 32, 11000, 2750, 1, 0) == 1
+    assert lib.loki_decode_path(2, 4, 2, 128, 32, 500, 125, 1, 0) != 1     # grouped heads: never
+
+
 def test_union_path_only_for_two_or_four_heads_per_kv_head(L):
     lib = L.load()
     assert lib.loki_decode_path(8, 32, 8, 128, 32, 8192, 2048, 1, 3) == 3    # G = 4
