@@ -28,6 +28,22 @@ HIPCC_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
 CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-I", os.path.join(ROOT, "include")]
 
 
+C_CLIENT_SRC = os.path.join(ROOT, "tests", "host", "c_client.c")
+C_CLIENT = os.path.join(ROOT, "tests", "host", "c_client")
+
+
+def build_c_client() -> str:
+    """The plain-C test client of the ABI (tests/host/c_client.c), linked
+    against the in-tree libloki.so and the HIP runtime."""
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    _run(["gcc", "-std=c99", "-O2", "-Wall", "-D__HIP_PLATFORM_AMD__",
+          "-I", os.path.join(rocm, "include"), "-I", os.path.join(ROOT, "include"), C_CLIENT_SRC,
+          "-L", PKG, "-lloki", "-L", os.path.join(rocm, "lib"), "-lamdhip64", "-lm",
+          "-Wl,-rpath,$ORIGIN/../../sparse_attention_decode_loki_amd:" + os.path.join(rocm, "lib"),
+          "-o", C_CLIENT])
+    return C_CLIENT
+
+
 def _hipcc() -> str:
     for c in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
         if c and os.path.exists(c):
@@ -65,3 +81,4 @@ def build(verbose: bool = False) -> str:
 
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_c_client())
