@@ -180,6 +180,44 @@ def test_topk_extreme_value_ranges(lib, kind):
         assert np.array_equal(idx[r].astype(np.int64), want), f"row {r}"
 
 
+def _random_topk_case(i):
+    """Case i of a fixed pseudo-random family: log-uniform S in [1, 40000],
+    any k in [1, S + 5], a padded row stride, and one of several value
+    distributions (continuous, few distinct values, signed zeros, outliers,
+    a narrow range)."""
+    rng = np.random.default_rng(9000 + i)
+    S = int(np.exp(rng.uniform(0.0, np.log(40000.0))))
+    k = int(rng.integers(1, S + 6))
+    ld = (S + 3) // 4 * 4 + 4 * int(rng.integers(0, 3))
+    kind = i % 5
+    if kind == 0:
+        row = rng.standard_normal(S) * 10.0 ** rng.uniform(-3, 3)
+    elif kind == 1:
+        row = rng.integers(-3, 4, S).astype(np.float64)
+    elif kind == 2:
+        row = np.where(rng.random(S) < 0.3, 0.0, rng.standard_normal(S))
+        row = np.where(rng.random(S) < 0.5, -row, row)  # -0.0 and +0.0 mixed
+    elif kind == 3:
+        row = rng.standard_normal(S)
+        row[rng.integers(0, S, max(1, S // 1000))] = 1e6
+    else:
+        row = 1.0 + rng.integers(0, 1000, S) * 2.0 ** -20
+    return S, k, ld, row.astype(np.float32)
+
+
+@pytest.mark.parametrize("i", range(40))
+def test_topk_random_family(lib, i):
+    import torch
+    S, k, ld, row = _random_topk_case(i)
+    host = np.full((2, ld), 1e30, np.float32)  # beyond S: must be ignored
+    host[0, :S] = row
+    host[1, :S] = row[::-1]
+    idx = lib.topk(torch.from_numpy(host).cuda(), k, S=S).cpu().numpy()
+    for r in range(2):
+        want = oracle.select_topk(host[r, :S].astype(np.float64), k)
+        assert np.array_equal(idx[r].astype(np.int64), want), f"S={S} k={k} row {r}"
+
+
 def test_topk_crossing_bin_of_signed_zeros(lib):
     """A crossing bin made of +0.0 and -0.0 only: they rank equal, so the
     lowest indices among them are kept."""
