@@ -174,3 +174,52 @@ def test_rope_pre_and_post_rotary_bases_both_decode(lib):
                                                 rope=(base, S - 1))
         check_decode(w.dtype, w.k, out.cpu().numpy(), idx.cpu().numpy(), ref_out, ref_idx, ref_s,
                      all_pairs(w))
+
+
+@pytest.mark.parametrize("path", [1, 2, 3], ids=["fused", "split", "union"])
+def test_rope_decode_step_replays_from_a_captured_graph(lib, path):
+    """The RoPE step launches only kernels, so it captures into a HIP graph:
+    three replays, with eager work between them, each writing the same slot
+    and producing the same output as an eager step on a fresh copy."""
+    import torch
+    w, S, S_max, base = CASES["rope_gqa4"]
+    if path == 1:
+        w, S, S_max, base = CASES["rope_mha"]
+    c, _ = case("rope_gqa4" if path != 1 else "rope_mha")
+    P = to_dev(c.P, "f32")
+    kn, vn = synth.new_tokens(w, 77)
+    q = to_dev(synth.queries(w, step=77), w.dtype)
+    kd, vd = to_dev(kn[:, :, 0], w.dtype), to_dev(vn[:, :, 0], w.dtype)
+    pos = S - 1
+    k = w.k_at(pos + 1)
+    ws = lib.alloc_workspace(w.B, w.Hq, w.D, c.S_max, k, torch.device("cuda"))
+    ref_cache = device_cache(lib, c)
+    ref_out, ref_idx = lib.decode_step(q, kd, vd, ref_cache, P, k, pos=pos, workspace=ws, path=path,
+                                       rope_base=base)
+    ref_out, ref_idx = ref_out.cpu().numpy(), ref_idx.cpu().numpy()
+    ref_slab = to_host(ref_cache.k_slab, w.dtype)
+    cache = device_cache(lib, c)
+    out = torch.empty((w.B, w.Hq, w.D), dtype=torch.float32, device="cuda")
+    idx = torch.empty((w.B, w.Hq, k), dtype=torch.int32, device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):  # warm up on the capture stream
+        lib.decode_step(q, kd, vd, cache, P, k, pos=pos, out=out, idx=idx, workspace=ws, path=path,
+                        rope_base=base)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        lib.decode_step(q, kd, vd, cache, P, k, pos=pos, out=out, idx=idx, workspace=ws, path=path,
+                        rope_base=base)
+    for rep in range(3):
+        out.fill_(float("nan"))
+        idx.fill_(-1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(idx.cpu().numpy(), ref_idx), f"replay {rep}"
+        assert np.array_equal(out.cpu().numpy().view(np.uint32), ref_out.view(np.uint32)), rep
+        assert np.array_equal(to_host(cache.k_slab, w.dtype), ref_slab), rep
+        lib.decode(q, cache, P, 7, workspace=ws, path=2, rope_base=base)  # eager work between
+        torch.cuda.synchronize()
