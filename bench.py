@@ -85,6 +85,8 @@ def main():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-read-probe", action="store_true")
     ap.add_argument("--no-jaccard", action="store_true")
+    ap.add_argument("--kf", type=float, default=None, help="override the budget k_f (k = floor(k_f*S))")
+    ap.add_argument("--df", type=float, default=None, help="override d_f (d = d_f*D, d*2 a multiple of 16)")
     ap.add_argument("--rope-base", type=float, default=None,
                     help="RoPE variant: keys embedded at their positions, the query at S-1")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -115,6 +117,10 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     w = synth.WORKLOADS[args.config]
+    if args.kf is not None or args.df is not None:
+        import dataclasses
+        w = dataclasses.replace(w, k_f=w.k_f if args.kf is None else args.kf,
+                                d=w.d if args.df is None else int(round(args.df * w.D)))
     S = w.S
     k = w.k
     t_setup = time.time()
@@ -232,7 +238,9 @@ def main():
     khash = kernel_source_hash()
     path_name = {1: "fused", 2: "split", 3: "union"}[
         loki.decode_path(w.B, w.Hq, w.Hkv, w.D, w.d, S, k, w.dtype, args.path)]
-    traffic = measured_traffic(khash, args.config) if "fused" in path_name else None
+    overridden = args.kf is not None or args.df is not None
+    traffic = (measured_traffic(khash, args.config)
+               if "fused" in path_name and not overridden else None)
 
     result = {
         "metric": METRIC,
@@ -247,7 +255,9 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic: seeded keys with a decaying PCA spectrum, N(0,1) values and queries",
-        "config": {"workload": f"{w.name} steady state at S={S}", "B": w.B, "Hq": w.Hq,
+        "config": {"workload": f"{w.name} steady state at S={S}"
+                               + (f" with k_f={w.k_f}, d={w.d}" if overridden else ""),
+                   "B": w.B, "Hq": w.Hq,
                    "Hkv": w.Hkv, "D": w.D, "d": w.d, "S": S, "k": k, "cache_dtype": w.dtype,
                    "step": "loki_decode_step: append 1 token/sequence at S-1 + decode over S",
                    "path": path_name,
