@@ -164,14 +164,6 @@ __global__ void __launch_bounds__(kFusedBlock) fused_kernel(FusedArgs a) {
       const T vn = static_cast<const T*>(a.v_new)[bgo * D + col];
       kslot[col] = st;
       vslot[col] = vn;
-      if (h % G == 0) {  // one writer per KV head
-        const int64_t slot = bgo * a.S_max + a.pos;
-        if (col < d)
-          static_cast<T*>(a.slab)[slot * d + col] = st;
-        else
-          static_cast<T*>(a.rest)[slot * (D - d) + (col - d)] = st;
-        static_cast<T*>(a.val)[slot * D + col] = vn;
-      }
     }
   }
   __syncthreads();
@@ -214,13 +206,11 @@ __global__ void __launch_bounds__(kFusedBlock) fused_kernel(FusedArgs a) {
   }
   __syncthreads();
 
-  // 3. top-k -> LDS and the idx output
+  // 3. top-k -> LDS (the idx output is written at the end: one in-order
+  //    counter tracks loads and stores alike, so stores issued here would
+  //    delay the first wait of the gather by their own latency)
   {
-    int* irow = a.idx + row * kk;
-    auto emit = [&](int p, int j) {
-      ib[p] = j;
-      irow[p] = j;
-    };
+    auto emit = [&](int p, int j) { ib[p] = j; };
     if (SMALL)
       block_select_topk_hist<NT, kFusedKeys, CAP>([&](int j) { return sb[j]; }, S, kk, hist0,
                                                   emit, sc.sel.s.reg, sc.sel.cand);
@@ -244,6 +234,20 @@ __global__ void __launch_bounds__(kFusedBlock) fused_kernel(FusedArgs a) {
   merge_groups<E, D, 1, NT>(st, sc.mrg, [&](int, int dim, float, float Ls, float A) {
     a.out[row * D + dim] = A / Ls;
   });
+  // The row's stores come last (see the selection above): the idx output and,
+  // for STEP, the appended token's cache row (one writer per KV head; this
+  // launch served that token from LDS).
+  int* irow = a.idx + row * kk;
+  for (int p = threadIdx.x; p < kk; p += NT) irow[p] = ib[p];
+  if (STEP && h % G == 0 && threadIdx.x < D) {
+    const int col = threadIdx.x;
+    const int64_t slot = bgo * a.S_max + a.pos;
+    if (col < d)
+      static_cast<T*>(a.slab)[slot * d + col] = kslot[col];
+    else
+      static_cast<T*>(a.rest)[slot * (D - d) + (col - d)] = kslot[col];
+    static_cast<T*>(a.val)[slot * D + col] = vslot[col];
+  }
 }
 
 // --------------------------------------------------------------- launchers --
