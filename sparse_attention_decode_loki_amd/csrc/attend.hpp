@@ -187,20 +187,51 @@ __device__ __forceinline__ void merge_groups(const Acc<E::VEC> (&st)[NH],
     for (int v = 0; v < VEC; ++v) sm.a[h][grp][r * VEC + v] = st[h].a[v];
   }
   __syncthreads();
-  for (int o = threadIdx.x; o < NH * D; o += NT) {
-    const int h = o / D, dim = o % D;
-    float M = -INFINITY;
+  // PT threads share one output (groups split PT ways, partial sums added
+  // across neighbouring lanes) when the workgroup has that many threads per
+  // output; otherwise each output is one thread's loop over all groups.
+  constexpr int PT = (NT >= 4 * NH * D && NG % 4 == 0) ? 4 : (NT >= 2 * NH * D && NG % 2 == 0) ? 2 : 1;
+  if constexpr (PT > 1) {
+    constexpr int GP = NG / PT;
+    const int o = threadIdx.x / PT, part = threadIdx.x % PT;
+    if (o < NH * D) {  // NT is a multiple of PT: whole lane quads take part
+      const int h = o / D, dim = o % D;
+      float M = -INFINITY;
 #pragma unroll
-    for (int g = 0; g < NG; ++g) M = fmaxf(M, sm.m[h][g]);
-    float L = 0.f, A = 0.f;
+      for (int g = 0; g < NG; ++g) M = fmaxf(M, sm.m[h][g]);
+      float L = 0.f, A = 0.f;
 #pragma unroll
-    for (int g = 0; g < NG; ++g) {
-      const float mg = sm.m[h][g];
-      const float w = (mg == -INFINITY) ? 0.f : fast_exp2(mg - M);
-      L = fmaf(sm.l[h][g], w, L);
-      A = fmaf(sm.a[h][g][dim], w, A);
+      for (int i = 0; i < GP; ++i) {
+        const int g = part * GP + i;
+        const float mg = sm.m[h][g];
+        const float w = (mg == -INFINITY) ? 0.f : fast_exp2(mg - M);
+        L = fmaf(sm.l[h][g], w, L);
+        A = fmaf(sm.a[h][g][dim], w, A);
+      }
+      L += dpp_f<0xB1>(L);  // lanes 0<->1, 2<->3
+      A += dpp_f<0xB1>(A);
+      if constexpr (PT == 4) {
+        L += dpp_f<0x4E>(L);  // lanes 0<->2, 1<->3
+        A += dpp_f<0x4E>(A);
+      }
+      if (part == 0) fin(h, dim, M, L, A);
     }
-    fin(h, dim, M, L, A);
+  } else {
+    for (int o = threadIdx.x; o < NH * D; o += NT) {
+      const int h = o / D, dim = o % D;
+      float M = -INFINITY;
+#pragma unroll
+      for (int g = 0; g < NG; ++g) M = fmaxf(M, sm.m[h][g]);
+      float L = 0.f, A = 0.f;
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        const float mg = sm.m[h][g];
+        const float w = (mg == -INFINITY) ? 0.f : fast_exp2(mg - M);
+        L = fmaf(sm.l[h][g], w, L);
+        A = fmaf(sm.a[h][g][dim], w, A);
+      }
+      fin(h, dim, M, L, A);
+    }
   }
 }
 
