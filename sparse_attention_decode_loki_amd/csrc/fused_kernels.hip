@@ -174,35 +174,28 @@ __global__ void __launch_bounds__(kFusedBlock) fused_kernel(FusedArgs a) {
     float qf[1][VEC];
 #pragma unroll
     for (int v = 0; v < VEC; ++v) qf[0][v] = (part * VEC < d) ? qs[part * VEC + v] : 0.f;
+    // STEP: the new token's score from its LDS row, with the streaming
+    // pass's arithmetic, formed by every wave (each lane group ends with the
+    // same sum), so the stream's value for that slot, read from the cache row
+    // the launch has not written yet, is replaced without a barrier
+    float snew = 0.f;
+    if (STEP) {
+      float x[VEC];
+      Chunk ch = (part * VEC < d) ? ld16(kslot + part * VEC) : zero_chunk();
+      unpack<E>(ch, x);
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) snew = fmaf(qf[0][v], x[v], snew);
+      snew = group_sum<LPS>(snew);
+    }
     constexpr int US = 4;  // 16-byte slab loads in flight per lane (8 waves)
     Chunk c[US];
     score_first<E, LPS, US, NT>(sl, d, 0, S, c);
     // the selection's first radix digit is counted here, under the stream
     score_loop<E, LPS, 1, US, NT>(sl, d, 0, S, qf, [&](int, int j, float s) {
+      if (STEP && j == a.pos) s = snew;
       sb[j] = s;
       if (SMALL) atomicAdd(&hist0[first_digit(order_key(s))], 1u);
     }, c);
-    if (STEP) {
-      // the new token's score from its LDS row, with the streaming pass's
-      // arithmetic (wave 0; sb[pos] written by the loop is discarded)
-      __syncthreads();
-      if (threadIdx.x < 64) {
-        float x[VEC];
-        Chunk ch = (part * VEC < d) ? ld16(kslot + part * VEC) : zero_chunk();
-        unpack<E>(ch, x);
-        float dot = 0.f;
-#pragma unroll
-        for (int v = 0; v < VEC; ++v) dot = fmaf(qf[0][v], x[v], dot);
-        dot = group_sum<LPS>(dot);
-        if (threadIdx.x == 0) {
-          if (SMALL) {
-            atomicSub(&hist0[first_digit(order_key(sb[a.pos]))], 1u);
-            atomicAdd(&hist0[first_digit(order_key(dot))], 1u);
-          }
-          sb[a.pos] = dot;
-        }
-      }
-    }
   }
   __syncthreads();
 
