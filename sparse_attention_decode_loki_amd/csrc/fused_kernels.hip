@@ -41,8 +41,10 @@ constexpr int kFusedKeys = 8;  // keys per thread of the SMALL selection
 
 // SMALL: S <= kFusedKeys * kFusedBlock, so the selection keeps the scores as
 // register keys with a first-digit histogram counted during the stream.
+// At least six waves per SIMD (at most 80 VGPRs): three workgroups of eight
+// waves share a CU when the rows outnumber the CUs.
 template <class E, int D, int LPS, bool SMALL, bool STEP>
-__global__ void __launch_bounds__(kFusedBlock) fused_kernel(FusedArgs a) {
+__global__ void __launch_bounds__(kFusedBlock, 6) fused_kernel(FusedArgs a) {
   using T = typename E::T;
   constexpr int NT = kFusedBlock;
   using Gm = Geo<E, D, NT>;
@@ -93,7 +95,10 @@ __global__ void __launch_bounds__(kFusedBlock) fused_kernel(FusedArgs a) {
 
   // 1. q' = q . P[g] (and, for STEP, k' = k_new . P[g] in float64): thread
   //    (cq, rb) adds rows [rb*RB, rb*RB + RB) for columns 4*cq .. 4*cq + 3,
-  //    read as 16-byte chunks; the NRB partials are added through LDS.
+  //    read as 16-byte chunks; the NRB partials are added through LDS.  The
+  //    new value row is loaded together with the query.
+  T vn{};
+  if (STEP && threadIdx.x < D) vn = static_cast<const T*>(a.v_new)[bgo * D + threadIdx.x];
   if (a.rope.base == 0.0) {
     if (threadIdx.x < D) {
       rin[threadIdx.x] = ld_elem<E>(static_cast<const T*>(a.q), row * D + threadIdx.x);
@@ -120,6 +125,7 @@ __global__ void __launch_bounds__(kFusedBlock) fused_kernel(FusedArgs a) {
       }
     }
   }
+  if (STEP && threadIdx.x < D) vslot[threadIdx.x] = vn;
   __syncthreads();
   if (threadIdx.x < kBlock) {
     const int cq = threadIdx.x % CQ, rb = threadIdx.x / CQ;
@@ -160,10 +166,7 @@ __global__ void __launch_bounds__(kFusedBlock) fused_kernel(FusedArgs a) {
       double x = 0.0;
 #pragma unroll
       for (int pp = 0; pp < NRB; ++pp) x += sc.rot.k[STEP ? pp : 0][col];
-      const T st = round_store<E>(x);
-      const T vn = static_cast<const T*>(a.v_new)[bgo * D + col];
-      kslot[col] = st;
-      vslot[col] = vn;
+      kslot[col] = round_store<E>(x);
     }
   }
   __syncthreads();
