@@ -21,6 +21,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -35,10 +36,14 @@ KERNEL_SOURCES = ["device.hpp", "select.hpp", "attend.hpp", "score.hpp", "fused_
 
 
 def kernel_source_hash() -> str:
+    """Hash of the fused kernel's sources with comments and layout removed, so
+    that a comment edit does not retire the recorded traffic counters but any
+    change of code does."""
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "sparse_attention_decode_loki_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "sparse_attention_decode_loki_amd", "csrc", f)) as fh:
+            text = re.sub(r"//[^\n]*", "", fh.read())
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -8,10 +8,11 @@
 // The STEP variant is one step of a generation loop: it also appends the
 // step's new key/value at position pos (the key rotated into the PCA basis in
 // float64 and rounded once, as loki_kv_append does) and decodes over the
-// pos + 1 tokens.  The new token's row is never read back from the cache: its
-// score and its rows come from LDS, so workgroups of the same KV head never
-// read a slot another workgroup is writing.  Only the workgroup of the first
-// query head of each KV head writes the slot.
+// pos + 1 tokens.  No workgroup uses the new token's row from the cache: the
+// stream's load of that slot is discarded, and the token's score and rows come
+// from LDS, so it does not matter when the writing workgroup's stores land.
+// Only the workgroup of the first query head of each KV head writes the slot,
+// after its gather.
 #include "attend.hpp"
 #include "launch.hpp"
 #include "score.hpp"
