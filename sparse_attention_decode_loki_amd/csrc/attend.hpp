@@ -190,7 +190,9 @@ __device__ __forceinline__ void merge_groups(const Acc<E::VEC> (&st)[NH],
   // PT threads share one output (groups split PT ways, partial sums added
   // across neighbouring lanes) when the workgroup has that many threads per
   // output; otherwise each output is one thread's loop over all groups.
-  constexpr int PT = (NT >= 4 * NH * D && NG % 4 == 0) ? 4 : (NT >= 2 * NH * D && NG % 2 == 0) ? 2 : 1;
+  constexpr int PT = (NT >= 4 * NH * D && NG % 4 == 0)   ? 4
+                     : (NT >= 2 * NH * D && NG % 2 == 0) ? 2
+                                                         : 1;
   if constexpr (PT > 1) {
     constexpr int GP = NG / PT;
     const int o = threadIdx.x / PT, part = threadIdx.x % PT;
