@@ -191,7 +191,7 @@ __global__ void __launch_bounds__(kFusedBlock, 6) fused_kernel(FusedArgs a) {
       for (int v = 0; v < VEC; ++v) snew = fmaf(qf[0][v], x[v], snew);
       snew = group_sum<LPS>(snew);
     }
-    constexpr int US = 4;  // 16-byte slab loads in flight per lane (8 waves)
+    constexpr int US = 3;  // 16-byte slab loads in flight per lane (8 waves)
     Chunk c[US];
     score_first<E, LPS, US, NT>(sl, d, 0, S, c);
     // the selection's first radix digit is counted here, under the stream
