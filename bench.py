@@ -80,6 +80,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--settle", type=int, default=1000,
+                    help="untimed launches of the step before the warmup steps, so that the GPU "
+                         "has left its idle clocks when the warmup starts (0: none)")
     ap.add_argument("--config", default="l2_13b_run")
     ap.add_argument("--layers", type=int, default=0,
                     help="cache copies cycled; 0: at least 4 and at least 1 GiB in all, "
@@ -210,6 +213,8 @@ def main():
         t1 = time.perf_counter()
         return (t1 - t0) * 1e3 / n, e0.elapsed_time(e1) / n
 
+    for i in range(args.settle):
+        step(i)
     for i in range(args.warmup):
         step(i)
     ms_per_step, step_avg_ms = timed(lambda i: step(args.warmup + i), args.steps)
@@ -254,6 +259,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_launches": args.settle,
         "ms_per_step": ms_per_step,
         "higher_is_better": True,
         "scaling": "weak",
