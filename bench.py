@@ -35,6 +35,12 @@ PEAK_HBM_GBS = 8000.0
 KERNEL_SOURCES = ["device.hpp", "select.hpp", "attend.hpp", "score.hpp", "fused_kernels.hip"]
 
 
+def code_tokens(text: str) -> str:
+    """Source text without // comments, with every run of whitespace made one
+    space."""
+    return " ".join(re.sub(r"//[^\n]*", "", text).split())
+
+
 def kernel_source_hash() -> str:
     """Hash of the fused kernel's sources with comments and layout removed, so
     that a comment edit does not retire the recorded traffic counters but any
@@ -42,8 +48,7 @@ def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
         with open(os.path.join(ROOT, "sparse_attention_decode_loki_amd", "csrc", f)) as fh:
-            text = re.sub(r"//[^\n]*", "", fh.read())
-        h.update(" ".join(text.split()).encode())
+            h.update(code_tokens(fh.read()).encode())
     return h.hexdigest()[:16]
 
 
