@@ -433,6 +433,9 @@ STEP_CASES = {
     "step_f32": synth.custom("step_f32", 303, B=1, Hq=2, Hkv=2, D=64, d=16, S=300, dtype="f32",
                              tau=8.0),
     "step_first": synth.custom("step_first", 304, B=2, Hq=2, Hkv=2, S=1),
+    # the benchmark's step at full size (B=16, 40 heads, S=3584, k=896): every
+    # (sequence, head) pair and every written slot against the oracle
+    "step_l2_13b_full": synth.WORKLOADS["l2_13b_run"],
 }
 
 
