@@ -21,6 +21,8 @@ CASES = {
     "rope_f32": (synth.custom("rope_f32", 603, B=1, Hq=2, Hkv=2, D=64, d=16, S=300, dtype="f32",
                               tau=8.0), 300, 310, 10000.0),
     "rope_long": (synth.custom("rope_long", 604, B=1, Hq=4, Hkv=2, S=5000), 5000, 5000, 10000.0),
+    # the benchmark's --rope-base 10000 shape at full size (13B, S=3584)
+    "rope_l2_13b_full": (synth.WORKLOADS["l2_13b_run"], 3584, 3584, 10000.0),
 }
 _cache = {}
 
