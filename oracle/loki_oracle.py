@@ -287,9 +287,11 @@ def decode(q, kslab, krest, v, P, k, dtype, S=None, heads=None, rope=None):
     return out, idx, s
 
 
-def attend_indices(q, kslab, krest, v, P, idx, dtype, heads=None):
+def attend_indices(q, kslab, krest, v, P, idx, dtype, heads=None, rope=None):
     """Exact attention over a given ascending index set per (b, h): the
-    oracle of loki_attend_indices.  idx [B, Hq, k]."""
+    oracle of loki_attend_indices, and of a decode's output over whatever set
+    that decode selected.  idx [B, Hq, k]; rope: optional (base, q_pos), the
+    query's embedding as in decode() (reading R)."""
     B, Hq, D = q.shape
     Hkv = kslab.shape[1]
     out = np.full((B, Hq, D), np.nan)
@@ -297,7 +299,10 @@ def attend_indices(q, kslab, krest, v, P, idx, dtype, heads=None):
     for b, h in pairs:
         g = kv_head(h, Hq, Hkv)
         sel = np.asarray(idx[b, h], dtype=np.int64)
-        o, _ = attend(to_f64(q[b, h], dtype), np.asarray(P[g], np.float64),
+        qv = to_f64(q[b, h], dtype)
+        if rope is not None:
+            qv = rope_embed(qv, rope[1], rope[0])
+        o, _ = attend(qv, np.asarray(P[g], np.float64),
                       to_f64(kslab[b, g], dtype), to_f64(krest[b, g], dtype),
                       to_f64(v[b, g], dtype), sel)
         out[b, h] = o

@@ -432,3 +432,113 @@ def test_rope_decode_full_budget_is_dense_attention_on_embedded_keys():
     plain, _, _ = oracle.decode(q[None, None], slab[None, None], rest[None, None],
                                 vv[None, None], P[None], S, "f64")
     assert not np.allclose(plain[0, 0], want, atol=1e-6)
+
+
+# ------------------------------------- given-index and dense attention, GQA --
+# Brute force written out with Python floats from the unrotated keys: for an
+# orthogonal P, (q.P).(k.P) = q.k, so exact attention over any token set can be
+# formed without the basis.  B > 1 and G = Hq/Hkv = 3 make a wrong KV-head
+# mapping (h mod Hkv), a per-query-head basis (P[h]) or a dropped rest block
+# disagree with it.
+
+def _gqa_cache(seed, B=2, Hq=6, Hkv=2, S=24, D=8, d=3, S_max=None):
+    rng = np.random.default_rng(seed)
+    S_max = S if S_max is None else S_max
+    P = np.stack([_haar(rng, D) for _ in range(Hkv)])
+    q = rng.standard_normal((B, Hq, D))
+    K = rng.standard_normal((B, Hkv, S_max, D))
+    V = rng.standard_normal((B, Hkv, S_max, D))
+    slab = np.empty((B, Hkv, S_max, d))
+    rest = np.empty((B, Hkv, S_max, D - d))
+    for g in range(Hkv):
+        slab[:, g], rest[:, g], _ = oracle.append(K[:, g], V[:, g], P[g], d, "f64")
+    return q, P, K, V, slab, rest
+
+
+def _brute_attention(qv, K, V, sel):
+    """softmax over sel of q.K_j / sqrt(D), then the weighted sum of V rows."""
+    D = len(qv)
+    e = [sum(float(qv[m]) * float(K[j][m]) for m in range(D)) / math.sqrt(D) for j in sel]
+    top = max(e)
+    z = [math.exp(x - top) for x in e]
+    tot = sum(z)
+    return [sum(z[i] * float(V[j][c]) for i, j in enumerate(sel)) / tot for c in range(D)]
+
+
+def test_attend_indices_gqa_batch_brute_force():
+    B, Hq, Hkv, S, D = 2, 6, 2, 24, 8
+    q, P, K, V, slab, rest = _gqa_cache(21, B, Hq, Hkv, S, D)
+    rng = np.random.default_rng(22)
+    k = 7
+    idx = np.stack([np.stack([np.sort(rng.choice(S, k, replace=False)) for _ in range(Hq)])
+                    for _ in range(B)])
+    out = oracle.attend_indices(q, slab, rest, V, P, idx, "f64")
+    for b in range(B):
+        for h in range(Hq):
+            g = h // (Hq // Hkv)  # heads 0-2 read KV head 0, heads 3-5 KV head 1
+            want = _brute_attention(q[b, h], K[b, g], V[b, g], idx[b, h].tolist())
+            assert np.allclose(out[b, h], want, rtol=0, atol=1e-12), (b, h)
+
+
+def test_attend_indices_single_token_returns_its_value_row():
+    B, Hq, Hkv, S, D = 2, 6, 2, 24, 8
+    q, P, K, V, slab, rest = _gqa_cache(23, B, Hq, Hkv, S, D)
+    idx = np.array([[[(5 * h + 3 * b) % S] for h in range(Hq)] for b in range(B)])
+    out = oracle.attend_indices(q, slab, rest, V, P, idx, "f64")
+    for b in range(B):
+        for h in range(Hq):
+            assert np.array_equal(out[b, h], V[b, h // 3, idx[b, h, 0]])
+
+
+def test_dense_decode_gqa_batch_brute_force_on_original_keys():
+    # S < S_max: the positions past S hold huge values that must not be read
+    B, Hq, Hkv, S, S_max, D, d = 2, 6, 2, 20, 26, 8, 3
+    q, P, K, V, slab, rest = _gqa_cache(24, B, Hq, Hkv, S, D, d, S_max)
+    slab[:, :, S:] = 1e6
+    rest[:, :, S:] = 1e6
+    V[:, :, S:] = 1e6
+    out = oracle.dense_decode(q, slab, rest, V, P, "f64", S=S)
+    for b in range(B):
+        for h in range(Hq):
+            g = h // (Hq // Hkv)
+            want = _brute_attention(q[b, h], K[b, g], V[b, g], list(range(S)))
+            assert np.allclose(out[b, h], want, rtol=0, atol=1e-12), (b, h)
+
+
+def test_dense_decode_equals_full_budget_decode_for_any_slab_width():
+    # dense attention is Loki with every token kept, whatever d is
+    B, Hq, Hkv, S, D = 2, 6, 2, 16, 8
+    for d in (1, 3, 8):
+        q, P, K, V, slab, rest = _gqa_cache(25 + d, B, Hq, Hkv, S, D, d)
+        dense = oracle.dense_decode(q, slab, rest, V, P, "f64")
+        full, idx, _ = oracle.decode(q, slab, rest, V, P, S, "f64")
+        assert np.array_equal(idx, np.broadcast_to(np.arange(S), idx.shape))
+        assert np.allclose(dense, full, rtol=0, atol=1e-13)
+
+
+def test_rope_attend_indices_brute_force_on_embedded_keys():
+    # a subset of tokens with the query embedded at q_pos: brute force over the
+    # embedded (unrotated) keys; without the embedding the result differs
+    rng = np.random.default_rng(31)
+    B, Hq, Hkv, S, D, d, base, m = 2, 4, 2, 18, 8, 3, 10000.0, 40
+    P = np.stack([_haar(rng, D) for _ in range(Hkv)])
+    q = rng.standard_normal((B, Hq, D))
+    K = rng.standard_normal((B, Hkv, S, D))
+    V = rng.standard_normal((B, Hkv, S, D))
+    slab = np.empty((B, Hkv, S, d))
+    rest = np.empty((B, Hkv, S, D - d))
+    for g in range(Hkv):
+        slab[:, g], rest[:, g], _ = oracle.append(K[:, g], V[:, g], P[g], d, "f64",
+                                                  rope_base=base, pos=0)
+    idx = np.stack([np.stack([np.sort(rng.choice(S, 6, replace=False)) for _ in range(Hq)])
+                    for _ in range(B)])
+    out = oracle.attend_indices(q, slab, rest, V, P, idx, "f64", rope=(base, m))
+    plain = oracle.attend_indices(q, slab, rest, V, P, idx, "f64")
+    for b in range(B):
+        for h in range(Hq):
+            g = h // (Hq // Hkv)
+            Ke = [oracle.rope_embed(K[b, g, j], j, base) for j in range(S)]
+            want = _brute_attention(oracle.rope_embed(q[b, h], m, base), Ke, V[b, g],
+                                    idx[b, h].tolist())
+            assert np.allclose(out[b, h], want, rtol=0, atol=1e-12), (b, h)
+            assert not np.allclose(plain[b, h], want, atol=1e-6)
