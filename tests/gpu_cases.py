@@ -114,10 +114,30 @@ def out_error(dtype: str, got: np.ndarray, ref: np.ndarray) -> float:
 TOL = {"f32": 1e-5, "bf16": 2e-3}
 
 
-def check_decode(dtype, k, out, idx, ref_out, ref_idx, ref_s, pairs, max_swaps=None):
+@dataclass
+class OracleSrc:
+    """The oracle-side inputs of a decode (storage form), from which the
+    oracle's attention over any index set is formed."""
+    q: np.ndarray
+    slab: np.ndarray
+    rest: np.ndarray
+    v: np.ndarray
+    P: np.ndarray
+    rope: tuple | None = None   # (base, q_pos) for the RoPE variant
+
+
+def src_of(c: Case, rope=None) -> OracleSrc:
+    return OracleSrc(c.q, c.slab, c.rest, c.v, c.P, rope)
+
+
+def check_decode(dtype, k, out, idx, ref_out, ref_idx, ref_s, pairs, src: OracleSrc,
+                 max_swaps=None):
     """Index sets: equal to the oracle's whenever the relative gap at the k-th
-    place exceeds 1e-4; otherwise a valid choice inside the tie band.
-    Outputs: compared with the oracle wherever the sets agree.
+    place exceeds 1e-4; otherwise a valid choice inside the tie band, and at
+    most 1 in 100 pairs (at least one) may differ from the oracle's set.
+    Outputs: every pair is compared with the oracle's exact attention over the
+    GPU's own index set (the oracle's decode output where the sets agree,
+    oracle.attend_indices over the GPU's set where they do not).
     Returns (n_band, n_swapped, worst_output_error)."""
     n_band = n_swap = 0
     worst = 0.0
@@ -133,11 +153,14 @@ def check_decode(dtype, k, out, idx, ref_out, ref_idx, ref_s, pairs, max_swaps=N
             n_band += 1
             assert oracle.valid_in_band(s, kk, gi), f"invalid near-tie set at (b={b}, h={h})"
         if np.array_equal(gi, ref_idx[b, h]):
-            e = out_error(dtype, out[b, h], ref_out[b, h])
-            worst = max(worst, e)
-            assert e <= TOL[dtype], f"output error {e:.3g} at (b={b}, h={h})"
+            ref = ref_out[b, h]
         else:
             n_swap += 1
+            ref = oracle.attend_indices(src.q, src.slab, src.rest, src.v, src.P, idx, dtype,
+                                        heads=[(b, h)], rope=src.rope)[b, h]
+        e = out_error(dtype, out[b, h], ref)
+        worst = max(worst, e)
+        assert e <= TOL[dtype], f"output error {e:.3g} at (b={b}, h={h})"
     limit = max(1, len(pairs) // 100) if max_swaps is None else max_swaps
     assert n_swap <= limit, f"{n_swap} near-tie swaps in {len(pairs)} head-queries"
     return n_band, n_swap, worst

@@ -12,8 +12,8 @@ import pytest
 
 import oracle
 import synth
-from gpu_cases import (TOL, all_pairs, check_decode, device_cache, make_case, out_error,
-                       to_dev, to_host, ulp_diff_bf16, ulp_diff_f32)
+from gpu_cases import (TOL, OracleSrc, all_pairs, check_decode, device_cache, make_case,
+                       out_error, src_of, to_dev, to_host, ulp_diff_bf16, ulp_diff_f32)
 
 pytestmark = pytest.mark.gpu
 
@@ -267,7 +267,7 @@ def test_decode_matches_oracle(lib, name, path):
     out, idx = out.cpu().numpy(), idx.cpu().numpy()
     ref_out, ref_idx, ref_s = oracle.decode(c.q, c.slab, c.rest, c.v, c.P, c.k, c.w.dtype, S=c.S)
     assert idx.dtype == np.int32 and idx.shape == (c.w.B, c.w.Hq, kk)
-    check_decode(c.w.dtype, c.k, out, idx, ref_out, ref_idx, ref_s, all_pairs(c.w))
+    check_decode(c.w.dtype, c.k, out, idx, ref_out, ref_idx, ref_s, all_pairs(c.w), src_of(c))
 
 
 @pytest.mark.parametrize("k", [1, 2, 499, 999, 1000, 5000])
@@ -278,7 +278,7 @@ def test_decode_budget_edges(lib, k):
     for path in (1, 2, 3):
         out, idx = lib.decode(_q(c), cache, _P(c), k, path=path)
         check_decode(c.w.dtype, k, out.cpu().numpy(), idx.cpu().numpy(), ref_out, ref_idx, ref_s,
-                     all_pairs(c.w))
+                     all_pairs(c.w), src_of(c))
 
 
 def test_decode_shorter_S_than_filled(lib):
@@ -290,7 +290,7 @@ def test_decode_shorter_S_than_filled(lib):
     for path in (1, 2, 3):
         out, idx = lib.decode(_q(c), cache, _P(c), 300, S=S, path=path)
         check_decode(c.w.dtype, 300, out.cpu().numpy(), idx.cpu().numpy(), ref_out, ref_idx,
-                     ref_s, all_pairs(c.w))
+                     ref_s, all_pairs(c.w), src_of(c))
 
 
 def test_decode_deterministic_and_paths_agree(lib):
@@ -389,7 +389,7 @@ def test_decode_at_size_limits(lib, name):
     for path in paths:
         out, idx = lib.decode(_q(c), cache, _P(c), c.k, path=path)
         check_decode(w.dtype, c.k, out.cpu().numpy(), idx.cpu().numpy(), ref_out, ref_idx, ref_s,
-                     all_pairs(w))
+                     all_pairs(w), src_of(c))
     if name == "union_max_S":
         assert lib.decode_path(1, 4, 1, 128, 32, (1 << 17) + 1, c.k, "bf16", 0) == 2
     else:
@@ -418,7 +418,7 @@ def test_full_size_decode_sampled(lib, name, path):
     out, idx = out.cpu().numpy(), idx.cpu().numpy()
     pairs = all_pairs(w)
     ref_out, ref_idx, ref_s = oracle.decode(c.q, c.slab, c.rest, c.v, c.P, w.k, w.dtype, heads=pairs)
-    check_decode(w.dtype, w.k, out, idx, ref_out, ref_idx, ref_s, pairs)
+    check_decode(w.dtype, w.k, out, idx, ref_out, ref_idx, ref_s, pairs, src_of(c))
     # every row: k distinct ascending ids in range, finite outputs
     assert np.all(np.diff(idx.astype(np.int64), axis=-1) > 0)
     assert idx.min() >= 0 and idx.max() < w.S
@@ -501,7 +501,7 @@ def test_decode_step_matches_oracle(lib, name, path):
     ref_out, ref_idx, ref_s = oracle.decode(q, full["slab"], full["rest"], full["v"], P, k,
                                             w.dtype, S=S)
     check_decode(w.dtype, k, out.cpu().numpy(), idx.cpu().numpy(), ref_out, ref_idx, ref_s,
-                 all_pairs(w))
+                 all_pairs(w), OracleSrc(q, full["slab"], full["rest"], full["v"], P))
 
 
 def test_decode_steps_in_sequence_paths_agree(lib):
@@ -576,7 +576,7 @@ def test_split_paths_ignore_stale_workspace(lib, path):
     import torch
     c = case("sinks")
     cache = device_cache(lib, c)
-    ws = lib.alloc_workspace(c.w.B, c.w.Hq, c.w.D, c.S_max, c.k, torch.device("cuda"))
+    ws = lib.alloc_workspace(c.w.B, c.w.Hq, c.S_max, c.w.D, c.k, torch.device("cuda"))
     res = []
     for fill in (0xFF, 0x00):
         ws.fill_(fill)
@@ -598,7 +598,7 @@ def test_per_layer_slab_width(lib):
         out, idx = lib.decode(_q(c), cache, _P(c), c.k)
         ref_out, ref_idx, ref_s = oracle.decode(c.q, c.slab, c.rest, c.v, c.P, c.k, w.dtype, S=c.S)
         check_decode(w.dtype, c.k, out.cpu().numpy(), idx.cpu().numpy(), ref_out, ref_idx, ref_s,
-                     all_pairs(w))
+                     all_pairs(w), src_of(c))
 
 
 # ------------------------------------------------------------ graph capture --
@@ -613,7 +613,7 @@ def test_decode_replays_from_a_captured_graph(lib, path):
     cache = device_cache(lib, c)
     q = _q(c)
     P = _P(c)
-    ws = lib.alloc_workspace(c.w.B, c.w.Hq, c.w.D, c.S_max, c.k, torch.device("cuda"))
+    ws = lib.alloc_workspace(c.w.B, c.w.Hq, c.S_max, c.w.D, c.k, torch.device("cuda"))
     out = torch.empty((c.w.B, c.w.Hq, c.w.D), dtype=torch.float32, device="cuda")
     idx = torch.empty((c.w.B, c.w.Hq, c.k), dtype=torch.int32, device="cuda")
     ref_out, ref_idx = lib.decode(q, cache, P, c.k, workspace=ws, path=path)

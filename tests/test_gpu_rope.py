@@ -9,8 +9,8 @@ import pytest
 
 import oracle
 import synth
-from gpu_cases import (TOL, all_pairs, basis, check_decode, device_cache, make_case, out_error,
-                       to_dev, to_host, ulp_diff_bf16, ulp_diff_f32)
+from gpu_cases import (TOL, OracleSrc, all_pairs, basis, check_decode, device_cache, make_case,
+                       out_error, src_of, to_dev, to_host, ulp_diff_bf16, ulp_diff_f32)
 
 pytestmark = pytest.mark.gpu
 
@@ -55,7 +55,7 @@ def test_rope_decode_matches_oracle(lib, name):
         for path in _paths(c.w):
             out, idx = lib.decode(q, cache, P, c.k, path=path, rope_base=base, q_pos=q_pos)
             check_decode(c.w.dtype, c.k, out.cpu().numpy(), idx.cpu().numpy(), ref_out, ref_idx,
-                         ref_s, all_pairs(c.w))
+                         ref_s, all_pairs(c.w), src_of(c, (base, q_pos)))
 
 
 @pytest.mark.parametrize("name", sorted(CASES))
@@ -141,7 +141,8 @@ def test_rope_decode_step_matches_oracle(lib, path):
         ref_out, ref_idx, ref_s = oracle.decode(q, full["slab"], full["rest"], full["v"], c.P, k,
                                                 w.dtype, S=pos + 1, rope=(base, pos))
         check_decode(w.dtype, k, out.cpu().numpy(), idx.cpu().numpy(), ref_out, ref_idx, ref_s,
-                     all_pairs(w))
+                     all_pairs(w),
+                     OracleSrc(q, full["slab"], full["rest"], full["v"], c.P, (base, pos)))
 
 
 def test_rope_pre_and_post_rotary_bases_both_decode(lib):
@@ -151,9 +152,11 @@ def test_rope_pre_and_post_rotary_bases_both_decode(lib):
     import torch
     w, S, S_max, base = CASES["rope_gqa4"]
     Ks = [synth.calib_keys(w, g) for g in range(w.Hkv)]
-    pre = np.stack([lib.calibrate(K.astype(np.float32))[0] for K in Ks])
-    post = np.stack([lib.calibrate(oracle.rope_embed(K, np.arange(K.shape[0]), base)
-                                   .astype(np.float32))[0] for K in Ks])
+    # both bases from the oracle's calibration: no library output enters the
+    # oracle side
+    pre = np.stack([oracle.calibrate(K)[0] for K in Ks]).astype(np.float32)
+    post = np.stack([oracle.calibrate(oracle.rope_embed(K, np.arange(K.shape[0]), base))[0]
+                     for K in Ks]).astype(np.float32)
     assert not np.allclose(pre, post, atol=1e-3)
     Kr, Vr = synth.raw_cache(w, S)
     q = synth.queries(w)
@@ -175,7 +178,7 @@ def test_rope_pre_and_post_rotary_bases_both_decode(lib):
         ref_out, ref_idx, ref_s = oracle.decode(q, slab, rest, vv, P, w.k, w.dtype, S=S,
                                                 rope=(base, S - 1))
         check_decode(w.dtype, w.k, out.cpu().numpy(), idx.cpu().numpy(), ref_out, ref_idx, ref_s,
-                     all_pairs(w))
+                     all_pairs(w), OracleSrc(q, slab, rest, vv, P, (base, S - 1)))
 
 
 @pytest.mark.parametrize("path", [1, 2, 3], ids=["fused", "split", "union"])
@@ -194,7 +197,7 @@ def test_rope_decode_step_replays_from_a_captured_graph(lib, path):
     kd, vd = to_dev(kn[:, :, 0], w.dtype), to_dev(vn[:, :, 0], w.dtype)
     pos = S - 1
     k = w.k_at(pos + 1)
-    ws = lib.alloc_workspace(w.B, w.Hq, w.D, c.S_max, k, torch.device("cuda"))
+    ws = lib.alloc_workspace(w.B, w.Hq, c.S_max, w.D, k, torch.device("cuda"))
     ref_cache = device_cache(lib, c)
     ref_out, ref_idx = lib.decode_step(q, kd, vd, ref_cache, P, k, pos=pos, workspace=ws, path=path,
                                        rope_base=base)
