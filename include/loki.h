@@ -93,7 +93,7 @@ const char* loki_status_string(int status);
 
 /* ABI revision of this header, incremented on any signature change; a caller
  * compares it with loki_abi_version() of the library it loaded. */
-#define LOKI_ABI_VERSION 3
+#define LOKI_ABI_VERSION 4
 
 /* ABI revision the library was built with (LOKI_ABI_VERSION of its header). */
 int loki_abi_version(void);
@@ -124,8 +124,10 @@ int loki_kv_append(const void* k_new, const void* v_new, const float* P,
                    int32_t pos, int32_t T, int32_t dtype, void* stream);
 
 /* Bytes of device workspace that every decode-family entry point below needs
- * for these sizes (any S <= S_max, any k <= k_max).  Always a multiple of 256. */
-size_t loki_decode_workspace_size(int32_t B, int32_t Hq, int32_t D, int32_t S_max, int32_t k_max);
+ * for these sizes (any S <= S_max, any k <= k_max, any Hkv dividing Hq).
+ * Always a multiple of 256; 0 when B, Hq, S_max or D is not positive.
+ * (ABI 4 put S_max before D; ABI 3 took D first.) */
+size_t loki_decode_workspace_size(int32_t B, int32_t Hq, int32_t S_max, int32_t D, int32_t k_max);
 
 /* One Loki decode step ("Approach"; "Abstract": ranking and selection by
  * attention scores computed in the low-dimensional space; summary line:
@@ -138,7 +140,7 @@ size_t loki_decode_workspace_size(int32_t B, int32_t Hq, int32_t D, int32_t S_ma
  *   out = sum_{j in I} softmax_I(e)_j * v[j]
  * Ranking scores are float32 sums of the stored keys times q' (float32);
  * accumulation is float32 throughout.  workspace: device, 16-byte aligned,
- * >= loki_decode_workspace_size(B, Hq, D, S_max, k) bytes; the fused path
+ * >= loki_decode_workspace_size(B, Hq, S_max, D, k) bytes; the fused path
  * does not touch it (loki_decode_ex with LOKI_PATH_FUSED accepts NULL). */
 int loki_decode(const void* q, const void* k_slab, const void* k_rest, const void* v,
                 const float* P, int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t d,

@@ -120,15 +120,80 @@ def _stream(t):
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
 
-def _need(t, name, dtype=None, cuda=True):
+def _need(t, name, dtype=None, shape=None, device=None):
+    """Reject a tensor the library could not use safely: the C ABI sees only
+    pointers, so a wrong extent would become an out-of-bounds device access
+    rather than an error.  Checks shape, dtype, contiguity and device."""
     if t is None:
         raise ValueError(f"{name} is required")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
-    if cuda and not t.is_cuda:
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the cache on {device}")
+
+
+def _on_gpu(t, name):
+    """Last check of every call: its tensors (all on one device by then) are
+    in device memory."""
+    if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
-    if dtype is not None and t.dtype != dtype:
-        raise ValueError(f"{name} must be {dtype}")
+
+
+def _need_q(q, cache):
+    """q [cache.B, Hq, cache.D] in the cache dtype, Hq a multiple of cache.Hkv.
+    Returns (B, Hq, D)."""
+    if q is None or q.dim() != 3:
+        raise ValueError("q must be [B, Hq, D]")
+    B, Hq, D = q.shape
+    if Hq < 1 or Hq % cache.Hkv != 0:
+        raise ValueError(f"q has {Hq} heads, not a multiple of the cache's {cache.Hkv} KV heads")
+    _need(q, "q", cache.dtype, (cache.B, Hq, cache.D), cache.device)
+    return B, Hq, D
+
+
+def _need_P(P, cache):
+    _need(P, "P", _torch().float32, (cache.Hkv, cache.D, cache.D), cache.device)
+
+
+def _need_new(k_new, v_new, cache, step: bool):
+    """New keys/values: [B, Hkv, D] for a decode step, [B, Hkv, T, D] for an
+    append.  Returns T."""
+    if k_new is None or k_new.dim() != (3 if step else 4):
+        raise ValueError("k_new must be " + ("[B, Hkv, D]" if step else "[B, Hkv, T, D]"))
+    shape = (cache.B, cache.Hkv, cache.D) if step else (cache.B, cache.Hkv, k_new.shape[2], cache.D)
+    _need(k_new, "k_new", cache.dtype, shape, cache.device)
+    _need(v_new, "v_new", cache.dtype, shape, cache.device)
+    return 1 if step else shape[2]
+
+
+def _out(out, shape, device, name="out"):
+    torch = _torch()
+    if out is None:
+        return torch.empty(shape, dtype=torch.float32, device=device)
+    _need(out, name, torch.float32, shape, device)
+    return out
+
+
+def _idx(idx, shape, device):
+    torch = _torch()
+    if idx is None:
+        return torch.empty(shape, dtype=torch.int32, device=device)
+    _need(idx, "idx", torch.int32, shape, device)
+    return idx
+
+
+def _ws(workspace, device):
+    if workspace is not None:
+        _need(workspace, "workspace", device=device)
+    return workspace
+
+
+def _ws_bytes(workspace) -> int:
+    return 0 if workspace is None else workspace.numel() * workspace.element_size()
 
 
 class KVCache:
@@ -145,6 +210,10 @@ class KVCache:
                        if d < D else None)
         self.v = torch.zeros((B, Hkv, S_max, D), dtype=dtype, device=device)
         self.length = 0
+
+    @property
+    def device(self):
+        return self.v.device
 
 
 def calibrate(keys: np.ndarray):
@@ -166,13 +235,13 @@ def append(cache: KVCache, k_new, v_new, P, pos: int | None = None,
     rope_base, each key is first given the rotary embedding of its position
     (loki_kv_append_rope)."""
     lib = load()
-    _need(k_new, "k_new", cache.dtype)
-    _need(v_new, "v_new", cache.dtype)
-    _need(P, "P", _torch().float32)
-    B, Hkv, T, D = k_new.shape
+    T = _need_new(k_new, v_new, cache, step=False)
+    _need_P(P, cache)
+    _on_gpu(k_new, "k_new")
     at = cache.length if pos is None else pos
     args = (_ptr(k_new), _ptr(v_new), _ptr(P), _ptr(cache.k_slab), _ptr(cache.k_rest),
-            _ptr(cache.v), B, Hkv, D, cache.d, cache.S_max, at, T, _dtype_code(k_new))
+            _ptr(cache.v), cache.B, cache.Hkv, cache.D, cache.d, cache.S_max, at, T,
+            _dtype_code(k_new))
     if rope_base is None:
         st = lib.loki_kv_append(*args, _stream(k_new))
     else:
@@ -182,14 +251,35 @@ def append(cache: KVCache, k_new, v_new, P, pos: int | None = None,
         cache.length = max(cache.length, at + T)
 
 
-def workspace_size(B, Hq, D, S_max, k_max) -> int:
-    return int(load().loki_decode_workspace_size(B, Hq, D, S_max, k_max))
+def workspace_size(B, Hq, S_max, D, k_max) -> int:
+    """loki_decode_workspace_size: bytes of device workspace (same argument
+    order as the C call)."""
+    return int(load().loki_decode_workspace_size(B, Hq, S_max, D, k_max))
 
 
-def alloc_workspace(B, Hq, D, S_max, k_max, device="cuda"):
+def alloc_workspace(B, Hq, S_max, D, k_max, device="cuda"):
     torch = _torch()
-    n = max(workspace_size(B, Hq, D, S_max, k_max), 256)
+    n = max(workspace_size(B, Hq, S_max, D, k_max), 256)
     return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def _decode_args(q, cache, P, k, S, out, idx, workspace, path):
+    """Checked and allocated arguments shared by decode and DecodePlan."""
+    B, Hq, D = _need_q(q, cache)
+    _need_P(P, cache)
+    S = cache.length if S is None else S
+    kk = min(k, S)
+    dev = cache.device
+    out = _out(out, (B, Hq, D), dev)
+    idx = _idx(idx, (B, Hq, kk), dev)
+    workspace = _ws(workspace, dev)
+    _on_gpu(q, "q")
+    if workspace is None and path != PATH_FUSED:
+        workspace = alloc_workspace(B, Hq, cache.S_max, D, kk, dev)
+    head = (_ptr(q), _ptr(cache.k_slab), _ptr(cache.k_rest), _ptr(cache.v), _ptr(P),
+            B, Hq, cache.Hkv, D, cache.d, S, cache.S_max, k, _dtype_code(q))
+    tail = (_ptr(out), _ptr(idx), _ptr(workspace), _ws_bytes(workspace), path, _stream(q))
+    return S, out, idx, workspace, head, tail
 
 
 def decode(q, cache: KVCache, P, k: int, S: int | None = None, out=None, idx=None,
@@ -199,23 +289,8 @@ def decode(q, cache: KVCache, P, k: int, S: int | None = None, out=None, idx=Non
     idx [B, Hq, min(k, S)] int32 ascending).  With rope_base the query is
     given the rotary embedding of position q_pos (default S - 1) first
     (loki_decode_rope; the cache must hold embedded keys)."""
-    torch = _torch()
     lib = load()
-    _need(q, "q", cache.dtype)
-    _need(P, "P", torch.float32)
-    B, Hq, D = q.shape
-    S = cache.length if S is None else S
-    kk = min(k, S)
-    if out is None:
-        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
-    if idx is None:
-        idx = torch.empty((B, Hq, kk), dtype=torch.int32, device=q.device)
-    if workspace is None and path != PATH_FUSED:
-        workspace = alloc_workspace(B, Hq, D, cache.S_max, kk, q.device)
-    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    head = (_ptr(q), _ptr(cache.k_slab), _ptr(cache.k_rest), _ptr(cache.v), _ptr(P),
-            B, Hq, cache.Hkv, D, cache.d, S, cache.S_max, k, _dtype_code(q))
-    tail = (_ptr(out), _ptr(idx), _ptr(workspace), wsb, path, _stream(q))
+    S, out, idx, _ws_keep, head, tail = _decode_args(q, cache, P, k, S, out, idx, workspace, path)
     if rope_base is None:
         st = lib.loki_decode_ex(*head, *tail)
     else:
@@ -225,31 +300,35 @@ def decode(q, cache: KVCache, P, k: int, S: int | None = None, out=None, idx=Non
     return out, idx
 
 
+def _step_args(q, k_new, v_new, cache, P, k, pos, out, idx, workspace, path):
+    """Checked and allocated arguments shared by decode_step and StepPlan."""
+    B, Hq, D = _need_q(q, cache)
+    _need_new(k_new, v_new, cache, step=True)
+    _need_P(P, cache)
+    kk = min(k, pos + 1)
+    dev = cache.device
+    out = _out(out, (B, Hq, D), dev)
+    idx = _idx(idx, (B, Hq, kk), dev)
+    workspace = _ws(workspace, dev)
+    _on_gpu(q, "q")
+    if workspace is None and path != PATH_FUSED:
+        workspace = alloc_workspace(B, Hq, cache.S_max, D, kk, dev)
+    head = (_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(P), _ptr(cache.k_slab), _ptr(cache.k_rest),
+            _ptr(cache.v), B, Hq, cache.Hkv, D, cache.d, pos, cache.S_max, k, _dtype_code(q))
+    tail = (_ptr(out), _ptr(idx), _ptr(workspace), _ws_bytes(workspace), path, _stream(q))
+    return out, idx, workspace, head, tail
+
+
 def decode_step(q, k_new, v_new, cache: KVCache, P, k: int, pos: int | None = None, out=None,
                 idx=None, workspace=None, path: int = PATH_AUTO, rope_base: float | None = None):
     """Append k_new/v_new [B, Hkv, D] at `pos` (default: the cache length) and
     decode over pos + 1 tokens, in one call.  With rope_base the new key and
     the query are both embedded at pos (loki_decode_step_rope).  Returns
     (out, idx)."""
-    torch = _torch()
     lib = load()
-    _need(q, "q", cache.dtype)
-    _need(k_new, "k_new", cache.dtype)
-    _need(v_new, "v_new", cache.dtype)
-    _need(P, "P", torch.float32)
-    B, Hq, D = q.shape
     at = cache.length if pos is None else pos
-    kk = min(k, at + 1)
-    if out is None:
-        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
-    if idx is None:
-        idx = torch.empty((B, Hq, kk), dtype=torch.int32, device=q.device)
-    if workspace is None and path != PATH_FUSED:
-        workspace = alloc_workspace(B, Hq, D, cache.S_max, kk, q.device)
-    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    head = (_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(P), _ptr(cache.k_slab), _ptr(cache.k_rest),
-            _ptr(cache.v), B, Hq, cache.Hkv, D, cache.d, at, cache.S_max, k, _dtype_code(q))
-    tail = (_ptr(out), _ptr(idx), _ptr(workspace), wsb, path, _stream(q))
+    out, idx, _ws_keep, head, tail = _step_args(q, k_new, v_new, cache, P, k, at, out, idx,
+                                                workspace, path)
     if rope_base is None:
         st = lib.loki_decode_step(*head, *tail)
     else:
@@ -271,17 +350,19 @@ def decode_path(B, Hq, Hkv, D, d, S, k, dtype="bf16", path=PATH_AUTO) -> int:
 
 def scores(q, cache: KVCache, P, S: int | None = None, out=None, workspace=None):
     """Ranking scores [B, Hq, S] float32 (the low-rank pass alone)."""
-    torch = _torch()
     lib = load()
-    B, Hq, D = q.shape
+    B, Hq, D = _need_q(q, cache)
+    _need_P(P, cache)
     S = cache.length if S is None else S
-    if out is None:
-        out = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
+    dev = cache.device
+    out = _out(out, (B, Hq, S), dev, "scores")
+    workspace = _ws(workspace, dev)
+    _on_gpu(q, "q")
     if workspace is None:
-        workspace = alloc_workspace(B, Hq, D, cache.S_max, 1, q.device)
+        workspace = alloc_workspace(B, Hq, cache.S_max, D, 1, dev)
     st = lib.loki_scores(_ptr(q), _ptr(cache.k_slab), _ptr(P), B, Hq, cache.Hkv, D, cache.d, S,
                          cache.S_max, _dtype_code(q), _ptr(out), _ptr(workspace),
-                         workspace.numel(), _stream(q))
+                         _ws_bytes(workspace), _stream(q))
     _check(st, "loki_scores")
     return out
 
@@ -290,12 +371,16 @@ def topk(scores_2d, k: int, S: int | None = None, idx=None):
     """Top-k of each row of a float32 device matrix [rows, ld]; ascending ids."""
     torch = _torch()
     lib = load()
+    if scores_2d is None or scores_2d.dim() != 2:
+        raise ValueError("scores must be [rows, ld]")
     _need(scores_2d, "scores", torch.float32)
     rows, ld = scores_2d.shape
     S = ld if S is None else S
+    if not 1 <= S <= ld:
+        raise ValueError(f"S must be in [1, {ld}]")
     kk = min(k, S)
-    if idx is None:
-        idx = torch.empty((rows, kk), dtype=torch.int32, device=scores_2d.device)
+    idx = _idx(idx, (rows, kk), scores_2d.device)
+    _on_gpu(scores_2d, "scores")
     st = lib.loki_topk(_ptr(scores_2d), rows, S, ld, k, _ptr(idx), _stream(scores_2d))
     _check(st, "loki_topk")
     return idx
@@ -305,37 +390,49 @@ def attend_indices(q, cache: KVCache, P, idx, S: int | None = None, out=None, wo
     """Exact attention over given ascending index rows idx [B, Hq, k] int32."""
     torch = _torch()
     lib = load()
-    _need(idx, "idx", torch.int32)
-    B, Hq, D = q.shape
+    B, Hq, D = _need_q(q, cache)
+    _need_P(P, cache)
+    if idx is None or idx.dim() != 3:
+        raise ValueError("idx must be [B, Hq, k]")
     k = idx.shape[-1]
+    dev = cache.device
+    _need(idx, "idx", torch.int32, (B, Hq, k), dev)
     S = cache.length if S is None else S
-    if out is None:
-        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    out = _out(out, (B, Hq, D), dev)
+    workspace = _ws(workspace, dev)
+    _on_gpu(q, "q")
     if workspace is None:
-        workspace = alloc_workspace(B, Hq, D, cache.S_max, k, q.device)
+        workspace = alloc_workspace(B, Hq, cache.S_max, D, k, dev)
     st = lib.loki_attend_indices(_ptr(q), _ptr(cache.k_slab), _ptr(cache.k_rest), _ptr(cache.v),
                                  _ptr(P), B, Hq, cache.Hkv, D, cache.d, S, cache.S_max, _ptr(idx),
-                                 k, _dtype_code(q), _ptr(out), _ptr(workspace), workspace.numel(),
-                                 _stream(q))
+                                 k, _dtype_code(q), _ptr(out), _ptr(workspace),
+                                 _ws_bytes(workspace), _stream(q))
     _check(st, "loki_attend_indices")
     return out
+
+
+def _dense_args(q, cache, P, S, out, workspace):
+    B, Hq, D = _need_q(q, cache)
+    _need_P(P, cache)
+    S = cache.length if S is None else S
+    dev = cache.device
+    out = _out(out, (B, Hq, D), dev)
+    workspace = _ws(workspace, dev)
+    _on_gpu(q, "q")
+    if workspace is None:
+        workspace = alloc_workspace(B, Hq, cache.S_max, D, 1, dev)
+    head = (_ptr(q), _ptr(cache.k_slab), _ptr(cache.k_rest), _ptr(cache.v), _ptr(P), B, Hq,
+            cache.Hkv, D, cache.d, S, cache.S_max, _dtype_code(q))
+    tail = (_ptr(out), _ptr(workspace), _ws_bytes(workspace), _stream(q))
+    return S, out, workspace, head, tail
 
 
 def dense_decode(q, cache: KVCache, P, S: int | None = None, out=None, workspace=None,
                  rope_base: float | None = None, q_pos: int | None = None):
     """Dense attention over all S tokens of the same rotated cache (the query
     embedded at q_pos, default S - 1, when rope_base is given)."""
-    torch = _torch()
     lib = load()
-    B, Hq, D = q.shape
-    S = cache.length if S is None else S
-    if out is None:
-        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
-    if workspace is None:
-        workspace = alloc_workspace(B, Hq, D, cache.S_max, 1, q.device)
-    head = (_ptr(q), _ptr(cache.k_slab), _ptr(cache.k_rest), _ptr(cache.v), _ptr(P), B, Hq,
-            cache.Hkv, D, cache.d, S, cache.S_max, _dtype_code(q))
-    tail = (_ptr(out), _ptr(workspace), workspace.numel(), _stream(q))
+    S, out, _ws_keep, head, tail = _dense_args(q, cache, P, S, out, workspace)
     if rope_base is None:
         st = lib.loki_dense_decode(*head, *tail)
     else:
@@ -351,7 +448,8 @@ def stream_read(buf, sink, workgroups: int):
     `sink` is a float32 device tensor of at least workgroups * 256 entries."""
     torch = _torch()
     _need(buf, "buf")
-    _need(sink, "sink", torch.float32)
+    _need(sink, "sink", torch.float32, device=buf.device)
+    _on_gpu(buf, "buf")
     if sink.numel() < workgroups * 256:
         raise ValueError("sink needs workgroups * 256 floats")
     st = load().loki_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
@@ -369,21 +467,9 @@ class DecodePlan:
     def __init__(self, q, cache: KVCache, P, k: int, S: int | None = None, out=None, idx=None,
                  workspace=None, path: int = PATH_AUTO, rope_base: float | None = None,
                  q_pos: int | None = None):
-        torch = _torch()
-        _need(q, "q", cache.dtype)
-        _need(P, "P", torch.float32)
-        B, Hq, D = q.shape
-        S = cache.length if S is None else S
-        kk = min(k, S)
-        self.out = out if out is not None else torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
-        self.idx = idx if idx is not None else torch.empty((B, Hq, kk), dtype=torch.int32, device=q.device)
-        if workspace is None and path != PATH_FUSED:
-            workspace = alloc_workspace(B, Hq, D, cache.S_max, kk, q.device)
+        S, self.out, self.idx, workspace, head, tail = _decode_args(q, cache, P, k, S, out, idx,
+                                                                    workspace, path)
         self._keep = (q, cache, P, workspace)
-        wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
-        head = (_ptr(q), _ptr(cache.k_slab), _ptr(cache.k_rest), _ptr(cache.v), _ptr(P),
-                B, Hq, cache.Hkv, D, cache.d, S, cache.S_max, k, _dtype_code(q))
-        tail = (_ptr(self.out), _ptr(self.idx), _ptr(workspace), wsb, path, _stream(q))
         if rope_base is None:
             self._fn = load().loki_decode_ex
             self._args = head + tail
@@ -402,13 +488,13 @@ class AppendPlan:
     """An append call marshalled once (fixed source buffers and position)."""
 
     def __init__(self, cache: KVCache, k_new, v_new, P, pos: int, rope_base: float | None = None):
-        _need(k_new, "k_new", cache.dtype)
-        _need(v_new, "v_new", cache.dtype)
-        _need(P, "P", _torch().float32)
-        B, Hkv, T, D = k_new.shape
+        T = _need_new(k_new, v_new, cache, step=False)
+        _need_P(P, cache)
+        _on_gpu(k_new, "k_new")
         self._keep = (cache, k_new, v_new, P)
         args = (_ptr(k_new), _ptr(v_new), _ptr(P), _ptr(cache.k_slab), _ptr(cache.k_rest),
-                _ptr(cache.v), B, Hkv, D, cache.d, cache.S_max, pos, T, _dtype_code(k_new))
+                _ptr(cache.v), cache.B, cache.Hkv, cache.D, cache.d, cache.S_max, pos, T,
+                _dtype_code(k_new))
         if rope_base is None:
             self._fn = load().loki_kv_append
             self._args = args + (_stream(k_new),)
@@ -427,19 +513,8 @@ class DensePlan:
 
     def __init__(self, q, cache: KVCache, P, S: int | None = None, out=None, workspace=None,
                  rope_base: float | None = None, q_pos: int | None = None):
-        torch = _torch()
-        _need(q, "q", cache.dtype)
-        _need(P, "P", torch.float32)
-        B, Hq, D = q.shape
-        S = cache.length if S is None else S
-        self.out = out if out is not None else torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
-        if workspace is None:
-            workspace = alloc_workspace(B, Hq, D, cache.S_max, 1, q.device)
+        S, self.out, workspace, head, tail = _dense_args(q, cache, P, S, out, workspace)
         self._keep = (q, cache, P, workspace)
-        head = (_ptr(q), _ptr(cache.k_slab), _ptr(cache.k_rest), _ptr(cache.v), _ptr(P),
-                B, Hq, cache.Hkv, D, cache.d, S, cache.S_max, _dtype_code(q))
-        tail = (_ptr(self.out), _ptr(workspace), workspace.numel() * workspace.element_size(),
-                _stream(q))
         if rope_base is None:
             self._fn = load().loki_dense_decode
             self._args = head + tail
@@ -460,23 +535,9 @@ class StepPlan:
 
     def __init__(self, q, k_new, v_new, cache: KVCache, P, k: int, pos: int, out=None, idx=None,
                  workspace=None, path: int = PATH_AUTO, rope_base: float | None = None):
-        torch = _torch()
-        _need(q, "q", cache.dtype)
-        _need(k_new, "k_new", cache.dtype)
-        _need(v_new, "v_new", cache.dtype)
-        _need(P, "P", torch.float32)
-        B, Hq, D = q.shape
-        kk = min(k, pos + 1)
-        self.out = out if out is not None else torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
-        self.idx = idx if idx is not None else torch.empty((B, Hq, kk), dtype=torch.int32, device=q.device)
-        if workspace is None and path != PATH_FUSED:
-            workspace = alloc_workspace(B, Hq, D, cache.S_max, kk, q.device)
-        wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        self.out, self.idx, workspace, head, tail = _step_args(q, k_new, v_new, cache, P, k, pos,
+                                                               out, idx, workspace, path)
         self._keep = (q, k_new, v_new, cache, P, workspace)
-        head = (_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(P), _ptr(cache.k_slab),
-                _ptr(cache.k_rest), _ptr(cache.v), B, Hq, cache.Hkv, D, cache.d, pos,
-                cache.S_max, k, _dtype_code(q))
-        tail = (_ptr(self.out), _ptr(self.idx), _ptr(workspace), wsb, path, _stream(q))
         if rope_base is None:
             self._fn = load().loki_decode_step
             self._args = head + tail

@@ -341,7 +341,7 @@ int loki_kv_append_rope(const void* k_new, const void* v_new, const float* P, vo
                      rope_base, stream);
 }
 
-size_t loki_decode_workspace_size(int32_t B, int32_t Hq, int32_t D, int32_t S_max, int32_t k_max) {
+size_t loki_decode_workspace_size(int32_t B, int32_t Hq, int32_t S_max, int32_t D, int32_t k_max) {
   if (B <= 0 || Hq <= 0 || D <= 0 || S_max <= 0) return 0;
   return workspace_bytes(B, Hq, D, S_max, k_max < 1 ? 1 : k_max);
 }

@@ -74,7 +74,7 @@ int main(void) {
   float *dk, *dv, *dq, *dP, *slab, *rest, *vc, *out, *out2;
   int32_t *idx, *idx2;
   void* ws;
-  const size_t wsb = loki_decode_workspace_size(B, HQ, D, SMAX, S);
+  const size_t wsb = loki_decode_workspace_size(B, HQ, SMAX, D, S);
   if (wsb == 0 || wsb % 256) FAIL("workspace size %zu", wsb);
   HIPOK(hipMalloc((void**)&dk, sizeof kh));
   HIPOK(hipMalloc((void**)&dv, sizeof vh));

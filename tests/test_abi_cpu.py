@@ -45,7 +45,7 @@ def test_version_and_status_strings(L):
     lib = L.load()
     with open(os.path.join(ROOT, "include", "loki.h")) as fh:
         header = int(re.search(r"#define LOKI_ABI_VERSION (\d+)", fh.read()).group(1))
-    assert lib.loki_abi_version() == header == 3
+    assert lib.loki_abi_version() == header == 4
     for st in (0, -1, -2, -3, -4, 7):
         assert lib.loki_status_string(st)
     assert L.status_string(-2).startswith("LOKI_EWORKSPACE")
@@ -198,14 +198,26 @@ def test_topk_and_scores_reject_bad_arguments(L):
 def test_workspace_size_properties(L):
     lib = L.load()
     ws = lambda *a: lib.loki_decode_workspace_size(*a)
-    assert ws(0, 4, 128, 100, 10) == 0
-    for args in [(16, 40, 128, 3584, 896), (1, 32, 128, 4096, 1024), (4, 32, 128, 32768, 4096),
-                 (1, 1, 64, 256, 64)]:
+    assert ws(0, 4, 100, 128, 10) == 0 and ws(1, 4, 0, 128, 10) == 0 and ws(1, 4, 100, 0, 1) == 0
+    for args in [(16, 40, 3584, 128, 896), (1, 32, 4096, 128, 1024), (4, 32, 32768, 128, 4096),
+                 (1, 1, 256, 64, 64)]:
         n = ws(*args)
         assert n % 256 == 0 and n > 0
-        B, Hq, D, S_max, k = args
-        assert n >= B * Hq * (D + S_max) * 4
-        assert ws(B, Hq, D, S_max, k + 100) >= n
+        B, Hq, S_max, D, k = args
+        # q', the score rows and the kept-position bitmaps at least
+        assert n >= B * Hq * (D * 4 + S_max * 4 + S_max // 8)
+        assert ws(B, Hq, S_max, D, k + 100) >= n
+
+
+def test_workspace_size_argument_order(L):
+    # (B, Hq, S_max, D, k_max): a long cache with a small head dim needs about
+    # 4 bytes per cached position per row; a short cache with a huge head dim
+    # needs at least two D-wide rows (q' and a slice partial)
+    ws = L.load().loki_decode_workspace_size
+    long_cache = ws(1, 1, 1 << 20, 64, 1)
+    assert 4 << 20 <= long_cache < 6 << 20
+    assert ws(1, 1, 64, 1 << 20, 1) >= 8 << 20
+    assert L.workspace_size(1, 1, 1 << 20, 64, 1) == long_cache
 
 
 def test_calibrate_matches_oracle(L):
