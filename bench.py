@@ -80,6 +80,21 @@ def measured_traffic(kernel_hash: str, workload: str):
     return float(t["hbm_bytes_per_launch"])
 
 
+def timed(torch, fn, n):
+    """Launch fn(i) for i < n back to back between two HIP events on the
+    launch stream; returns (wall ms per call, event ms per call)."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    for i in range(n):
+        fn(i)
+    e1.record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    return (t1 - t0) * 1e3 / n, e0.elapsed_time(e1) / n
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -104,7 +119,19 @@ def main():
                     help="RoPE variant: keys embedded at their positions, the query at S-1")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="first run a plain device copy of this size (counter calibration)")
+    ap.add_argument("--no-per-config", action="store_true",
+                    help="skip the decode measurements of the other workloads")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="CPU oracle: seconds of work per worker process")
+    ap.add_argument("--cpu-workers", type=int, default=0,
+                    help="CPU oracle: worker processes (0: every host core, at most 16)")
+    ap.add_argument("--cpu-baseline-child", action="store_true", help=argparse.SUPPRESS)
     args = ap.parse_args()
+    if args.cpu_baseline_child:
+        # the CPU oracle's timing, in a process that never touches the GPU
+        print(json.dumps(cpu_baseline_child(args.config, args.rope_base, args.cpu_seconds,
+                                            args.cpu_workers)), flush=True)
+        return
     if args.gpus != 1:
         print(f"bench.py: this implementation runs on a single GPU; --gpus {args.gpus} is not "
               "supported (the decode shards by sequence or head with no communication, but only "
@@ -185,7 +212,7 @@ def main():
 
     out = torch.empty((w.B, w.Hq, w.D), dtype=torch.float32, device=dev)
     idx = torch.empty((w.B, w.Hq, k), dtype=torch.int32, device=dev)
-    ws = loki.alloc_workspace(w.B, w.Hq, w.D, S, k, dev)
+    ws = loki.alloc_workspace(w.B, w.Hq, S, w.D, k, dev)
     # every (layer, token) combination marshalled once, so the timed loop is
     # one C call per step: loki_decode_step appends the step's token at S-1
     # and decodes over S tokens
@@ -204,25 +231,14 @@ def main():
     def step(i):
         step_plans[i % n_plans]()
 
-    def timed(fn, n):
-        """Launch fn n times back to back between two HIP events on the
-        launch stream; returns (wall ms per call, event ms per call)."""
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        e0.record()
-        for i in range(n):
-            fn(i)
-        e1.record()
-        torch.cuda.synchronize()
-        t1 = time.perf_counter()
-        return (t1 - t0) * 1e3 / n, e0.elapsed_time(e1) / n
+    def timed_(fn, n):
+        return timed(torch, fn, n)
 
     for i in range(args.settle):
         step(i)
     for i in range(args.warmup):
         step(i)
-    ms_per_step, step_avg_ms = timed(lambda i: step(args.warmup + i), args.steps)
+    ms_per_step, step_avg_ms = timed_(lambda i: step(args.warmup + i), args.steps)
     log(f"timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step, events {step_avg_ms * 1e3:.1f} us/launch")
 
     # per-launch distribution: each step between its own pair of events
@@ -242,7 +258,7 @@ def main():
     # decode alone (append excluded, as the pages time it), same caches
     for i in range(args.warmup):
         dec_plans[i % n_plans]()
-    _, dec_avg_ms = timed(lambda i: dec_plans[i % n_plans](), args.steps)
+    _, dec_avg_ms = timed_(lambda i: dec_plans[i % n_plans](), args.steps)
     log(f"decode alone {dec_avg_ms * 1e3:.1f} us/launch")
 
     hq = w.B * w.Hq
@@ -269,7 +285,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": ("bf16 cache, f32 accumulation" if w.dtype == "bf16" else "f32"),
         "data": "synthetic: seeded keys with a decaying PCA spectrum, N(0,1) values and queries",
         "config": {"workload": f"{w.name} steady state at S={S}"
                                + (f" with k_f={w.k_f}, d={w.d}" if overridden else ""),
@@ -281,6 +297,10 @@ def main():
                    "rope_base": rb},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
+                     "traffic_source": (
+                         "recorded, not measured in this run: rocprofv3 --pmc FETCH_SIZE and "
+                         f"WRITE_SIZE in profiles/traffic_fused_decode_step_{args.config}.txt, "
+                         "taken on this kernel source hash" if traffic is not None else None),
                      "kernel": ("fused decode step (append + decode, one launch)" if "fused" in path_name
                                 else "decode step (split kernels)"),
                      "algorithmic_bytes_per_launch": step_bytes,
@@ -301,7 +321,7 @@ def main():
             sink = torch.empty(wg * 256, dtype=torch.float32, device=dev)
             for _ in range(2):
                 loki.stream_read(buf, sink, wg)
-            _, rms = timed(lambda i: loki.stream_read(buf, sink, wg), 10)
+            _, rms = timed_(lambda i: loki.stream_read(buf, sink, wg), 10)
             best = max(best, buf.numel() / (rms * 1e-3) / 1e9)
         del buf
         result["roofline"]["measured_stream_read_GBs"] = best
@@ -318,19 +338,19 @@ def main():
                      for i in range(n_plans)]
         for i in range(args.warmup):
             alt_plans[i % n_plans]()
-        _, ams = timed(lambda i: alt_plans[i % n_plans](), args.steps)
+        _, ams = timed_(lambda i: alt_plans[i % n_plans](), args.steps)
         result[key] = {"avg_ms": ams, "head_queries_per_s": hq / (ams * 1e-3),
                        "vs_decode_only": dec_avg_ms / ams}
         log(f"{key.replace('_', ' ')} decode {ams * 1e3:.1f} us/launch")
 
     # ---- same-GPU dense baseline on the same caches
     if not args.no_dense:
-        dws = loki.alloc_workspace(w.B, w.Hq, w.D, S, 1, dev)
+        dws = loki.alloc_workspace(w.B, w.Hq, S, w.D, 1, dev)
         dense_plans = [loki.DensePlan(qs[i % R], caches[i % L], Pd, S=S, out=out, workspace=dws,
                                       rope_base=rb) for i in range(n_plans)]
         for i in range(args.warmup):
             dense_plans[i % n_plans]()
-        _, dms = timed(lambda i: dense_plans[i % n_plans](), args.steps)
+        _, dms = timed_(lambda i: dense_plans[i % n_plans](), args.steps)
         result["dense_baseline"] = {
             "avg_ms": dms, "head_queries_per_s": hq / (dms * 1e-3),
             "achieved_GBs": by["dense"] / (dms * 1e-3) / 1e9,
@@ -361,13 +381,13 @@ def main():
                                    path=args.path, rope_base=rb) for st in range(w.steps)]
         n = w.steps
         run = {"prompt": w.prefill, "generated": n,
-               "step_ms_total": timed(lambda i: run_step[i](), n)[1] * n,
-               "append_ms_total": timed(lambda i: run_app[i](), n)[1] * n,
-               "decode_ms_total": timed(lambda i: run_dec[i](), n)[1] * n}
+               "step_ms_total": timed_(lambda i: run_step[i](), n)[1] * n,
+               "append_ms_total": timed_(lambda i: run_app[i](), n)[1] * n,
+               "decode_ms_total": timed_(lambda i: run_dec[i](), n)[1] * n}
         if not args.no_dense:
             run_dense = [loki.DensePlan(qs[st % R], run_cache, Pd, S=Ss[st], out=out, workspace=dws,
                                         rope_base=rb) for st in range(w.steps)]
-            run["dense_ms_total"] = timed(lambda i: run_dense[i](), n)[1] * n
+            run["dense_ms_total"] = timed_(lambda i: run_dense[i](), n)[1] * n
             run["loki_decode_speedup_vs_dense"] = run["dense_ms_total"] / run["decode_ms_total"]
         result["generation_run"] = run
         log(f"run: step {run['step_ms_total']:.2f} ms, decode {run['decode_ms_total']:.2f} ms, "
@@ -382,9 +402,20 @@ def main():
                                                            new_v[0], qs[0], Pd, up, dev, rb)
         log(f"top-k Jaccard vs exact: {result['topk_agreement_vs_exact']}")
 
-    # ---- CPU oracle on a bounded sample (rank 0, one GPU)
+    # ---- the other workloads: decode alone on the AUTO path, the dense
+    # baseline and (grouped-query shapes) the other gather, same method
+    if not args.no_per_config and args.kf is None and args.df is None and rb is None:
+        result["per_config"] = {}
+        for name in PER_CONFIG:
+            if name == args.config:
+                continue
+            result["per_config"][name] = measure_config(loki, torch, name, dev, args.steps,
+                                                        args.warmup, log)
+            torch.cuda.empty_cache()
+
+    # ---- CPU oracle on a bounded sample (rank 0, one GPU), in a child process
     if not args.no_cpu:
-        result["cpu_baseline"] = cpu_baseline(w, S, k, K_raw, V_raw, log, rb)
+        result["cpu_baseline"] = cpu_baseline(args, log)
 
     print(json.dumps(result), flush=True)
 
@@ -416,43 +447,199 @@ def topk_agreement(loki, w, S, k, K_raw, V_raw, kn, vn, q, Pd, up, dev, rb=None)
     return res
 
 
-def cpu_baseline(w, S, k, K_raw, V_raw, log, rb=None):
-    """The CPU oracle, as it stands, decoding a bounded sample of the same
-    workload: every query head of the first `nb` sequences at S tokens.  The
-    oracle gets its own inputs (its own calibration and float64 append of the
-    same raw keys); BLAS is held to one thread."""
-    import oracle
+def design_bytes(w, S, k, path, idx) -> int:
+    """HBM bytes the chosen path's kernels move by their design, from the
+    selections the decode actually made (idx [B, Hq, k] on the host): the
+    slab once per KV head (once per query head on the fused path, where the
+    two are equal), the kept tokens' rest and value rows (each query head's
+    own on the fused and split paths, each KV head's union of its query heads'
+    on the union path; the slab dims of a kept key are never re-read), the
+    ids, and on the split and union paths the float32 score rows written and
+    read back."""
+    e = w.esize
+    row = (2 * w.D - w.d) * e
+    total = w.B * w.Hkv * S * w.d * e + w.B * w.Hq * k * 4
+    if path == "union":
+        G = w.Hq // w.Hkv
+        for b in range(w.B):
+            for g in range(w.Hkv):
+                total += np.unique(idx[b, g * G:(g + 1) * G]).size * row
+    else:
+        total += w.B * w.Hq * k * row
+    if path != "fused":
+        total += 2 * w.B * w.Hq * S * 4
+    return int(total)
+
+
+PER_CONFIG = ["l2_7b", "l3_8b_gqa", "mistral_32k"]
+
+
+def measure_config(loki, torch, name, dev, steps, warmup, log) -> dict:
+    """Decode alone (AUTO path), the dense baseline and, for grouped-query
+    shapes, the other gather, for one workload at its full size, timed as
+    the headline's decode: back-to-back launches between two HIP events,
+    cache copies cycled so that no launch finds its bytes cached."""
     import synth
+    w = synth.WORKLOADS[name]
+    S, k = w.S, w.k
+    Qs = synth.bases(w)
+    P = np.stack([loki.calibrate(synth.calib_keys(w, g, Qs[g]).astype(np.float32))[0]
+                  for g in range(w.Hkv)])
+    Pd = torch.from_numpy(P).to(dev)
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+
+    def up(a):
+        if w.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    K_raw, V_raw = synth.raw_cache(w, S, Qs)
+    base = loki.KVCache(w.B, w.Hkv, S, w.D, w.d, tdt, dev)
+    loki.append(base, up(K_raw), up(V_raw), Pd, pos=0)
+    del K_raw, V_raw
+    cache_bytes = sum(t.numel() * t.element_size() for t in (base.k_slab, base.k_rest, base.v)
+                      if t is not None)
+    L = max(4, -(-(1 << 30) // cache_bytes))
+    caches = [base]
+    for _ in range(L - 1):
+        c = loki.KVCache(w.B, w.Hkv, S, w.D, w.d, tdt, dev)
+        c.k_slab.copy_(base.k_slab)
+        if c.k_rest is not None:
+            c.k_rest.copy_(base.k_rest)
+        c.v.copy_(base.v)
+        c.length = S
+        caches.append(c)
+    R = 4
+    qs = [up(synth.queries(w, step=r)) for r in range(R)]
+    n_plans = L * R // np.gcd(L, R)
+    out = torch.empty((w.B, w.Hq, w.D), dtype=torch.float32, device=dev)
+    idx = torch.empty((w.B, w.Hq, k), dtype=torch.int32, device=dev)
+    ws = loki.alloc_workspace(w.B, w.Hq, S, w.D, k, dev)
+    code = loki.decode_path(w.B, w.Hq, w.Hkv, w.D, w.d, S, k, w.dtype, loki.PATH_AUTO)
+    path = {1: "fused", 2: "split", 3: "union"}[code]
+
+    def run(p):
+        plans = [loki.DecodePlan(qs[i % R], caches[i % L], Pd, k, S=S, out=out, idx=idx,
+                                 workspace=ws, path=p) for i in range(n_plans)]
+        for i in range(warmup):
+            plans[i % n_plans]()
+        return timed(torch, lambda i: plans[i % n_plans](), steps)[1]
+
+    dec_ms = run(loki.PATH_AUTO)
+    loki.DecodePlan(qs[0], caches[0], Pd, k, S=S, out=out, idx=idx, workspace=ws)()
+    torch.cuda.synchronize()
+    by = algorithmic_bytes(w, S, k)
+    moved = design_bytes(w, S, k, path, idx.cpu().numpy())
+    res = {"workload": f"{name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} D={w.D} d={w.d} S={S} k={k} "
+                       f"{w.dtype} cache",
+           "path": path, "decode_us": dec_ms * 1e3,
+           "head_queries_per_s": w.B * w.Hq / (dec_ms * 1e-3),
+           "algorithmic_bytes": by["total"],
+           "achieved_GBs": by["total"] / (dec_ms * 1e-3) / 1e9,
+           "frac": by["total"] / (dec_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+           "path_design_bytes": moved,
+           "path_design_GBs": moved / (dec_ms * 1e-3) / 1e9,
+           "layers_cycled": L}
+    if w.Hq // w.Hkv in (2, 4) and path in ("split", "union"):
+        other = "union" if path == "split" else "split"
+        oms = run(loki.PATH_UNION if other == "union" else loki.PATH_SPLIT)
+        res[f"{other}_gather_us"] = oms * 1e3
+    dws = loki.alloc_workspace(w.B, w.Hq, S, w.D, 1, dev)
+    dplans = [loki.DensePlan(qs[i % R], caches[i % L], Pd, S=S, out=out, workspace=dws)
+              for i in range(n_plans)]
+    for i in range(warmup):
+        dplans[i % n_plans]()
+    dms = timed(torch, lambda i: dplans[i % n_plans](), steps)[1]
+    res.update({"dense_us": dms * 1e3, "dense_GBs": by["dense"] / (dms * 1e-3) / 1e9,
+                "loki_speedup_vs_dense": dms / dec_ms})
+    log(f"{name}: {path} decode {dec_ms * 1e3:.1f} us ({res['achieved_GBs']:.0f} GB/s "
+        f"algorithmic, {res['path_design_GBs']:.0f} GB/s by the path's design), dense "
+        f"{dms * 1e3:.1f} us, speedup {dms / dec_ms:.2f}x")
+    return res
+
+
+def cpu_baseline(args, log):
+    """Runs the CPU oracle's timing in a child process (which never touches
+    the GPU, so it may fork its workers) and returns its record."""
+    import subprocess
+    cmd = [sys.executable, os.path.abspath(__file__), "--cpu-baseline-child", "--config",
+           args.config, "--cpu-seconds", str(args.cpu_seconds), "--cpu-workers",
+           str(args.cpu_workers)]
+    if args.rope_base is not None:
+        cmd += ["--rope-base", str(args.rope_base)]
+    r = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
+    if r.returncode != 0:
+        raise RuntimeError("CPU oracle timing failed:\n" + r.stderr[-2000:])
+    rec = json.loads(r.stdout.strip().splitlines()[-1])
+    log(f"cpu oracle: {rec['value']:.0f} head-queries/s on {rec['cores']} processes")
+    return rec
+
+
+def _cpu_worker(job):
+    """One worker of the CPU oracle's timing: decode its share of the sampled
+    head-queries again and again for `seconds`, BLAS held to one thread."""
     from threadpoolctl import threadpool_limits
 
-    nb = 4
+    import oracle
+    pairs, seconds = job
+    st = _CPU_STATE
+    n, elapsed = 0, 0.0
+    with threadpool_limits(limits=1):
+        while n == 0 or elapsed < seconds:
+            t = time.perf_counter()
+            oracle.decode(st["q"], st["slab"], st["rest"], st["v"], st["P"], st["k"], st["dtype"],
+                          S=st["S"], heads=pairs, rope=st["rope"])
+            elapsed += time.perf_counter() - t
+            n += len(pairs)
+    return n, elapsed
+
+
+_CPU_STATE = {}
+
+
+def cpu_baseline_child(config, rb, seconds, workers) -> dict:
+    """The CPU oracle, as it stands, decoding a bounded sample of the same
+    workload (every query head of the first sequences at S tokens) on the
+    host's cores: the sampled head-queries are split into one contiguous
+    share per worker process, each worker decodes its share repeatedly for
+    `seconds`, and the rate is all head-queries decoded over the longest
+    worker time.  The oracle gets its own inputs: its own calibration and
+    float64 append of the generator's keys."""
+    import multiprocessing as mp
+
+    import oracle
+    import synth
+    w = synth.WORKLOADS[config]
+    S, k = w.S, w.k
+    nb = min(4, w.B)
+    workers = workers if workers > 0 else min(16, os.cpu_count() or 1)
     Qs = synth.bases(w)
-    P = np.stack([oracle.calibrate(synth.calib_keys(w, g, Qs[g]))[0] for g in range(w.Hkv)])
-    P32 = P.astype(np.float32)
+    P = np.stack([oracle.calibrate(synth.calib_keys(w, g, Qs[g]))[0]
+                  for g in range(w.Hkv)]).astype(np.float32)
     kn, vn = synth.new_tokens(w, 0, Qs)
     st = np.uint16 if w.dtype == "bf16" else np.float32
     slab = np.empty((nb, w.Hkv, S, w.d), st)
     rest = np.empty((nb, w.Hkv, S, w.D - w.d), st)
     vv = np.empty((nb, w.Hkv, S, w.D), st)
-    for g in range(w.Hkv):
-        Kg = np.concatenate([K_raw[:nb, g], kn[:nb, g]], axis=1)
-        Vg = np.concatenate([V_raw[:nb, g], vn[:nb, g]], axis=1)
-        slab[:, g], rest[:, g], vv[:, g] = oracle.append(oracle.to_f64(Kg, w.dtype),
-                                                         oracle.to_f64(Vg, w.dtype),
-                                                         P32[g].astype(np.float64), w.d, w.dtype,
-                                                         rope_base=rb)
-    q = synth.queries(w)[:nb]
+    for b in range(nb):
+        for g in range(w.Hkv):
+            Kg = np.concatenate([synth.to_storage(synth.cache_keys(w, b, g, S - 1, Qs[g]), w.dtype),
+                                 kn[b, g]])
+            Vg = np.concatenate([synth.to_storage(synth.cache_values(w, b, g, S - 1), w.dtype),
+                                 vn[b, g]])
+            slab[b, g], rest[b, g], vv[b, g] = oracle.append(
+                oracle.to_f64(Kg, w.dtype), oracle.to_f64(Vg, w.dtype),
+                P[g].astype(np.float64), w.d, w.dtype, rope_base=rb)
+    _CPU_STATE.update(q=synth.queries(w)[:nb], slab=slab, rest=rest, v=vv, P=P, k=k,
+                      dtype=w.dtype, S=S, rope=None if rb is None else (rb, S - 1))
     pairs = [(b, h) for b in range(nb) for h in range(w.Hq)]
-    reps, elapsed = 0, 0.0
-    with threadpool_limits(limits=1):
-        while reps < 1 or (elapsed < 10.0 and reps < 200):  # about 10 s of CPU work
-            t = time.perf_counter()
-            oracle.decode(q, slab, rest, vv, P32, k, w.dtype, S=S, heads=pairs,
-                          rope=None if rb is None else (rb, S - 1))
-            elapsed += time.perf_counter() - t
-            reps += 1
-    n = reps * len(pairs)
-    log(f"cpu oracle: {n} head-queries in {elapsed:.1f}s")
+    shares = [pairs[i * len(pairs) // workers:(i + 1) * len(pairs) // workers]
+              for i in range(workers)]
+    shares = [sh for sh in shares if sh]
+    with mp.get_context("fork").Pool(len(shares)) as pool:
+        res = pool.map(_cpu_worker, [(sh, seconds) for sh in shares])
+    n = sum(r[0] for r in res)
+    wall = max(r[1] for r in res)
     cpu = "unknown"
     try:
         with open("/proc/cpuinfo") as fh:
@@ -462,9 +649,11 @@ def cpu_baseline(w, S, k, K_raw, V_raw, log, rb=None):
                     break
     except OSError:
         pass
-    return {"value": n / elapsed, "unit": "head-queries/s", "cores": 1, "kind": "oracle",
+    return {"value": n / wall, "unit": "head-queries/s", "cores": len(shares), "kind": "oracle",
             "sample": f"{len(pairs)} head-queries (all {w.Hq} heads of {nb} sequences) at S={S}, "
-                      f"k={k}, x{reps} repetitions, float64 numpy oracle, 1 BLAS thread",
+                      f"k={k}, split over {len(shares)} worker processes (one BLAS thread each), "
+                      f"each decoding its share repeatedly for >= {seconds:g} s; float64 numpy "
+                      "oracle; rate = head-queries decoded / longest worker time",
             "host_cpu": cpu, "host_nproc": os.cpu_count()}
 
 

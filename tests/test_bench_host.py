@@ -49,3 +49,17 @@ def test_recorded_traffic_only_for_its_kernel_hash():
         assert 400e6 < t < 480e6
     assert bench.measured_traffic("0" * 16, "l2_13b_run") is None
     assert bench.measured_traffic(h, "no_such_workload") is None
+
+
+def test_design_bytes_per_path():
+    # a toy grouped-query shape, bf16: B=1, Hq=4, Hkv=2, D=8, d=2, S=10, k=3
+    import dataclasses
+    import numpy as np
+    w = dataclasses.replace(synth.WORKLOADS["l3_8b_gqa"], B=1, Hq=4, Hkv=2, D=8, d=2)
+    idx = np.array([[[0, 1, 2], [1, 2, 3], [5, 6, 7], [5, 6, 7]]])
+    slab, ids, scores = 1 * 2 * 10 * 2 * 2, 4 * 3 * 4, 2 * 4 * 10 * 4
+    row = (2 * 8 - 2) * 2
+    assert bench.design_bytes(w, 10, 3, "split", idx) == slab + ids + scores + 4 * 3 * row
+    # union: KV head 0 gathers {0,1,2,3}, KV head 1 gathers {5,6,7}
+    assert bench.design_bytes(w, 10, 3, "union", idx) == slab + ids + scores + 7 * row
+    assert bench.design_bytes(w, 10, 3, "fused", idx) == slab + ids + 4 * 3 * row
