@@ -260,6 +260,32 @@ int loki_dense_decode_rope(const void* q, const void* k_slab, const void* k_rest
                            double rope_base, float* out, void* workspace,
                            size_t workspace_bytes, void* stream);
 
+/* ---- Decode without allocation ---------------------------------------------
+ *
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): this
+ * variant of loki_decode_ex takes no workspace.  Its split and union paths
+ * use instead a scratch array that the library holds in device memory, one
+ * copy of LOKI_NOALLOC_SCRATCH_BYTES per GPU it runs on, from the first call
+ * on that GPU (which looks up the array's address with that GPU current;
+ * later calls allocate nothing and call no allocating routine) until the
+ * process ends.  The GPU is the current device, which must be the one
+ * `stream` belongs to.  No kernel relies on the scratch's contents at entry.
+ * Every call on a GPU shares that GPU's array, so calls whose work overlaps
+ * on one GPU (different streams, different host threads without ordering)
+ * race and give undefined results; calls ordered on one stream are safe.
+ * Arguments, path choice and results are those of loki_decode_ex; sizes
+ * whose workspace (loki_decode_workspace_size for the resolved path) would
+ * exceed LOKI_NOALLOC_SCRATCH_BYTES return LOKI_EWORKSPACE with nothing
+ * launched (32 MiB covers every benchmark shape: e.g. 128 rows of 32768
+ * tokens need about 18 MB).  The fused path uses no scratch. */
+#define LOKI_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+int loki_decode_noalloc(const void* q, const void* k_slab, const void* k_rest, const void* v,
+                        const float* P, int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t d,
+                        int32_t S, int32_t S_max, int32_t k, int32_t dtype, float* out,
+                        int32_t* idx, int32_t path, void* stream);
+
 /* Measurement helper, not part of the method: reads `bytes` of device memory
  * at buf (16-byte aligned, bytes a multiple of 16) with nontemporal 16-byte
  * loads in a grid-stride loop of `workgroups` workgroups of 256 threads, and

@@ -45,6 +45,8 @@ _SIGS = {
     "loki_dense_decode": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P,
                                          _P, ctypes.c_size_t, _P]),
     "loki_stream_read": (ctypes.c_int, [_P, ctypes.c_size_t, _P, _I, _P]),
+    "loki_decode_noalloc": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I,
+                                           _P, _P, _I, _P]),
     "loki_kv_append_rope": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I,
                                            _F64, _P]),
     "loki_decode_rope": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I,
@@ -297,6 +299,31 @@ def decode(q, cache: KVCache, P, k: int, S: int | None = None, out=None, idx=Non
         st = lib.loki_decode_rope(*head, S - 1 if q_pos is None else q_pos, float(rope_base),
                                   *tail)
     _check(st, "loki_decode")
+    return out, idx
+
+
+# bytes of the library's own scratch behind decode_noalloc (one copy per GPU)
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def decode_noalloc(q, cache: KVCache, P, k: int, out, idx, S: int | None = None,
+                   path: int = PATH_AUTO):
+    """loki_decode_noalloc: decode_ex without a workspace (the split and
+    union paths use the library's per-GPU scratch array).  out [B, Hq, D]
+    float32 and idx [B, Hq, min(k, S)] int32 are the caller's; nothing is
+    allocated here either."""
+    lib = load()
+    B, Hq, D = _need_q(q, cache)
+    _need_P(P, cache)
+    S = cache.length if S is None else S
+    dev = cache.device
+    _need(out, "out", _torch().float32, (B, Hq, D), dev)
+    _need(idx, "idx", _torch().int32, (B, Hq, min(k, S)), dev)
+    _on_gpu(q, "q")
+    st = lib.loki_decode_noalloc(_ptr(q), _ptr(cache.k_slab), _ptr(cache.k_rest), _ptr(cache.v),
+                                 _ptr(P), B, Hq, cache.Hkv, D, cache.d, S, cache.S_max, k,
+                                 _dtype_code(q), _ptr(out), _ptr(idx), path, _stream(q))
+    _check(st, "loki_decode_noalloc")
     return out, idx
 
 

@@ -4,11 +4,20 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 
 #include "loki.h"
 #include "launch.hpp"
 
 using loki::DecodeArgs;
+
+// Device memory of the library itself for callers that cannot allocate
+// (loki_decode_noalloc): one copy of this array per GPU, alive until the
+// process ends.  In host code its name is only a stand-in, never a device
+// address.
+constexpr size_t kNoallocScratch = LOKI_NOALLOC_SCRATCH_BYTES;
+static_assert(kNoallocScratch % 256 == 0, "the workspace layout is in 256-byte units");
+static __device__ __align__(256) unsigned char scratch[kNoallocScratch];
 
 namespace {
 
@@ -307,6 +316,31 @@ int dense_impl(const void* q, const void* k_slab, const void* k_rest, const void
   return status_of(e);
 }
 
+// ---- scratch of loki_decode_noalloc ----------------------------------------
+//
+// The array itself (`scratch`) is at file scope above; its device address is
+// what hipGetSymbolAddress reports with a device current, looked up once per
+// device and kept.
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// Address of the current device's scratch, or a status.
+int device_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return LOKI_EDEVICE;
+  if (dev < 0 || dev >= kMaxDevices) return LOKI_EUNSUPPORTED;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = p;
+  });
+  if (g_scratch_err[dev] != hipSuccess || g_scratch_ptr[dev] == nullptr) return LOKI_EDEVICE;
+  *out = g_scratch_ptr[dev];
+  return LOKI_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -406,6 +440,28 @@ int loki_decode(const void* q, const void* k_slab, const void* k_rest, const voi
                 void* workspace, size_t ws_bytes, void* stream) {
   return loki_decode_ex(q, k_slab, k_rest, v, P, B, Hq, Hkv, D, d, S, S_max, k, dtype, out, idx,
                         workspace, ws_bytes, LOKI_PATH_AUTO, stream);
+}
+
+int loki_decode_noalloc(const void* q, const void* k_slab, const void* k_rest, const void* v,
+                        const float* P, int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t d,
+                        int32_t S, int32_t S_max, int32_t k, int32_t dtype, float* out,
+                        int32_t* idx, int32_t path, void* stream) {
+  // argument checks first: a rejected call touches no device
+  int st = check_shape(B, Hq, Hkv, D, d, S, S_max, dtype);
+  if (st != LOKI_OK) return st;
+  if (k < 1 || !valid_path(path)) return LOKI_EINVAL;
+  const int kk = std::min(k, S);
+  const int resolved = path == LOKI_PATH_AUTO ? auto_path(B, Hq, Hkv, D, d, S, kk, dtype) : path;
+  if (resolved == LOKI_PATH_UNION && !union_ok(Hq, Hkv, S)) return LOKI_EUNSUPPORTED;
+  if (B == 0) return LOKI_OK;
+  if (resolved != LOKI_PATH_FUSED &&
+      split_layout(B, Hq, Hkv, D, S, S_max, kk, resolved == LOKI_PATH_UNION).total > kNoallocScratch)
+    return LOKI_EWORKSPACE;
+  void* ws = nullptr;
+  st = device_scratch(&ws);
+  if (st != LOKI_OK) return st;
+  return decode_impl(q, k_slab, k_rest, v, P, B, Hq, Hkv, D, d, S, S_max, k, dtype, out, idx, ws,
+                     kNoallocScratch, resolved, loki::Rope(), stream);
 }
 
 int loki_scores(const void* q, const void* k_slab, const float* P, int32_t B, int32_t Hq,

@@ -249,3 +249,24 @@ def test_stream_read_rejects_bad_arguments(L):
     assert lib.loki_stream_read(None, 1024, FAKE, 4, None) == -1
     assert lib.loki_stream_read(FAKE_MIS, 1024, FAKE, 4, None) == -1
     assert lib.loki_stream_read(FAKE, 0, FAKE, 4, None) == 0
+
+
+def test_decode_noalloc_rejects_before_touching_a_device(L):
+    lib = L.load()
+    a = [FAKE, FAKE, FAKE, FAKE, FAKE, 2, 4, 2, 128, 32, 100, 128, 25, 1, FAKE, FAKE, 2, None]
+    bad = list(a); bad[12] = 0          # k < 1
+    assert lib.loki_decode_noalloc(*bad) == -1
+    bad = list(a); bad[13] = 7          # dtype
+    assert lib.loki_decode_noalloc(*bad) == -1
+    bad = list(a); bad[16] = 9          # path
+    assert lib.loki_decode_noalloc(*bad) == -1
+    bad = list(a); bad[8] = 96          # D
+    assert lib.loki_decode_noalloc(*bad) == -4
+    bad = list(a); bad[16] = 3; bad[6] = 3; bad[7] = 1  # union with 3 query heads per KV head
+    assert lib.loki_decode_noalloc(*bad) == -4
+    # split path over 64 x 64 rows of 32768 tokens: 512 MiB of scores > the scratch
+    big = list(a); big[5:12] = [64, 64, 64, 128, 32, 32768, 32768]
+    assert lib.loki_decode_noalloc(*big) == -2
+    assert L.NOALLOC_SCRATCH_BYTES == 32 << 20
+    zero = list(a); zero[5] = 0         # B == 0: nothing to do
+    assert lib.loki_decode_noalloc(*zero) == 0
