@@ -79,13 +79,22 @@ typedef enum { LOKI_F32 = 0, LOKI_BF16 = 1 } loki_dtype;
  * products are formed over it (on the matrix cores for bf16 caches).  AUTO
  * takes it for bf16 caches with d >= D - 96 when, even for independently
  * selecting heads, the union, a fraction 1 - (1 - k/S)^G of the positions,
- * is at most 3/4 of the G*k/S per-head reads.  All paths compute the same
- * function. */
+ * is at most 3/4 of the G*k/S per-head reads.  SLICED is FUSED with each
+ * row's gather split over several workgroups (each ranks and selects the
+ * whole row, then gathers its share of the kept tokens; the shares are
+ * merged by a second launch through the workspace, which it then needs);
+ * AUTO takes it for one query head per KV head at 48 to 128 rows of at most
+ * 4096 tokens.  For rows of at most 4096 tokens the SPLIT and UNION paths
+ * rank and select in one launch (the selecting workgroups wait for the
+ * ranking workgroups of their row; the workspace's first bytes hold the
+ * flags and epoch of that hand-over, which any contents of a fresh
+ * workspace leave valid).  All paths compute the same function. */
 typedef enum {
   LOKI_PATH_AUTO = 0,
   LOKI_PATH_FUSED = 1,
   LOKI_PATH_SPLIT = 2,
-  LOKI_PATH_UNION = 3
+  LOKI_PATH_UNION = 3,
+  LOKI_PATH_SLICED = 4
 } loki_path;
 
 /* Human-readable name of a status code.  Never NULL. */

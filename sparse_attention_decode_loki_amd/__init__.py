@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libloki.so")
 
 LOKI_OK, LOKI_EINVAL, LOKI_EWORKSPACE, LOKI_EDEVICE, LOKI_EUNSUPPORTED = 0, -1, -2, -3, -4
 LOKI_F32, LOKI_BF16 = 0, 1
-PATH_AUTO, PATH_FUSED, PATH_SPLIT, PATH_UNION = 0, 1, 2, 3
+PATH_AUTO, PATH_FUSED, PATH_SPLIT, PATH_UNION, PATH_SLICED = 0, 1, 2, 3, 4
 
 # name -> (restype, argtypes); mirrors include/loki.h
 _P = ctypes.c_void_p

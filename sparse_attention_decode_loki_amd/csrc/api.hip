@@ -60,16 +60,19 @@ int dense_nsplit(int B, int Hq, int Hkv, int S) {
 }
 
 struct Layout {
-  size_t qrot, scores, part, bits, total;
+  size_t sync, qrot, scores, part, bits, total;
 };
 
+// sync (the combined ranking + top-k launch's epoch, given-up count and
+// flags; first, so the epoch sits at the same offset for every shape) |
 // qrot [B*Hq, D] | scores [B*Hq, S_max] | split partials |
 // kept-position bitmaps [B*Hq, ceil(S_max/32)] (union gather)
 Layout layout(int B, int Hq, int D, int S_max, int nsplit) {
   Layout L;
   const size_t rows = static_cast<size_t>(B) * Hq;
-  L.qrot = 0;
-  L.scores = align256(rows * D * sizeof(float));
+  L.sync = 0;
+  L.qrot = align256((2 + rows * loki::kScoreSelectFlags) * sizeof(unsigned long long));
+  L.scores = L.qrot + align256(rows * D * sizeof(float));
   L.part = L.scores + align256(rows * static_cast<size_t>(S_max) * sizeof(float));
   L.bits = L.part + align256(rows * static_cast<size_t>(nsplit) * (D + 2) * sizeof(float));
   L.total = L.bits + align256(rows * static_cast<size_t>(cdiv(S_max, 32)) * sizeof(unsigned));
@@ -83,7 +86,19 @@ Layout split_layout(int B, int Hq, int Hkv, int D, int S, int S_max, int kk, boo
 
 bool valid_path(int path) {
   return path == LOKI_PATH_AUTO || path == LOKI_PATH_FUSED || path == LOKI_PATH_SPLIT ||
-         path == LOKI_PATH_UNION;
+         path == LOKI_PATH_UNION || path == LOKI_PATH_SLICED;
+}
+
+// Slices per row of the sliced single-kernel path: enough workgroups for
+// about kSlicedTarget in all, at least 64 kept tokens per slice, and never
+// more than the split path's slices (which size the workspace).
+#ifndef LOKI_SLICED_TARGET
+#define LOKI_SLICED_TARGET 512
+#endif
+constexpr int kSlicedTarget = LOKI_SLICED_TARGET;
+int sliced_n(int rows, int kk) {
+  const int n = std::min(cdiv(kSlicedTarget, rows), cdiv(kk, 64));
+  return std::max(1, std::min(n, sparse_nsplit(rows, kk)));
 }
 
 int max_nsplit(int B, int Hq, int S_max, int k_max) {
@@ -183,8 +198,19 @@ bool auto_union(int Hq, int Hkv, int D, int d, int S, int kk, int dtype) {
   return 1.0 - std::pow(1.0 - f, G) <= 0.75 * G * f;
 }
 
+// The sliced single-kernel path for one query head per KV head at 48..128
+// rows of at most 4096 tokens, where it measures faster than both the fused
+// and the split path (bf16, D = 128, d = 32, k = S/4: 64 rows of 4096 26.1 us
+// against split 27.7; 128 rows 32.4 against fused 33.8; at 32 rows, 160 rows
+// of 3584 and rows of 8192 it is slower).
+bool auto_sliced(int B, int Hq, int Hkv, int D, int S, int kk) {
+  const int64_t rows = static_cast<int64_t>(B) * Hq;
+  return Hq == Hkv && fused_fits(D, S, kk) && S <= 4096 && rows >= 48 && rows <= 128;
+}
+
 // The path AUTO resolves to.
 int auto_path(int B, int Hq, int Hkv, int D, int d, int S, int kk, int dtype) {
+  if (auto_sliced(B, Hq, Hkv, D, S, kk)) return LOKI_PATH_SLICED;
   if (auto_fused(B, Hq, Hkv, D, S, kk)) return LOKI_PATH_FUSED;
   return auto_union(Hq, Hkv, D, d, S, kk, dtype) ? LOKI_PATH_UNION : LOKI_PATH_SPLIT;
 }
@@ -230,11 +256,18 @@ int decode_impl(const void* q, const void* k_slab, const void* k_rest, const voi
   DecodeArgs a = make_args(q, k_slab, k_rest, v, P, B, Hq, Hkv, D, d, S, S_max, dtype, out, idx,
                            stream);
   a.rope = rope;
-  if (path == LOKI_PATH_FUSED) {
-    if (!fused_fits(D, S, kk)) return LOKI_EUNSUPPORTED;
-    return status_of(loki::launch_fused(a, kk));
-  }
   const int rows = B * Hq;
+  if (path == LOKI_PATH_FUSED || path == LOKI_PATH_SLICED) {
+    if (!fused_fits(D, S, kk)) return LOKI_EUNSUPPORTED;
+    const int nsl = path == LOKI_PATH_SLICED ? sliced_n(rows, kk) : 1;
+    float* part = nullptr;
+    if (nsl > 1) {
+      const Layout L = layout(B, Hq, D, S_max, nsl);
+      if (!workspace || ws_bytes < L.total || !aligned16(workspace)) return LOKI_EWORKSPACE;
+      part = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.part);
+    }
+    return status_of(loki::launch_fused(a, kk, nsl, part));
+  }
   const int nsplit = uni ? union_nsplit(B, Hkv, S) : sparse_nsplit(rows, kk);
   const Layout L = split_layout(B, Hq, Hkv, D, S, S_max, kk, uni);
   if (!workspace || ws_bytes < L.total || !aligned16(workspace)) return LOKI_EWORKSPACE;
@@ -243,9 +276,16 @@ int decode_impl(const void* q, const void* k_slab, const void* k_rest, const voi
   float* scores = reinterpret_cast<float*>(ws + L.scores);
   float* part = reinterpret_cast<float*>(ws + L.part);
   unsigned* bits = reinterpret_cast<unsigned*>(ws + L.bits);
-  hipError_t e = loki::launch_scores(a, qrot, scores);
-  if (e == hipSuccess)
-    e = loki::launch_topk(scores, rows, S, S, kk, idx, a.stream, uni ? bits : nullptr);
+  hipError_t e;
+  if (S <= loki::kScoreSelectMaxS) {
+    // ranking and top-k in one launch; the gather launch advances its epoch
+    a.sync = reinterpret_cast<unsigned long long*>(ws + L.sync);
+    e = loki::launch_score_select(a, qrot, scores, kk, uni ? bits : nullptr);
+  } else {
+    e = loki::launch_scores(a, qrot, scores);
+    if (e == hipSuccess)
+      e = loki::launch_topk(scores, rows, S, S, kk, idx, a.stream, uni ? bits : nullptr);
+  }
   if (e == hipSuccess)
     e = uni ? loki::launch_attend_union(a, qrot, scores, bits, part, nsplit)
             : loki::launch_attend(a, qrot, scores, idx, kk, part, nsplit, true);
@@ -277,9 +317,16 @@ int step_impl(const void* q, const void* k_new, const void* v_new, const float* 
   rope.base = rope_base;
   rope.pos = pos;
   a.rope = rope;
-  if (path == LOKI_PATH_FUSED) {
+  if (path == LOKI_PATH_FUSED || path == LOKI_PATH_SLICED) {
     if (!fused_fits(D, S, kk)) return LOKI_EUNSUPPORTED;
-    return status_of(loki::launch_fused_step(a, k_new, v_new, pos, kk));
+    const int nsl = path == LOKI_PATH_SLICED ? sliced_n(B * Hq, kk) : 1;
+    float* part = nullptr;
+    if (nsl > 1) {
+      const Layout L = layout(B, Hq, D, S_max, nsl);
+      if (!workspace || ws_bytes < L.total || !aligned16(workspace)) return LOKI_EWORKSPACE;
+      part = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.part);
+    }
+    return status_of(loki::launch_fused_step(a, k_new, v_new, pos, kk, nsl, part));
   }
   const Layout L = split_layout(B, Hq, Hkv, D, S, S_max, kk, uni);
   if (!workspace || ws_bytes < L.total || !aligned16(workspace)) return LOKI_EWORKSPACE;
@@ -387,7 +434,8 @@ int loki_decode_path(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t d, i
   if (k < 1) return LOKI_EINVAL;
   const int kk = std::min(k, S);
   if (path == LOKI_PATH_SPLIT) return LOKI_PATH_SPLIT;
-  if (path == LOKI_PATH_FUSED) return fused_fits(D, S, kk) ? LOKI_PATH_FUSED : LOKI_EUNSUPPORTED;
+  if (path == LOKI_PATH_FUSED || path == LOKI_PATH_SLICED)
+    return fused_fits(D, S, kk) ? path : LOKI_EUNSUPPORTED;
   if (path == LOKI_PATH_UNION) return union_ok(Hq, Hkv, S) ? LOKI_PATH_UNION : LOKI_EUNSUPPORTED;
   if (path != LOKI_PATH_AUTO) return LOKI_EINVAL;
   return auto_path(B, Hq, Hkv, D, d, S, kk, dtype);
@@ -476,7 +524,7 @@ int loki_scores(const void* q, const void* k_slab, const float* P, int32_t B, in
   if (!workspace || ws_bytes < L.scores || !aligned16(workspace)) return LOKI_EWORKSPACE;
   DecodeArgs a = make_args(q, k_slab, nullptr, k_slab, P, B, Hq, Hkv, D, d, S, S_max, dtype,
                            nullptr, nullptr, stream);
-  float* qrot = static_cast<float*>(workspace);
+  float* qrot = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.qrot);
   hipError_t e = loki::launch_scores(a, qrot, scores);
   return status_of(e);
 }

@@ -117,30 +117,43 @@ int score_chunk(int units, int S) {
 // every path ranks with the same float32 q'.  Chunk-0 workgroups form all D
 // columns and store q' for the attention kernel; the others form only the d
 // columns that ranking needs.
+template <int D, int NH>
+struct ScoreSmem {
+  static constexpr int NRB = kBlock / (D / 4);  // row blocks of P
+  float qin[NH][D];
+  float red[NRB][NH][D];
+  float qr[NH][D];
+  // this chunk's scores; the pad puts the heads of one token in different banks
+  __align__(16) float ssc[NH][kScoreChunkMax + 16];
+};
+
+// Unit `unit` (= (b*Hkv + g)*nhb + hb) and chunk `ci` of the ranking pass.
+// With `flag` the chunk's scores are published to top-k workgroups of the
+// same launch: stored with device scope, then, once they have completed,
+// `flag` is set to `fval`.
 template <class E, int D, int LPS, int NH>
-__global__ void __launch_bounds__(kBlock) score_kernel(const typename E::T* __restrict__ slab,
-                                                       const typename E::T* __restrict__ q,
-                                                       const float* __restrict__ P,
-                                                       float* __restrict__ qrot,
-                                                       float* __restrict__ scores, int Hq, int Hkv,
-                                                       int d, int S, int S_max, int nhb,
-                                                       int chunk, Rope rope) {
+__device__ __forceinline__ void score_role(const typename E::T* __restrict__ slab,
+                                           const typename E::T* __restrict__ q,
+                                           const float* __restrict__ P, float* __restrict__ qrot,
+                                           float* __restrict__ scores, int Hq, int Hkv, int d,
+                                           int S, int S_max, int nhb, int chunk, Rope rope,
+                                           int unit, int ci, ScoreSmem<D, NH>& sm,
+                                           unsigned long long* flag, unsigned long long fval) {
   constexpr int VEC = E::VEC;
   constexpr int CQ = D / 4;         // column quads of P
   constexpr int NRB = kBlock / CQ;  // row blocks of P
   constexpr int RB = D / NRB;       // rows per block
-  __shared__ float qin[NH][D];
-  __shared__ float red[NRB][NH][D];
-  __shared__ float qr[NH][D];
-  // this chunk's scores; the pad puts the heads of one token in different banks
-  __shared__ __align__(16) float ssc[NH][kScoreChunkMax + 16];
+  auto& qin = sm.qin;
+  auto& red = sm.red;
+  auto& qr = sm.qr;
+  auto& ssc = sm.ssc;
   const int G = Hq / Hkv;
-  const int bg = blockIdx.x / nhb;
-  const int hb = blockIdx.x % nhb;
+  const int bg = unit / nhb;
+  const int hb = unit % nhb;
   const int b = bg / Hkv, g = bg % Hkv;
   const int h0 = g * G + hb * NH;
   const int nh = min(NH, G - hb * NH);
-  const int j0 = blockIdx.y * chunk;
+  const int j0 = ci * chunk;
   const int j1 = min(S, j0 + chunk);
   const typename E::T* sl = slab + static_cast<int64_t>(bg) * S_max * d;
 
@@ -154,7 +167,7 @@ __global__ void __launch_bounds__(kBlock) score_kernel(const typename E::T* __re
   constexpr bool kEarly = NH == 1;
   constexpr int QPT = (NH * D + kBlock - 1) / kBlock;  // query elements per thread
   constexpr int H2 = D / 2;
-  const int ncols = blockIdx.y == 0 ? D : d;
+  const int ncols = ci == 0 ? D : d;
   const int cq = threadIdx.x % CQ, rb = threadIdx.x / CQ;
   const bool rot = 4 * cq < ncols;
   const float* Pg = P + static_cast<int64_t>(g) * D * D;
@@ -228,7 +241,7 @@ __global__ void __launch_bounds__(kBlock) score_kernel(const typename E::T* __re
 #pragma unroll
     for (int pp = 0; pp < NRB; ++pp) x += red[pp][h][col];
     qr[h][col] = x;
-    if (blockIdx.y == 0 && h < nh) qrot[(static_cast<int64_t>(b) * Hq + h0 + h) * D + col] = x;
+    if (ci == 0 && h < nh) qrot[(static_cast<int64_t>(b) * Hq + h0 + h) * D + col] = x;
   }
   __syncthreads();
 
@@ -290,6 +303,23 @@ __global__ void __launch_bounds__(kBlock) score_kernel(const typename E::T* __re
   __syncthreads();
   const int n = j1 - j0;
   float* srow = scores + (static_cast<int64_t>(b) * Hq + h0) * S + j0;
+  if (flag) {
+    // device-scope stores (written through this XCD's L2), then the flag
+    const bool vec = (S & 3) == 0 && (reinterpret_cast<uintptr_t>(scores) & 15) == 0;
+    if (vec) {
+      const Region rr = make_region(srow, 0x7fffffffu);
+      for (int h = 0; h < nh; ++h)
+        for (int i = threadIdx.x; 4 * i < n; i += kBlock)
+          st16_dev(rr, static_cast<uint32_t>((h * S + 4 * i) * 4),
+                   *reinterpret_cast<const uint4*>(&ssc[h][4 * i]));
+    } else {
+      for (int h = 0; h < nh; ++h)
+        for (int i = threadIdx.x; i < n; i += kBlock)
+          st_dev(srow + static_cast<int64_t>(h) * S + i, ssc[h][i]);
+    }
+    publish(flag, fval);
+    return;
+  }
   if ((S & 3) == 0 && (reinterpret_cast<uintptr_t>(scores) & 15) == 0) {
     // rows start 16-byte aligned (chunks are multiples of 256 tokens)
     for (int h = 0; h < nh; ++h)
@@ -300,6 +330,20 @@ __global__ void __launch_bounds__(kBlock) score_kernel(const typename E::T* __re
     for (int h = 0; h < nh; ++h)
       for (int i = threadIdx.x; i < n; i += kBlock) srow[static_cast<int64_t>(h) * S + i] = ssc[h][i];
   }
+}
+
+// The ranking pass alone.  Grid (B*Hkv*nhb, ceil(S / chunk)).
+template <class E, int D, int LPS, int NH>
+__global__ void __launch_bounds__(kBlock) score_kernel(const typename E::T* __restrict__ slab,
+                                                       const typename E::T* __restrict__ q,
+                                                       const float* __restrict__ P,
+                                                       float* __restrict__ qrot,
+                                                       float* __restrict__ scores, int Hq, int Hkv,
+                                                       int d, int S, int S_max, int nhb,
+                                                       int chunk, Rope rope) {
+  __shared__ ScoreSmem<D, NH> sm;
+  score_role<E, D, LPS, NH>(slab, q, P, qrot, scores, Hq, Hkv, d, S, S_max, nhb, chunk, rope,
+                            blockIdx.x, blockIdx.y, sm, nullptr, 0ull);
 }
 
 // -------------------------------------------------------------------- topk --
@@ -366,9 +410,130 @@ __global__ void __launch_bounds__(BLOCK) topk_kernel(const float* __restrict__ s
   }
 }
 
+// ------------------------------------------------------- ranking + top-k --
+
+// The ranking pass and the top-k in one launch, for rows of at most
+// kSelectMaxS scores.  Workgroups [0, nscore) are the ranking pass's chunks
+// (unit id % nunits, chunk id / nunits); workgroup nscore + r selects the
+// top k of row r once every chunk of its unit has published its scores.  A
+// selecting workgroup waits only on workgroups of lower index, which are
+// dispatched before it, so the wait needs no co-residency.  The flags of a
+// launch carry its epoch + 1; the epoch, a workspace word, is advanced by the
+// gather launch that follows, so flags left by earlier launches never read
+// as set, nor do the contents of a fresh workspace (short of a 64-bit
+// match), also when a captured graph replays the launches.
+// 16 register keys per thread: the 32-key select would raise the whole
+// kernel's registers past four waves per SIMD, which the ranking pass needs
+constexpr int kSelectMaxS = 16 * kBlock;
+static_assert(kSelectMaxS == kScoreSelectMaxS, "the host's limit of the combined launch");
+// ranking chunks are at least 256 tokens: at most this many per unit (one
+// lane of the waiting wave each)
+constexpr int kSelectMaxChunks = kSelectMaxS / 256;
+static_assert(kSelectMaxChunks <= 64, "one wave polls a unit's flags");
+
+struct SelSmem {
+  SelectSmemR<kBlock> r;
+  unsigned bits[kSelectMaxS / 32];
+};
+
+// Top-k of one score row (srow, published by other workgroups of this
+// launch) into out (kk ascending ids) and, when brow is given, the row's
+// kept-position bitmap.  Gives up after kSpinMax polls: then the ids are -1
+// and err counts it, so a failure shows in every check of the output.
+template <int EMAX, bool LIN>
+__device__ __forceinline__ void select_role(const float* __restrict__ srow, int S, int kk, int* __restrict__ out,
+                            unsigned* __restrict__ brow, const unsigned long long* flags, int nch,
+                            unsigned long long fval, unsigned* err, SelSmem& sm) {
+  const int nw = (S + 31) >> 5;
+  if (brow)
+    for (int i = threadIdx.x; i < nw; i += kBlock) sm.bits[i] = 0u;
+  if (!wait_flags(flags, nch, fval)) {
+    if (threadIdx.x == 0) atomicAdd(err, 1u);
+    for (int p = threadIdx.x; p < kk; p += kBlock) out[p] = -1;
+    if (brow)
+      for (int i = threadIdx.x; i < nw; i += kBlock) brow[i] = 0u;
+    return;
+  }
+  // this thread's E consecutive scores, loaded with device scope
+  const int E = (S + kBlock - 1) / kBlock;
+  const int j0 = threadIdx.x * E;
+  int nvalid = S - j0;
+  nvalid = nvalid < 0 ? 0 : (nvalid > E ? E : nvalid);
+  uint32_t key[EMAX];
+  if ((E & 3) == 0 && (reinterpret_cast<uintptr_t>(srow) & 15) == 0) {
+    const Region rg = make_region(srow, static_cast<uint32_t>(S) * 4u);
+#pragma unroll
+    for (int c = 0; c < EMAX / 4; ++c) {
+      const uint4 v = 4 * c < nvalid ? ld16_dev(rg, static_cast<uint32_t>(j0 + 4 * c) * 4u)
+                                     : make_uint4(0u, 0u, 0u, 0u);
+      key[4 * c] = order_key(__uint_as_float(v.x));
+      key[4 * c + 1] = order_key(__uint_as_float(v.y));
+      key[4 * c + 2] = order_key(__uint_as_float(v.z));
+      key[4 * c + 3] = order_key(__uint_as_float(v.w));
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < EMAX; ++e) key[e] = e < nvalid ? order_key(ld_dev(srow + j0 + e)) : 0u;
+  }
+#pragma unroll
+  for (int e = 0; e < EMAX; ++e)
+    if (e >= nvalid) key[e] = 0u;
+  auto emit = [&](int p, int j) {
+    out[p] = j;
+    if (brow) atomicOr(&sm.bits[j >> 5], 1u << (j & 31));
+  };
+  block_select_topk_keys<kBlock, EMAX, LIN>(key, nvalid, j0, S, kk, emit, sm.r);
+  if (brow) {
+    __syncthreads();
+    for (int i = threadIdx.x; i < nw; i += kBlock) brow[i] = sm.bits[i];
+  }
+}
+
+// sync: [0] the epoch, [1] (low word) the count of given-up waits, [2 ..)
+// the flags, nch per unit.
+template <class E, int D, int LPS, int NH>
+__global__ void __launch_bounds__(kBlock) score_select_kernel(
+    const typename E::T* __restrict__ slab, const typename E::T* __restrict__ q,
+    const float* __restrict__ P, float* __restrict__ qrot, float* __restrict__ scores, int Hq,
+    int Hkv, int d, int S, int S_max, int nhb, int chunk, int nch, int nunits, Rope rope, int kk,
+    int* __restrict__ idx, unsigned* __restrict__ bits, unsigned long long* __restrict__ sync) {
+  __shared__ union {
+    ScoreSmem<D, NH> sc;
+    SelSmem sel;
+  } sm;
+  const unsigned long long fval = ld_dev(sync) + 1ull;
+  unsigned long long* flags = sync + 2;
+  const int nscore = nunits * nch;
+  const int id = blockIdx.x;
+  if (id < nscore) {
+    const int unit = id % nunits, ci = id / nunits;
+    score_role<E, D, LPS, NH>(slab, q, P, qrot, scores, Hq, Hkv, d, S, S_max, nhb, chunk, rope,
+                              unit, ci, sm.sc, flags + static_cast<int64_t>(unit) * nch + ci, fval);
+    return;
+  }
+  const int row = id - nscore;
+  const int G = Hq / Hkv;
+  const int b = row / Hq, h = row % Hq;
+  const int unit = (b * Hkv + h / G) * nhb + (h % G) / NH;
+  const int nw = (S + 31) >> 5;
+  const float* srow = scores + static_cast<int64_t>(row) * S;
+  int* out = idx + static_cast<int64_t>(row) * kk;
+  unsigned* brow = bits ? bits + static_cast<int64_t>(row) * nw : nullptr;
+  const unsigned long long* fl = flags + static_cast<int64_t>(unit) * nch;
+  unsigned* err = reinterpret_cast<unsigned*>(sync + 1);
+  select_role<16, true>(srow, S, kk, out, brow, fl, nch, fval, err, sm.sel);
+}
+
 // ------------------------------------------------------------------ attend --
 
 constexpr int kAttendStage = 2048;  // max kept tokens per attend workgroup
+
+// The gather launch after a combined ranking + top-k launch advances the
+// epoch of the flags (one thread; the launches on either side are ordered
+// by the stream).
+__device__ __forceinline__ void advance_epoch(unsigned long long* epoch) {
+  if (epoch && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *epoch += 1ull;
+}
 
 // Grid (rows, nsplit).  SPARSE: rows = B*Hq, one head per workgroup, tokens
 // are slice `split` of the kept list; the slice's ids and scores are staged
@@ -380,8 +545,9 @@ __global__ void __launch_bounds__(kBlock) attend_kernel(
     const typename E::T* __restrict__ val, const float* __restrict__ qrot,
     const float* __restrict__ scores, const int* __restrict__ idx, float* __restrict__ part,
     float* __restrict__ out, int Hq, int Hkv, int d, int S, int S_max, int kk, int nsplit,
-    int nhb, float scale_log2) {
+    int nhb, float scale_log2, unsigned long long* __restrict__ epoch) {
   using Gm = Geo<E, D>;
+  advance_epoch(epoch);
   constexpr int VEC = Gm::VEC;
   constexpr int LPV = Gm::LPV;
   __shared__ MergeSmem<D, NH, Gm::NG> msm;
@@ -555,8 +721,9 @@ __global__ void __launch_bounds__(kBlock, 4) attend_union_kernel(
     const typename E::T* __restrict__ val, const float* __restrict__ qrot,
     const float* __restrict__ scores, const unsigned* __restrict__ bits, float* __restrict__ part,
     float* __restrict__ out, int Hq, int Hkv, int d, int S, int S_max, int R, int nsplit,
-    float scale_log2) {
+    float scale_log2, unsigned long long* __restrict__ epoch) {
   using Gm = Geo<E, D>;
+  advance_epoch(epoch);
   constexpr int VEC = Gm::VEC;
   constexpr int LPV = Gm::LPV;
   __shared__ UnionSmem<D, NH, Gm::NG> sm;
@@ -683,8 +850,9 @@ __global__ void __launch_bounds__(kBlock, 4) attend_union_mfma_kernel(
     const uint16_t* __restrict__ val, const float* __restrict__ qrot,
     const float* __restrict__ scores, const unsigned* __restrict__ bits,
     float* __restrict__ part, float* __restrict__ out, int Hq, int Hkv, int d, int S, int S_max,
-    int R, int nsplit, float scale_log2) {
+    int R, int nsplit, float scale_log2, unsigned long long* __restrict__ epoch) {
   constexpr int VEC = 8;
+  advance_epoch(epoch);
   constexpr int LPV = D / VEC;     // lanes per value row
   constexpr int GPW = 64 / LPV;    // value rows per wave load
   constexpr int TILE = 16;         // union tokens per wave step
@@ -1043,6 +1211,51 @@ hipError_t score_t(const DecodeArgs& a, float* qrot, float* scores) {
   return hipGetLastError();
 }
 
+template <class E, int D, int LPS>
+hipError_t score_select_t(const DecodeArgs& a, float* qrot, float* scores, int kk,
+                          unsigned* bits) {
+  const int G = a.Hq / a.Hkv;
+  const int nh = G >= 4 ? 4 : (G >= 2 ? 2 : 1);
+  const int nhb = (G + nh - 1) / nh;
+  const int nunits = a.B * a.Hkv * nhb;
+  const int chunk = score_chunk(nunits, a.S);
+  const int nch = (a.S + chunk - 1) / chunk;
+  if (nch > kSelectMaxChunks) return hipErrorInvalidValue;
+  dim3 grid(nunits * nch + a.B * a.Hq);
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, grid, dim3(kBlock), 0, a.stream, cptr<E>(a.k_slab), cptr<E>(a.q), a.P,
+                       qrot, scores, a.Hq, a.Hkv, a.d, a.S, a.S_max, nhb, chunk, nch, nunits,
+                       a.rope, kk, a.idx, bits, a.sync);
+  };
+  if (nh == 4)
+    go(score_select_kernel<E, D, LPS, 4>);
+  else if (nh == 2)
+    go(score_select_kernel<E, D, LPS, 2>);
+  else
+    go(score_select_kernel<E, D, LPS, 1>);
+  return hipGetLastError();
+}
+
+template <class E, int D>
+hipError_t score_select_lps(const DecodeArgs& a, float* qrot, float* scores, int kk,
+                            unsigned* bits) {
+  constexpr int MAXL = D / E::VEC;
+  switch (lps_for(a.d, E::VEC)) {
+    case 1: return score_select_t<E, D, 1>(a, qrot, scores, kk, bits);
+    case 2: return score_select_t<E, D, 2>(a, qrot, scores, kk, bits);
+    case 4: return score_select_t<E, D, 4>(a, qrot, scores, kk, bits);
+    case 8: return score_select_t<E, D, 8>(a, qrot, scores, kk, bits);
+    case 16:
+      if constexpr (MAXL >= 16) return score_select_t<E, D, 16>(a, qrot, scores, kk, bits);
+      break;
+    case 32:
+      if constexpr (MAXL >= 32) return score_select_t<E, D, 32>(a, qrot, scores, kk, bits);
+      break;
+    default: break;
+  }
+  return hipErrorInvalidValue;
+}
+
 template <class E, int D>
 hipError_t score_lps(const DecodeArgs& a, float* qrot, float* scores) {
   constexpr int MAXL = D / E::VEC;
@@ -1065,15 +1278,7 @@ hipError_t score_lps(const DecodeArgs& a, float* qrot, float* scores) {
 hipError_t combine(const DecodeArgs& a, const float* part, int nsplit) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || nsplit == 1) return e;
-  if (nsplit > kCombineMaxSplit) return hipErrorInvalidValue;
-  const size_t lds = static_cast<size_t>(nsplit) * sizeof(float);
-  if (a.D == 64)
-    hipLaunchKernelGGL((combine_kernel<64>), dim3(a.B * a.Hq), dim3(kCombineBlock), lds, a.stream,
-                       part, a.out, nsplit);
-  else
-    hipLaunchKernelGGL((combine_kernel<128>), dim3(a.B * a.Hq), dim3(kCombineBlock), lds,
-                       a.stream, part, a.out, nsplit);
-  return hipGetLastError();
+  return launch_combine(part, a.out, a.B * a.Hq, a.D, nsplit, a.stream);
 }
 
 template <class E, int D, bool SPARSE>
@@ -1087,7 +1292,7 @@ hipError_t attend_t(const DecodeArgs& a, const float* qrot, const float* scores,
     dim3 grid(a.B * a.Hq, nsplit);
     hipLaunchKernelGGL((attend_kernel<E, D, 1, true>), grid, dim3(kBlock), 0, a.stream, sl, rs, vv,
                        qrot, scores, idx, part, a.out, a.Hq, a.Hkv, a.d, a.S, a.S_max, kk,
-                       nsplit, 1, scale_log2);
+                       nsplit, 1, scale_log2, a.sync);
   } else {
     const int G = a.Hq / a.Hkv;
     if constexpr (std::is_same_v<E, BF16>) {
@@ -1100,7 +1305,7 @@ hipError_t attend_t(const DecodeArgs& a, const float* qrot, const float* scores,
         auto go = [&](auto kern) {
           hipLaunchKernelGGL(kern, grid, dim3(kBlock), 0, a.stream, sl, rs, vv, qrot, nullptr,
                              nullptr, part, a.out, a.Hq, a.Hkv, a.d, a.S, a.S_max, R, nsplit,
-                             scale_log2);
+                             scale_log2, nullptr);
         };
         if constexpr (D == 128) {
           if (G == 4)
@@ -1130,15 +1335,15 @@ hipError_t attend_t(const DecodeArgs& a, const float* qrot, const float* scores,
     if (nh == 4)
       hipLaunchKernelGGL((attend_kernel<E, D, 4, false>), grid, dim3(kBlock), 0, a.stream, sl, rs,
                          vv, qrot, scores, idx, part, a.out, a.Hq, a.Hkv, a.d, a.S, a.S_max,
-                         kk, nsplit, nhb, scale_log2);
+                         kk, nsplit, nhb, scale_log2, nullptr);
     else if (nh == 2)
       hipLaunchKernelGGL((attend_kernel<E, D, 2, false>), grid, dim3(kBlock), 0, a.stream, sl, rs,
                          vv, qrot, scores, idx, part, a.out, a.Hq, a.Hkv, a.d, a.S, a.S_max,
-                         kk, nsplit, nhb, scale_log2);
+                         kk, nsplit, nhb, scale_log2, nullptr);
     else
       hipLaunchKernelGGL((attend_kernel<E, D, 1, false>), grid, dim3(kBlock), 0, a.stream, sl, rs,
                          vv, qrot, scores, idx, part, a.out, a.Hq, a.Hkv, a.d, a.S, a.S_max,
-                         kk, nsplit, nhb, scale_log2);
+                         kk, nsplit, nhb, scale_log2, nullptr);
   }
   return combine(a, part, nsplit);
 }
@@ -1158,7 +1363,7 @@ hipError_t union_t(const DecodeArgs& a, const float* qrot, const float* scores,
       auto go = [&](auto kern) {
         hipLaunchKernelGGL(kern, grid, dim3(kBlock), 0, a.stream, cptr<E>(a.k_slab),
                            cptr<E>(a.k_rest), cptr<E>(a.v), qrot, scores, bits, part, a.out, a.Hq,
-                           a.Hkv, a.d, a.S, a.S_max, R, nsplit, scale_log2);
+                           a.Hkv, a.d, a.S, a.S_max, R, nsplit, scale_log2, a.sync);
       };
       if (G == 4) {
         if (nt == 1) go(attend_union_mfma_kernel<D, 4, 1, 0, false>);
@@ -1175,19 +1380,41 @@ hipError_t union_t(const DecodeArgs& a, const float* qrot, const float* scores,
   if (G == 4)
     hipLaunchKernelGGL((attend_union_kernel<E, D, 4>), grid, dim3(kBlock), 0, a.stream,
                        cptr<E>(a.k_slab), cptr<E>(a.k_rest), cptr<E>(a.v), qrot, scores, bits, part,
-                       a.out, a.Hq, a.Hkv, a.d, a.S, a.S_max, R, nsplit, scale_log2);
+                       a.out, a.Hq, a.Hkv, a.d, a.S, a.S_max, R, nsplit, scale_log2, a.sync);
   else
     hipLaunchKernelGGL((attend_union_kernel<E, D, 2>), grid, dim3(kBlock), 0, a.stream,
                        cptr<E>(a.k_slab), cptr<E>(a.k_rest), cptr<E>(a.v), qrot, scores, bits, part,
-                       a.out, a.Hq, a.Hkv, a.d, a.S, a.S_max, R, nsplit, scale_log2);
+                       a.out, a.Hq, a.Hkv, a.d, a.S, a.S_max, R, nsplit, scale_log2, a.sync);
   return combine(a, part, nsplit);
 }
 
 }  // namespace
 
+hipError_t launch_combine(const float* part, float* out, int rows, int D, int nsplit,
+                          hipStream_t stream) {
+  if (nsplit > kCombineMaxSplit) return hipErrorInvalidValue;
+  const size_t lds = static_cast<size_t>(nsplit) * sizeof(float);
+  if (D == 64)
+    hipLaunchKernelGGL((combine_kernel<64>), dim3(rows), dim3(kCombineBlock), lds, stream, part,
+                       out, nsplit);
+  else
+    hipLaunchKernelGGL((combine_kernel<128>), dim3(rows), dim3(kCombineBlock), lds, stream, part,
+                       out, nsplit);
+  return hipGetLastError();
+}
+
 hipError_t launch_rotate(const DecodeArgs& a, float* qrot) {
   if (a.dtype == kF32) return a.D == 64 ? rotate_t<F32, 64>(a, qrot) : rotate_t<F32, 128>(a, qrot);
   return a.D == 64 ? rotate_t<BF16, 64>(a, qrot) : rotate_t<BF16, 128>(a, qrot);
+}
+
+hipError_t launch_score_select(const DecodeArgs& a, float* qrot, float* scores, int kk,
+                               unsigned* bits) {
+  if (a.dtype == kF32)
+    return a.D == 64 ? score_select_lps<F32, 64>(a, qrot, scores, kk, bits)
+                     : score_select_lps<F32, 128>(a, qrot, scores, kk, bits);
+  return a.D == 64 ? score_select_lps<BF16, 64>(a, qrot, scores, kk, bits)
+                   : score_select_lps<BF16, 128>(a, qrot, scores, kk, bits);
 }
 
 hipError_t launch_scores(const DecodeArgs& a, float* qrot, float* scores) {

@@ -210,6 +210,70 @@ __device__ __forceinline__ uint32_t order_key(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// ---- handing data from one workgroup to another within a launch ----------
+//
+// The XCDs have their own L2 caches, which are not kept coherent with each
+// other for ordinary stores and loads.  Data that one workgroup leaves for
+// another of the same launch is therefore stored and loaded with device
+// scope (the store is written through its L2, the load is served
+// coherently), and the hand-over is a device-scope flag set after the
+// producer's stores have completed.  No release fence is used: on this chip
+// it writes back the whole of the producing XCD's L2.
+constexpr int kDevScope = 16;  // cache-policy bits of device-scope buffer accesses
+
+__device__ __forceinline__ void st_dev(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned long long ld_dev(const unsigned long long* p) {
+  return __hip_atomic_load(const_cast<unsigned long long*>(p), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st16_dev(const Region& g, uint32_t off, const uint4& v) {
+  __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{v.x, v.y, v.z, v.w}, g.r, static_cast<int>(off),
+                                         0, kDevScope);
+}
+__device__ __forceinline__ uint4 ld16_dev(const Region& g, uint32_t off) {
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(g.r, static_cast<int>(off), 0, kDevScope);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// Called by every thread of a workgroup after its device-scope stores: once
+// they have all completed, sets *flag = value (device scope).
+__device__ __forceinline__ void publish(unsigned long long* flag, unsigned long long value) {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);  // this thread's stores have been acknowledged
+  __syncthreads();                // ... and every other thread's
+  if (threadIdx.x == 0)
+    __hip_atomic_store(flag, value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Longest wait for other workgroups' flags, in polls of about 0.1 us: far
+// beyond any launch of this library, so only a workgroup that never ran
+// could exhaust it; the waiter then gives up rather than hang.
+constexpr int kSpinMax = 1 << 19;
+
+// Called by every thread of a workgroup: waits until flags[0 .. n) (n <= 64)
+// all equal `value`.  Returns false in every thread if the wait gave up.
+__device__ __forceinline__ bool wait_flags(const unsigned long long* flags, int n,
+                                           unsigned long long value) {
+  __shared__ int ok;
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    bool done = false;
+    for (int spins = 0; !done && spins < kSpinMax; ++spins) {
+      const unsigned long long f = lane < n ? ld_dev(flags + lane) : value;
+      done = __all(f == value);
+      if (!done) __builtin_amdgcn_s_sleep(2);
+    }
+    if (lane == 0) ok = done ? 1 : 0;
+  }
+  __syncthreads();
+  return ok != 0;
+}
+
 // float64 -> bf16 bits, round to nearest, ties to even, done on the bit
 // pattern so that there is a single rounding.
 __device__ __forceinline__ uint16_t f64_to_bf16_rne(double x) {

@@ -33,6 +33,11 @@ struct FusedArgs {
   int B, Hq, Hkv, d, S, S_max, kk, pos;
   float scale_log2;
   Rope rope;  // the query's embedding; STEP embeds the new key at pos
+  // slices per row: nsl workgroups each rank and select the whole row and
+  // gather 1/nsl of its kept tokens, leaving [max, sum, accumulator] partials
+  // in part [rows][nsl][D + 2] for the combine launch (nsl == 1: out directly)
+  int nsl;
+  float* part;
 };
 
 // Eight waves per row: the slab stream and the gather each keep twice the
@@ -81,8 +86,11 @@ __global__ void __launch_bounds__(kFusedBlock, 6) fused_kernel(FusedArgs a) {
   int* ib = reinterpret_cast<int*>(dyn + D + a.S);
 
   const int S = a.S, d = a.d, kk = a.kk;
+  // the slices of a row have consecutive logical ids, so they run on one XCD
+  // and all but the first find the row's slab in its L2
   const int L = xcd_logical(blockIdx.x, gridDim.x);
-  const int h = L / a.B, b = L % a.B;
+  const int slice = L % a.nsl;
+  const int h = (L / a.nsl) / a.B, b = (L / a.nsl) % a.B;
   const int G = a.Hq / a.Hkv;
   const int g = h / G;
   const int64_t row = static_cast<int64_t>(b) * a.Hq + h;
@@ -216,7 +224,9 @@ __global__ void __launch_bounds__(kFusedBlock, 6) fused_kernel(FusedArgs a) {
   }
   __syncthreads();
 
-  // 4. gather + exact attention over the kept tokens
+  // 4. gather + exact attention over this slice of the kept tokens
+  const int per = (kk + a.nsl - 1) / a.nsl;
+  const int t0 = min(kk, slice * per), t1 = min(kk, t0 + per);
   const int r = threadIdx.x % Gm::LPV;
   const int kd0 = r * VEC;
   float qf[1][VEC];
@@ -225,18 +235,27 @@ __global__ void __launch_bounds__(kFusedBlock, 6) fused_kernel(FusedArgs a) {
   Acc<VEC> st[1];
   acc_init(st[0]);
   attend_loop<E, D, 1, true, 4, NT>([&](int t) { return ib[t]; },
-                                [&](int, int, int j) { return sb[j]; }, 0, kk, sl, rs, vv, d,
+                                [&](int, int, int j) { return sb[j]; }, t0, t1, sl, rs, vv, d,
                                 qf, a.scale_log2, st, STEP ? a.pos : -1, kslot, vslot);
   __syncthreads();  // the merge scratch aliases the selection scratch
-  merge_groups<E, D, 1, NT>(st, sc.mrg, [&](int, int dim, float, float Ls, float A) {
-    a.out[row * D + dim] = A / Ls;
+  merge_groups<E, D, 1, NT>(st, sc.mrg, [&](int, int dim, float M, float Ls, float A) {
+    if (a.nsl == 1) {
+      a.out[row * D + dim] = A / Ls;
+    } else {
+      float* pp = a.part + (row * a.nsl + slice) * (D + 2);
+      pp[dim] = A;
+      if (dim == 0) {
+        pp[D] = M;
+        pp[D + 1] = Ls;
+      }
+    }
   });
-  // The row's stores come last (see the selection above): the idx output and,
-  // for STEP, the appended token's cache row (one writer per KV head; this
-  // launch served that token from LDS).
+  // The row's stores come last (see the selection above): this slice's part
+  // of the idx output and, for STEP, the appended token's cache row (one
+  // writer per KV head; this launch served that token from LDS).
   int* irow = a.idx + row * kk;
-  for (int p = threadIdx.x; p < kk; p += NT) irow[p] = ib[p];
-  if (STEP && h % G == 0 && threadIdx.x < D) {
+  for (int p = t0 + threadIdx.x; p < t1; p += NT) irow[p] = ib[p];
+  if (STEP && h % G == 0 && slice == 0 && threadIdx.x < D) {
     const int col = threadIdx.x;
     const int64_t slot = bgo * a.S_max + a.pos;
     if (col < d)
@@ -287,7 +306,7 @@ hipError_t fused_lps(const FusedArgs& fa, size_t lds, hipStream_t stream, int gr
 template <bool STEP>
 hipError_t fused_dispatch(const FusedArgs& fa, int dtype, int D, hipStream_t stream) {
   const size_t lds = fused_lds_bytes(D, fa.S, fa.kk);
-  const int grid = fa.B * fa.Hq;
+  const int grid = fa.B * fa.Hq * fa.nsl;
   if (dtype == kF32)
     return D == 64 ? fused_lps<F32, 64, STEP>(fa, lds, stream, grid)
                    : fused_lps<F32, 128, STEP>(fa, lds, stream, grid);
@@ -316,6 +335,8 @@ FusedArgs fused_args(const DecodeArgs& a, int kk) {
   fa.pos = -1;
   fa.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(a.D)));
   fa.rope = a.rope;
+  fa.nsl = 1;
+  fa.part = nullptr;
   return fa;
 }
 
@@ -325,17 +346,26 @@ size_t fused_lds_bytes(int D, int S, int kk) {
   return (static_cast<size_t>(D) + S + kk) * sizeof(float);
 }
 
-hipError_t launch_fused(const DecodeArgs& a, int kk) {
-  return fused_dispatch<false>(fused_args(a, kk), a.dtype, a.D, a.stream);
+hipError_t launch_fused(const DecodeArgs& a, int kk, int nsl, float* part) {
+  FusedArgs fa = fused_args(a, kk);
+  fa.nsl = nsl;
+  fa.part = part;
+  hipError_t e = fused_dispatch<false>(fa, a.dtype, a.D, a.stream);
+  if (e == hipSuccess && nsl > 1) e = launch_combine(part, a.out, a.B * a.Hq, a.D, nsl, a.stream);
+  return e;
 }
 
 hipError_t launch_fused_step(const DecodeArgs& a, const void* k_new, const void* v_new, int pos,
-                             int kk) {
+                             int kk, int nsl, float* part) {
   FusedArgs fa = fused_args(a, kk);
   fa.k_new = k_new;
   fa.v_new = v_new;
   fa.pos = pos;
-  return fused_dispatch<true>(fa, a.dtype, a.D, a.stream);
+  fa.nsl = nsl;
+  fa.part = part;
+  hipError_t e = fused_dispatch<true>(fa, a.dtype, a.D, a.stream);
+  if (e == hipSuccess && nsl > 1) e = launch_combine(part, a.out, a.B * a.Hq, a.D, nsl, a.stream);
+  return e;
 }
 
 }  // namespace loki

@@ -33,11 +33,25 @@ struct DecodeArgs {
   int* idx;
   hipStream_t stream;
   Rope rope;
+  // workspace words of the combined ranking + top-k launch: [0] epoch, [1]
+  // given-up waits, [2 ..) flags (kScoreSelectFlags per row); nullptr where
+  // that launch is not used
+  unsigned long long* sync = nullptr;
 };
+
+// The combined ranking + top-k launch takes rows of up to this many scores,
+// with at most kScoreSelectFlags ranking chunks per row.
+constexpr int kScoreSelectMaxS = 4096;
+constexpr int kScoreSelectFlags = 16;
 
 hipError_t launch_rotate(const DecodeArgs& a, float* qrot);
 // rotates the queries itself (q' of every query head also stored to qrot)
 hipError_t launch_scores(const DecodeArgs& a, float* qrot, float* scores);
+// the ranking pass and the top-k in one launch (a.S <= kScoreSelectMaxS,
+// a.sync set): scores, a.idx and, when bits is given, the kept-position
+// bitmaps, as launch_scores followed by launch_topk would write them
+hipError_t launch_score_select(const DecodeArgs& a, float* qrot, float* scores, int kk,
+                               unsigned* bits);
 // bits (optional): also write each row's kept-position bitmap, ceil(S/32)
 // words per row, bit j%32 of word j/32 set when token j is kept
 hipError_t launch_topk(const float* scores, int rows, int S, int64_t ld, int k, int* idx,
@@ -55,12 +69,17 @@ constexpr int kUnionMaxS = 1 << 17;
 hipError_t launch_attend_union(const DecodeArgs& a, const float* qrot, const float* scores,
                                const unsigned* bits, float* part, int nsplit);
 size_t fused_lds_bytes(int D, int S, int kk);
-hipError_t launch_fused(const DecodeArgs& a, int kk);
+// nsl > 1: each row's gather split over nsl workgroups (each ranks and
+// selects the whole row), partials in part [B*Hq][nsl][D + 2], then merged
+hipError_t launch_fused(const DecodeArgs& a, int kk, int nsl = 1, float* part = nullptr);
 // append (k_new, v_new [B, Hkv, D]) at pos and decode over a.S = pos + 1;
 // with a.rope.base > 0 the new key is embedded at pos (the query at
 // a.rope.pos)
 hipError_t launch_fused_step(const DecodeArgs& a, const void* k_new, const void* v_new, int pos,
-                             int kk);
+                             int kk, int nsl = 1, float* part = nullptr);
+// log-sum-exp merge of nsplit slice partials [rows][nsplit][D + 2] into out
+hipError_t launch_combine(const float* part, float* out, int rows, int D, int nsplit,
+                          hipStream_t stream);
 
 // rope_base > 0: new token t is embedded at position pos + t before rotating
 hipError_t launch_append(const void* k_new, const void* v_new, const float* P, void* k_slab,

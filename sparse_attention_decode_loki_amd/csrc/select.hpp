@@ -381,23 +381,16 @@ __device__ __forceinline__ bool linear_select(const uint32_t (&key)[EMAX], int n
   return true;
 }
 
-template <int BLOCK, int EMAX, bool LIN = false, class Src, class Emit>
-__device__ void block_select_topk_reg(Src src, int S, int k, Emit emit, SelectSmemR<BLOCK>& sm) {
+// The selection of block_select_topk_reg once the keys are in registers:
+// the calling thread's key[e] (e < nvalid) is element j0 + e, with j0 =
+// threadIdx.x * ceil(S / BLOCK).
+template <int BLOCK, int EMAX, bool LIN = false, class Emit>
+__device__ __forceinline__ void block_select_topk_keys(const uint32_t (&key)[EMAX], int nvalid, int j0, int S,
+                                       int k, Emit emit, SelectSmemR<BLOCK>& sm) {
   constexpr int PER = kSelBins / BLOCK;  // histogram bins owned per thread in the scan
   static_assert(kSelBins % BLOCK == 0, "bins must split evenly");
   static_assert(!LIN || BLOCK >= kLinCap, "one thread per ranked key");
   const int tid = threadIdx.x;
-  const int E = (S + BLOCK - 1) / BLOCK;
-  const int j0 = tid * E;
-  uint32_t key[EMAX];
-#pragma unroll
-  for (int e = 0; e < EMAX; ++e) {
-    const int j = j0 + e;
-    key[e] = (e < E && j < S) ? order_key(src(j)) : 0u;
-  }
-  int nvalid = S - j0;
-  nvalid = nvalid < 0 ? 0 : (nvalid > E ? E : nvalid);
-
   uint32_t prefix = 0u, mask = 0u;
   int krem = k;
   int buf = 0;
@@ -445,6 +438,21 @@ __device__ void block_select_topk_reg(Src src, int S, int k, Emit emit, SelectSm
   }
 
   emit_kept<BLOCK, EMAX>(key, nvalid, prefix, mask, krem, j0, emit, sm, buf);
+}
+
+template <int BLOCK, int EMAX, bool LIN = false, class Src, class Emit>
+__device__ void block_select_topk_reg(Src src, int S, int k, Emit emit, SelectSmemR<BLOCK>& sm) {
+  const int E = (S + BLOCK - 1) / BLOCK;
+  const int j0 = threadIdx.x * E;
+  uint32_t key[EMAX];
+#pragma unroll
+  for (int e = 0; e < EMAX; ++e) {
+    const int j = j0 + e;
+    key[e] = (e < E && j < S) ? order_key(src(j)) : 0u;
+  }
+  int nvalid = S - j0;
+  nvalid = nvalid < 0 ? 0 : (nvalid > E ? E : nvalid);
+  block_select_topk_keys<BLOCK, EMAX, LIN>(key, nvalid, j0, S, k, emit, sm);
 }
 
 }  // namespace loki

@@ -98,12 +98,22 @@ def test_auto_takes_fused_by_rows_and_context(L):
     lib = L.load()
     assert lib.loki_decode_path(1, 1, 1, 128, 32, 2222, 555, 1, 0) == 1    # short rows: any count
     assert lib.loki_decode_path(1, 1, 1, 128, 32, 2223, 555, 1, 0) == 2
-    assert lib.loki_decode_path(1, 87, 87, 128, 32, 4096, 1024, 1, 0) == 2
-    assert lib.loki_decode_path(1, 88, 88, 128, 32, 4096, 1024, 1, 0) == 1
+    assert lib.loki_decode_path(1, 87, 87, 128, 32, 4097, 1024, 1, 0) == 2
+    assert lib.loki_decode_path(1, 88, 88, 128, 32, 4097, 1024, 1, 0) == 1
     assert lib.loki_decode_path(1, 138, 138, 128, 32, 8192, 2048, 1, 0) == 2
     assert lib.loki_decode_path(1, 139, 139, 128, 32, 8192, 2048, 1, 0) == 1
     assert lib.loki_decode_path(1, 190, 190, 128, 32, 11000, 2750, 1, 0) == 1
     assert lib.loki_decode_path(2, 4, 2, 128, 32, 500, 125, 1, 0) != 1     # grouped heads: never
+
+
+def test_auto_takes_sliced_for_48_to_128_rows_of_up_to_4096(L):
+    lib = L.load()
+    assert lib.loki_decode_path(1, 47, 47, 128, 32, 4096, 1024, 1, 0) == 2
+    assert lib.loki_decode_path(1, 48, 48, 128, 32, 4096, 1024, 1, 0) == 4
+    assert lib.loki_decode_path(2, 64, 64, 128, 32, 4096, 1024, 1, 0) == 4   # 128 rows
+    assert lib.loki_decode_path(1, 129, 129, 128, 32, 4096, 1024, 1, 0) == 1
+    assert lib.loki_decode_path(2, 32, 32, 128, 32, 4097, 1024, 1, 0) == 2
+    assert lib.loki_decode_path(2, 32, 8, 128, 32, 4096, 1024, 1, 0) != 4    # grouped heads
 
 
 def test_union_path_only_for_two_or_four_heads_per_kv_head(L):
@@ -114,10 +124,21 @@ def test_union_path_only_for_two_or_four_heads_per_kv_head(L):
     assert lib.loki_decode_path(2, 16, 2, 128, 32, 700, 100, 1, 3) == -4     # G = 8
     assert lib.loki_decode_path(1, 4, 1, 128, 32, 1 << 17, 100, 1, 3) == 3
     assert lib.loki_decode_path(1, 4, 1, 128, 32, (1 << 17) + 1, 100, 1, 3) == -4
-    assert lib.loki_decode_path(1, 4, 1, 128, 32, 100, 10, 1, 4) == -1       # no such path
+    assert lib.loki_decode_path(1, 4, 1, 128, 32, 100, 10, 1, 5) == -1       # no such path
     # rejected before any pointer is looked at
     assert _decode(lib, Hq=4, Hkv=4, path=3) == -4
-    assert _decode(lib, path=4) == -1
+    assert _decode(lib, path=5) == -1
+
+
+def test_sliced_path_needs_the_fused_kernels_lds(L):
+    # the sliced path runs the single-kernel decode with each row's gather
+    # split: same LDS limit as FUSED, (D + S + min(k, S)) floats <= 56 KiB
+    lib = L.load()
+    assert lib.loki_decode_path(1, 32, 32, 128, 32, 4096, 1024, 1, 4) == 4
+    assert lib.loki_decode_path(1, 2, 2, 128, 32, 11000, 3208, 1, 4) == 4
+    assert lib.loki_decode_path(1, 2, 2, 128, 32, 11000, 3209, 1, 4) == -4
+    # it needs a workspace (for its slice partials) when a row has several slices
+    assert _decode(lib, Hq=4, Hkv=4, S=100, S_max=128, k=100, path=4, ws=None, wsb=0) == -2
 
 
 def test_empty_batch_is_a_noop(L):

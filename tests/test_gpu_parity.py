@@ -253,12 +253,12 @@ def test_attend_given_indices_matches_oracle(lib, name):
 
 # ------------------------------------------------------------- end to end --
 
-@pytest.mark.parametrize("path", [1, 2, 3], ids=["fused", "split", "union"])
+@pytest.mark.parametrize("path", [1, 2, 3, 4], ids=["fused", "split", "union", "sliced"])
 @pytest.mark.parametrize("name", sorted(SMALL))
 def test_decode_matches_oracle(lib, name, path):
     c = case(name)
     kk = min(c.k, c.S)
-    if path == 1 and (c.w.D + c.S + kk) * 4 > 56 * 1024:
+    if path in (1, 4) and (c.w.D + c.S + kk) * 4 > 56 * 1024:
         pytest.skip("fused path needs q', scores and kept ids within 56 KiB of LDS")
     if path == 3 and not union_applies(c.w):
         pytest.skip("union gather needs 2 or 4 query heads per KV head")
@@ -275,7 +275,7 @@ def test_decode_budget_edges(lib, k):
     c = case("ragged_gqa2")
     cache = device_cache(lib, c)
     ref_out, ref_idx, ref_s = oracle.decode(c.q, c.slab, c.rest, c.v, c.P, k, c.w.dtype, S=c.S)
-    for path in (1, 2, 3):
+    for path in (1, 2, 3, 4):
         out, idx = lib.decode(_q(c), cache, _P(c), k, path=path)
         check_decode(c.w.dtype, k, out.cpu().numpy(), idx.cpu().numpy(), ref_out, ref_idx, ref_s,
                      all_pairs(c.w), src_of(c))
@@ -287,7 +287,7 @@ def test_decode_shorter_S_than_filled(lib):
     cache = device_cache(lib, c)
     S = 1234
     ref_out, ref_idx, ref_s = oracle.decode(c.q, c.slab, c.rest, c.v, c.P, 300, c.w.dtype, S=S)
-    for path in (1, 2, 3):
+    for path in (1, 2, 3, 4):
         out, idx = lib.decode(_q(c), cache, _P(c), 300, S=S, path=path)
         check_decode(c.w.dtype, 300, out.cpu().numpy(), idx.cpu().numpy(), ref_out, ref_idx,
                      ref_s, all_pairs(c.w), src_of(c))
@@ -301,6 +301,9 @@ def test_decode_deterministic_and_paths_agree(lib):
     o3, i3 = lib.decode(_q(c), cache, _P(c), c.k, path=1)
     o4, i4 = lib.decode(_q(c), cache, _P(c), c.k, path=3)
     o5, _ = lib.decode(_q(c), cache, _P(c), c.k, path=3)
+    o6, i6 = lib.decode(_q(c), cache, _P(c), c.k, path=4)
+    assert np.array_equal(i1.cpu().numpy(), i6.cpu().numpy())
+    assert np.max(np.abs(o1.cpu().numpy() - o6.cpu().numpy())) < 1e-5
     assert np.array_equal(o1.cpu().numpy(), o2.cpu().numpy())
     assert np.array_equal(i1.cpu().numpy(), i2.cpu().numpy())
     assert np.array_equal(o4.cpu().numpy(), o5.cpu().numpy())
@@ -452,7 +455,7 @@ def _oracle_token(w, P, kn, vn):
     return slab, rest, vv
 
 
-@pytest.mark.parametrize("path", [1, 2, 3], ids=["fused", "split", "union"])
+@pytest.mark.parametrize("path", [1, 2, 3, 4], ids=["fused", "split", "union", "sliced"])
 @pytest.mark.parametrize("name", sorted(STEP_CASES))
 def test_decode_step_matches_oracle(lib, name, path):
     """Append at pos = S-1 and decode over S tokens in one call; the written
@@ -568,7 +571,7 @@ def test_stream_read_probe_reads_every_element(lib):
         assert got == float((torch.arange(n, dtype=torch.float64) % 7).sum())
 
 
-@pytest.mark.parametrize("path", [2, 3], ids=["split", "union"])
+@pytest.mark.parametrize("path", [2, 3, 4], ids=["split", "union", "sliced"])
 def test_split_paths_ignore_stale_workspace(lib, path):
     """The split and union paths read nothing from the workspace that the same
     call did not write: a workspace full of NaN bit patterns and a zeroed one
@@ -603,7 +606,7 @@ def test_per_layer_slab_width(lib):
 
 # ------------------------------------------------------------ graph capture --
 
-@pytest.mark.parametrize("path", [1, 2, 3], ids=["fused", "split", "union"])
+@pytest.mark.parametrize("path", [1, 2, 3, 4], ids=["fused", "split", "union", "sliced"])
 def test_decode_replays_from_a_captured_graph(lib, path):
     """Each path launches only kernels (no allocation, no memset), so a decode
     captured into a HIP graph replays correctly: three replays, with eager
