@@ -267,7 +267,7 @@ def main():
     step_bytes = by["total"] + w.B * w.Hkv * (2 * w.D + 2 * w.D) * w.esize
     achieved = step_bytes / (step_avg_ms * 1e-3) / 1e9
     khash = kernel_source_hash()
-    path_name = {1: "fused", 2: "split", 3: "union"}[
+    path_name = PATH_NAMES[
         loki.decode_path(w.B, w.Hq, w.Hkv, w.D, w.d, S, k, w.dtype, args.path)]
     overridden = args.kf is not None or args.df is not None
     traffic = (measured_traffic(khash, args.config)
@@ -447,18 +447,46 @@ def topk_agreement(loki, w, S, k, K_raw, V_raw, kn, vn, q, Pd, up, dev, rb=None)
     return res
 
 
+PATH_NAMES = {1: "fused", 2: "split", 3: "union", 4: "sliced"}
+PATH_CODES = {v: c for c, v in PATH_NAMES.items()}
+COMPUTE_UNITS = 256
+
+
+def sliced_slices(rows, kk) -> int:
+    """Workgroups per sliced row of the sliced path (the library's plan: for
+    fewer rows than compute units, the fewest slices that bring the busiest
+    CU's share of rows within 10% of the best any allowed count gives; past
+    whole rounds of the CUs, slices of a remainder of at most 64 rows that
+    give every CU one more workgroup).  Used only to count the bytes of the
+    score exchange."""
+    cap = min(16, -(-kk // 64))
+    if rows < COMPUTE_UNITS:
+        sparse = max(min(-(-1024 // rows), -(-kk // 64)), -(-kk // 2048), 1)
+        nmax = max(1, min(cap, sparse))
+        load = [(-(-rows * n // COMPUTE_UNITS)) / n for n in range(1, nmax + 1)]
+        return next(n for n in range(1, nmax + 1) if load[n - 1] <= 1.1 * min(load))
+    rem = rows % COMPUTE_UNITS
+    if rows % 8 or rem == 0 or rem > 64:
+        return 1
+    return max(1, min(COMPUTE_UNITS // rem, cap))
+
+
 def design_bytes(w, S, k, path, idx) -> int:
     """HBM bytes the chosen path's kernels move by their design, from the
     selections the decode actually made (idx [B, Hq, k] on the host): the
-    slab once per KV head (once per query head on the fused path, where the
-    two are equal), the kept tokens' rest and value rows (each query head's
-    own on the fused and split paths, each KV head's union of its query heads'
-    on the union path; the slab dims of a kept key are never re-read), the
-    ids, and on the split and union paths the float32 score rows written and
-    read back."""
+    slab once per KV head (once per query head on the fused and sliced
+    paths), the kept tokens' rest and value rows (each query head's own on
+    the fused, sliced and split paths, each KV head's union of its query
+    heads' on the union path; the slab dims of a kept key are never re-read),
+    the ids, on the split and union paths the float32 score rows written and
+    read back, and on the sliced path the float32 scores and partials its
+    slices exchange (each slice's share written once, read by the row's
+    other slices; counted although they may be served by the last-level
+    cache)."""
     e = w.esize
     row = (2 * w.D - w.d) * e
-    total = w.B * w.Hkv * S * w.d * e + w.B * w.Hq * k * 4
+    slab_heads = w.Hq if path in ("fused", "sliced") else w.Hkv
+    total = w.B * slab_heads * S * w.d * e + w.B * w.Hq * k * 4
     if path == "union":
         G = w.Hq // w.Hkv
         for b in range(w.B):
@@ -466,8 +494,13 @@ def design_bytes(w, S, k, path, idx) -> int:
                 total += np.unique(idx[b, g * G:(g + 1) * G]).size * row
     else:
         total += w.B * w.Hq * k * row
-    if path != "fused":
+    if path in ("split", "union"):
         total += 2 * w.B * w.Hq * S * 4
+    if path == "sliced":
+        rows = w.B * w.Hq
+        nsl = sliced_slices(rows, k)
+        sliced_rows = 0 if nsl == 1 else (rows if rows < COMPUTE_UNITS else rows % COMPUTE_UNITS)
+        total += sliced_rows * (S * 4 * nsl + 2 * (nsl - 1) * (w.D + 2) * 4)
     return int(total)
 
 
@@ -516,7 +549,7 @@ def measure_config(loki, torch, name, dev, steps, warmup, log) -> dict:
     idx = torch.empty((w.B, w.Hq, k), dtype=torch.int32, device=dev)
     ws = loki.alloc_workspace(w.B, w.Hq, S, w.D, k, dev)
     code = loki.decode_path(w.B, w.Hq, w.Hkv, w.D, w.d, S, k, w.dtype, loki.PATH_AUTO)
-    path = {1: "fused", 2: "split", 3: "union"}[code]
+    path = PATH_NAMES[code]
 
     def run(p):
         plans = [loki.DecodePlan(qs[i % R], caches[i % L], Pd, k, S=S, out=out, idx=idx,
@@ -540,10 +573,15 @@ def measure_config(loki, torch, name, dev, steps, warmup, log) -> dict:
            "path_design_bytes": moved,
            "path_design_GBs": moved / (dec_ms * 1e-3) / 1e9,
            "layers_cycled": L}
-    if w.Hq // w.Hkv in (2, 4) and path in ("split", "union"):
-        other = "union" if path == "split" else "split"
-        oms = run(loki.PATH_UNION if other == "union" else loki.PATH_SPLIT)
-        res[f"{other}_gather_us"] = oms * 1e3
+    # the other paths this shape supports, on the same caches
+    for other in ("fused", "sliced", "split", "union"):
+        if other == path:
+            continue
+        try:
+            loki.decode_path(w.B, w.Hq, w.Hkv, w.D, w.d, S, k, w.dtype, PATH_CODES[other])
+        except loki.LokiError:
+            continue
+        res[f"{other}_us"] = run(PATH_CODES[other]) * 1e3
     dws = loki.alloc_workspace(w.B, w.Hq, S, w.D, 1, dev)
     dplans = [loki.DensePlan(qs[i % R], caches[i % L], Pd, S=S, out=out, workspace=dws)
               for i in range(n_plans)]

@@ -66,29 +66,34 @@ typedef enum { LOKI_F32 = 0, LOKI_BF16 = 1 } loki_dtype;
 /* Execution path of loki_decode_ex.  AUTO picks one by shape and dtype
  * (loki_decode_path reports which).  FUSED runs one kernel per (sequence,
  * query head) that scores, selects and attends with the scores held in LDS
- * (requires (D + S + min(k, S)) * 4 bytes <= 56 KiB); AUTO takes it for one
- * query head per KV head when rows = B * Hq satisfies rows * S + 420000 >=
- * 190 * S (any rows for S <= 2222, at least 88 rows at S = 4096, 139 at
- * S = 8192, never more than 190).  SPLIT runs
- * separate score, selection and attention kernels through the workspace; its
- * attention reads each query head's kept rows, with the query heads of one
- * KV head scheduled together so that rows several of them kept are served
- * from cache.  UNION is SPLIT with a grouped-query gather (Hq/Hkv of 2 or 4,
- * S <= 131072, else LOKI_EUNSUPPORTED): per KV head and position range, the
- * union of its query heads' kept tokens is loaded once and all heads'
- * products are formed over it (on the matrix cores for bf16 caches).  AUTO
- * takes it for bf16 caches with d >= D - 96 when, even for independently
- * selecting heads, the union, a fraction 1 - (1 - k/S)^G of the positions,
- * is at most 3/4 of the G*k/S per-head reads.  SLICED is FUSED with each
- * row's gather split over several workgroups (each ranks and selects the
- * whole row, then gathers its share of the kept tokens; the shares are
- * merged by a second launch through the workspace, which it then needs);
- * AUTO takes it for one query head per KV head at 48 to 128 rows of at most
- * 4096 tokens.  For rows of at most 4096 tokens the SPLIT and UNION paths
- * rank and select in one launch (the selecting workgroups wait for the
- * ranking workgroups of their row; the workspace's first bytes hold the
- * flags and epoch of that hand-over, which any contents of a fresh
- * workspace leave valid).  All paths compute the same function. */
+ * (requires (D + S + min(k, S)) * 4 bytes <= 56 KiB).  SLICED is FUSED with
+ * some rows split over several workgroups ("slices"): the slices of a row
+ * each rank a share of its tokens and exchange the scores through the
+ * workspace, each selects the whole row and gathers a share of the kept
+ * tokens, and the row's last slice merges the shares, all in one launch.
+ * Rows are sliced when there are fewer rows (B * Hq) than the GPU's 256
+ * compute units (enough slices to spread the rows evenly over them), and
+ * past whole rounds of 256 rows a remainder of at most 64 rows (rows a
+ * multiple of 8), sliced to give every compute unit one more workgroup;
+ * otherwise SLICED runs as FUSED.  It needs the workspace whenever it
+ * slices.  SPLIT runs separate score, selection and attention kernels
+ * through the workspace; its attention reads each query head's kept rows,
+ * with the query heads of one KV head scheduled together so that rows
+ * several of them kept are served from cache.  UNION is SPLIT with a
+ * grouped-query gather (Hq/Hkv of 2 or 4, S <= 131072, else
+ * LOKI_EUNSUPPORTED): per KV head and position range, the union of its
+ * query heads' kept tokens is loaded once and all heads' products are
+ * formed over it (on the matrix cores for bf16 caches).  For rows of at
+ * most 4096 tokens the SPLIT and UNION paths rank and select in one launch
+ * (the selecting workgroups wait for the ranking workgroups of their row).
+ * The workspace's first bytes hold the flags and epochs of these hand-overs
+ * within a launch, which any contents of a fresh workspace leave valid.
+ * AUTO, where FUSED's LDS fits: SLICED when it slices and S >= 2048, else
+ * FUSED when rows * S + 420000 >= 190 * S.  Otherwise UNION for bf16 caches
+ * with d >= D - 96 when, even for independently selecting heads, the
+ * union, a fraction 1 - (1 - k/S)^G of the positions, is at most 3/4 of
+ * the G*k/S per-head reads; else SPLIT.  All paths compute the same
+ * function. */
 typedef enum {
   LOKI_PATH_AUTO = 0,
   LOKI_PATH_FUSED = 1,
@@ -273,14 +278,14 @@ int loki_dense_decode_rope(const void* q, const void* k_slab, const void* k_rest
  *
  * For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): this
- * variant of loki_decode_ex takes no workspace.  Its split and union paths
- * use instead a scratch array that the library holds in device memory, one
- * copy of LOKI_NOALLOC_SCRATCH_BYTES per GPU it runs on, from the first call
- * on that GPU (which looks up the array's address with that GPU current;
- * later calls allocate nothing and call no allocating routine) until the
- * process ends.  The GPU is the current device, which must be the one
- * `stream` belongs to.  No kernel relies on the scratch's contents at entry.
- * Every call on a GPU shares that GPU's array, so calls whose work overlaps
+ * variant of loki_decode_ex takes no workspace.  Its sliced, split and
+ * union paths use instead a scratch array that the library holds in device
+ * memory, one copy of LOKI_NOALLOC_SCRATCH_BYTES per GPU it runs on, from
+ * the first call on that GPU (which looks up the array's address with that
+ * GPU current; later calls allocate nothing and call no allocating routine)
+ * until the process ends.  The GPU is the current device, which must be the
+ * one `stream` belongs to.  No result depends on the scratch's contents at
+ * entry.  Every call on a GPU shares that GPU's array, so calls whose work overlaps
  * on one GPU (different streams, different host threads without ordering)
  * race and give undefined results; calls ordered on one stream are safe.
  * Arguments, path choice and results are those of loki_decode_ex; sizes

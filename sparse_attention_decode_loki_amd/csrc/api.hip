@@ -60,18 +60,21 @@ int dense_nsplit(int B, int Hq, int Hkv, int S) {
 }
 
 struct Layout {
-  size_t sync, qrot, scores, part, bits, total;
+  size_t sync, coop, qrot, scores, part, bits, total;
 };
 
 // sync (the combined ranking + top-k launch's epoch, given-up count and
 // flags; first, so the epoch sits at the same offset for every shape) |
-// qrot [B*Hq, D] | scores [B*Hq, S_max] | split partials |
-// kept-position bitmaps [B*Hq, ceil(S_max/32)] (union gather)
+// coop (the sliced single-kernel path's given-up count, epochs and flags) |
+// qrot [B*Hq, D] | scores [B*Hq, S_max] (also the sliced path's score
+// exchange) | split partials | kept-position bitmaps [B*Hq, ceil(S_max/32)]
+// (union gather)
 Layout layout(int B, int Hq, int D, int S_max, int nsplit) {
   Layout L;
   const size_t rows = static_cast<size_t>(B) * Hq;
   L.sync = 0;
-  L.qrot = align256((2 + rows * loki::kScoreSelectFlags) * sizeof(unsigned long long));
+  L.coop = align256((2 + rows * loki::kScoreSelectFlags) * sizeof(unsigned long long));
+  L.qrot = L.coop + align256((1 + rows * loki::kCoopStride) * sizeof(unsigned long long));
   L.scores = L.qrot + align256(rows * D * sizeof(float));
   L.part = L.scores + align256(rows * static_cast<size_t>(S_max) * sizeof(float));
   L.bits = L.part + align256(rows * static_cast<size_t>(nsplit) * (D + 2) * sizeof(float));
@@ -89,16 +92,45 @@ bool valid_path(int path) {
          path == LOKI_PATH_UNION || path == LOKI_PATH_SLICED;
 }
 
-// Slices per row of the sliced single-kernel path: enough workgroups for
-// about kSlicedTarget in all, at least 64 kept tokens per slice, and never
-// more than the split path's slices (which size the workspace).
-#ifndef LOKI_SLICED_TARGET
-#define LOKI_SLICED_TARGET 512
+// The sliced single-kernel path's split of the rows over workgroups
+// (slices of one row share its ranking, so slicing moves no extra bytes,
+// but each slice repeats the row's selection).  Fewer rows than compute
+// units: every row in nsl slices, the fewest that bring the busiest CU's
+// share of rows, ceil(rows * nsl / CUs) / nsl, within 10% of the least
+// any allowed count gives (32 rows: 8 slices, one workgroup per CU; 16
+// slices, two per CU, measure slower), at least 64 kept tokens per slice.  More rows: whole rows for
+// whole rounds of the compute units, and a remainder of at most
+// kSlicedTail rows in slices that give every CU one more workgroup (a
+// larger remainder measures slower sliced).  The partials fit the split
+// path's workspace: rows * nsl <= rows * sparse_nsplit(rows, kk) for few
+// rows, and (rows - nfull) * nsl <= kComputeUnits <= rows otherwise.
+#ifndef LOKI_SLICED_TAIL
+#define LOKI_SLICED_TAIL 64
 #endif
-constexpr int kSlicedTarget = LOKI_SLICED_TARGET;
-int sliced_n(int rows, int kk) {
-  const int n = std::min(cdiv(kSlicedTarget, rows), cdiv(kk, 64));
-  return std::max(1, std::min(n, sparse_nsplit(rows, kk)));
+constexpr int kSlicedTail = LOKI_SLICED_TAIL;
+constexpr int kComputeUnits = 256;  // MI355X
+loki::FusedSlices sliced_plan(int rows, int kk) {
+  loki::FusedSlices fs;
+  fs.coop = true;
+  const int cap = std::min(loki::kCoopMaxSlices, cdiv(kk, 64));
+  if (rows < kComputeUnits) {
+    const int nmax = std::max(1, std::min(cap, sparse_nsplit(rows, kk)));
+    // the busiest CU's share of rows with n slices, times 256 * 2^20 / rows
+    auto load = [&](int n) {
+      return (static_cast<int64_t>(cdiv(static_cast<int64_t>(rows) * n, kComputeUnits)) << 28) / n;
+    };
+    int64_t best = load(1);
+    for (int n = 2; n <= nmax; ++n) best = std::min(best, load(n));
+    int n = 1;
+    while (10 * load(n) > 11 * best) ++n;
+    fs.nsl = n;
+    return fs;
+  }
+  const int rem = rows % kComputeUnits;
+  if (rows % 8 != 0 || rem == 0 || rem > kSlicedTail) return fs;  // whole rows
+  fs.nsl = std::max(1, std::min(kComputeUnits / rem, cap));
+  fs.nfull = fs.nsl > 1 ? rows - rem : 0;
+  return fs;
 }
 
 int max_nsplit(int B, int Hq, int S_max, int k_max) {
@@ -170,16 +202,19 @@ bool fused_fits(int D, int S, int kk) {
   return loki::fused_lds_bytes(D, S, kk) <= loki::kFusedLdsMax;
 }
 
-// The fused kernel reads the key slab once per query head, so it is chosen
-// only for one query head per KV head, and when its LDS fits.  One
-// workgroup streams a whole row: its time grows with S but hardly with the
-// number of rows while they fit on the chip, about 8.7 + 0.0051 * S us.  The
-// split path's four launches cost about 20 us plus 2.7e-5 us per row and
-// token.  Fused is faster when rows > 190 - 420000 / S (measured, bf16,
-// D = 128, d = 32, k = S/4: split wins at 64 rows of 4096 and 128 rows of
-// 8192, fused at 96 and 192).
+// The fused kernel, when its LDS fits.  One workgroup streams a whole row:
+// its time grows with S but hardly with the number of rows while they fit
+// on the chip, about 8.7 + 0.0051 * S us; the split path costs about 20 us
+// plus 2.7e-5 us per row and token.  Fused is faster when rows > 190 -
+// 420000 / S (measured, bf16, D = 128, d = 32, k = S/4: split wins at 64
+// rows of 4096 and 128 rows of 8192, fused at 96 and 192).  With grouped
+// query heads it reads each KV head's slab once per query head, but the G
+// workgroups of one KV head run on one XCD and share it in L2: at 256 and
+// 512 rows of G = 4 it beats the union gather (Llama3-8B shape, 8 x 32
+// heads of 8192: 58.6 against 63.3 us; 16 x 32 of 4096: 55.7 against 60.6).
 bool auto_fused(int B, int Hq, int Hkv, int D, int S, int kk) {
-  if (Hq != Hkv || !fused_fits(D, S, kk)) return false;
+  (void)Hkv;
+  if (!fused_fits(D, S, kk)) return false;
   const int64_t rows = static_cast<int64_t>(B) * Hq;
   return rows * S + 420000 >= 190LL * S;
 }
@@ -198,14 +233,21 @@ bool auto_union(int Hq, int Hkv, int D, int d, int S, int kk, int dtype) {
   return 1.0 - std::pow(1.0 - f, G) <= 0.75 * G * f;
 }
 
-// The sliced single-kernel path for one query head per KV head at 48..128
-// rows of at most 4096 tokens, where it measures faster than both the fused
-// and the split path (bf16, D = 128, d = 32, k = S/4: 64 rows of 4096 26.1 us
-// against split 27.7; 128 rows 32.4 against fused 33.8; at 32 rows, 160 rows
-// of 3584 and rows of 8192 it is slower).
+// The sliced single-kernel path wherever its plan slices rows (fewer rows
+// than CUs, or a remainder of at most kSlicedTail rows past whole rounds)
+// and rows hold at least 2048 tokens, when its LDS fits.  Measured (bf16,
+// D = 128, d = 32, k = S/4, us): 32 rows of 4096 18.3 against split 22.2,
+// fused 30.3 and dense 22.1; 64 rows 21.4 against split 27.8; 128 rows
+// 28.2 against fused 33.9; 32 rows of 8192 24.0 against split 30.6; 288
+// rows of 3584 37.9 against fused 44.8, 576 rows 67.3 against 72.0; 32
+// query heads on 8 KV heads, 32 rows of 4096, 16.9 against split 23.6 and
+// union 25.9.  Shorter rows give the slices too little to rank: 128 rows
+// of 1024 16.8 against fused 15.4.
 bool auto_sliced(int B, int Hq, int Hkv, int D, int S, int kk) {
+  (void)Hkv;
   const int64_t rows = static_cast<int64_t>(B) * Hq;
-  return Hq == Hkv && fused_fits(D, S, kk) && S <= 4096 && rows >= 48 && rows <= 128;
+  return fused_fits(D, S, kk) && S >= 2048 && rows <= (1 << 30) &&
+         sliced_plan(static_cast<int>(rows), kk).nsl > 1;
 }
 
 // The path AUTO resolves to.
@@ -236,6 +278,23 @@ int append_impl(const void* k_new, const void* v_new, const float* P, void* k_sl
 }
 
 
+// The sliced path's plan and its workspace regions (any slicing needs the
+// workspace: partials, the score exchange and the hand-over flags).
+int sliced_slices(int B, int Hq, int D, int S_max, int kk, void* workspace, size_t ws_bytes,
+                  loki::FusedSlices& fs) {
+  const int rows = B * Hq;
+  fs = sliced_plan(rows, kk);
+  if (fs.nsl == 1) return LOKI_OK;
+  // partials of the sliced rows only, as many as nsplit per row would hold
+  const Layout L = layout(B, Hq, D, S_max, cdiv(static_cast<int64_t>(rows - fs.nfull) * fs.nsl, rows));
+  if (!workspace || ws_bytes < L.total || !aligned16(workspace)) return LOKI_EWORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  fs.part = reinterpret_cast<float*>(ws + L.part);
+  fs.xsc = reinterpret_cast<float*>(ws + L.scores);
+  fs.sync = reinterpret_cast<unsigned long long*>(ws + L.coop);
+  return LOKI_OK;
+}
+
 int decode_impl(const void* q, const void* k_slab, const void* k_rest, const void* v,
                 const float* P, int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t d,
                 int32_t S, int32_t S_max, int32_t k, int32_t dtype, float* out, int32_t* idx,
@@ -259,14 +318,12 @@ int decode_impl(const void* q, const void* k_slab, const void* k_rest, const voi
   const int rows = B * Hq;
   if (path == LOKI_PATH_FUSED || path == LOKI_PATH_SLICED) {
     if (!fused_fits(D, S, kk)) return LOKI_EUNSUPPORTED;
-    const int nsl = path == LOKI_PATH_SLICED ? sliced_n(rows, kk) : 1;
-    float* part = nullptr;
-    if (nsl > 1) {
-      const Layout L = layout(B, Hq, D, S_max, nsl);
-      if (!workspace || ws_bytes < L.total || !aligned16(workspace)) return LOKI_EWORKSPACE;
-      part = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.part);
+    loki::FusedSlices fs;
+    if (path == LOKI_PATH_SLICED) {
+      st = sliced_slices(B, Hq, D, S_max, kk, workspace, ws_bytes, fs);
+      if (st != LOKI_OK) return st;
     }
-    return status_of(loki::launch_fused(a, kk, nsl, part));
+    return status_of(loki::launch_fused(a, kk, fs));
   }
   const int nsplit = uni ? union_nsplit(B, Hkv, S) : sparse_nsplit(rows, kk);
   const Layout L = split_layout(B, Hq, Hkv, D, S, S_max, kk, uni);
@@ -319,14 +376,12 @@ int step_impl(const void* q, const void* k_new, const void* v_new, const float* 
   a.rope = rope;
   if (path == LOKI_PATH_FUSED || path == LOKI_PATH_SLICED) {
     if (!fused_fits(D, S, kk)) return LOKI_EUNSUPPORTED;
-    const int nsl = path == LOKI_PATH_SLICED ? sliced_n(B * Hq, kk) : 1;
-    float* part = nullptr;
-    if (nsl > 1) {
-      const Layout L = layout(B, Hq, D, S_max, nsl);
-      if (!workspace || ws_bytes < L.total || !aligned16(workspace)) return LOKI_EWORKSPACE;
-      part = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.part);
+    loki::FusedSlices fs;
+    if (path == LOKI_PATH_SLICED) {
+      st = sliced_slices(B, Hq, D, S_max, kk, workspace, ws_bytes, fs);
+      if (st != LOKI_OK) return st;
     }
-    return status_of(loki::launch_fused_step(a, k_new, v_new, pos, kk, nsl, part));
+    return status_of(loki::launch_fused_step(a, k_new, v_new, pos, kk, fs));
   }
   const Layout L = split_layout(B, Hq, Hkv, D, S, S_max, kk, uni);
   if (!workspace || ws_bytes < L.total || !aligned16(workspace)) return LOKI_EWORKSPACE;

@@ -231,6 +231,9 @@ __device__ __forceinline__ unsigned long long ld_dev(const unsigned long long* p
   return __hip_atomic_load(const_cast<unsigned long long*>(p), __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ void st_dev(unsigned long long* p, unsigned long long v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 __device__ __forceinline__ void st16_dev(const Region& g, uint32_t off, const uint4& v) {
   __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{v.x, v.y, v.z, v.w}, g.r, static_cast<int>(off),
                                          0, kDevScope);

@@ -33,17 +33,31 @@ struct FusedArgs {
   int B, Hq, Hkv, d, S, S_max, kk, pos;
   float scale_log2;
   Rope rope;  // the query's embedding; STEP embeds the new key at pos
-  // slices per row: nsl workgroups each rank and select the whole row and
-  // gather 1/nsl of its kept tokens, leaving [max, sum, accumulator] partials
-  // in part [rows][nsl][D + 2] for the combine launch (nsl == 1: out directly)
-  int nsl;
+  // Rows in launch order (head-major: row r is head r / B of sequence
+  // r % B).  The first nfull are taken whole by one workgroup each; each
+  // later row by nsl workgroups ("slices", consecutive ids), which each
+  // gather 1/nsl of the row's kept tokens.  With nfull > 0 (the grid, nfull
+  // and the sliced rows all multiples of 8) each XCD takes an eighth of the
+  // whole rows, then an eighth of the sliced rows, so every CU gets the same
+  // mix.  Without coop every slice ranks
+  // and selects the whole row and leaves its [accumulator, max, sum] partial
+  // in part [rows][nsl][D + 2] for the combine launch.  With coop slice s
+  // ranks only its share of the tokens and the slices exchange the scores
+  // through xsc [rows][S]; each then selects the whole row and gathers its
+  // share, and the last slice merges the others' partials into out itself.
+  int nsl, nfull, coop;
   float* part;
+  float* xsc;
+  // coop: [0] given-up waits, then kCoopStride words per sliced row: its
+  // epoch, then the flags of the slices' scores and of their partials
+  unsigned long long* sync;
 };
 
 // Eight waves per row: the slab stream and the gather each keep twice the
 // bytes in flight of a four-wave workgroup, which is what bounds both.
 constexpr int kFusedBlock = 512;
 constexpr int kFusedKeys = 8;  // keys per thread of the SMALL selection
+static_assert(kCoopStride == 1 + 2 * kCoopMaxSlices, "epoch + two flags per slice");
 
 // SMALL: S <= kFusedKeys * kFusedBlock, so the selection keeps the scores as
 // register keys with a first-digit histogram counted during the stream.
@@ -80,6 +94,7 @@ __global__ void __launch_bounds__(kFusedBlock, 6) fused_kernel(FusedArgs a) {
   __shared__ double kin[STEP ? D : 1];         // STEP: the new key, float64 (embedded)
   __shared__ __align__(16) T kslot[STEP ? D : VEC];  // new key row [slab | rest], stored values
   __shared__ __align__(16) T vslot[STEP ? D : VEC];  // new value row
+  __shared__ float mown[D + 2];                 // coop: the merging slice's own partial
   extern __shared__ float dyn[];
   float* qs = dyn;
   float* sb = dyn + D;
@@ -87,10 +102,24 @@ __global__ void __launch_bounds__(kFusedBlock, 6) fused_kernel(FusedArgs a) {
 
   const int S = a.S, d = a.d, kk = a.kk;
   // the slices of a row have consecutive logical ids, so they run on one XCD
-  // and all but the first find the row's slab in its L2
+  // (and, without coop, all but the first find the row's slab in its L2)
   const int L = xcd_logical(blockIdx.x, gridDim.x);
-  const int slice = L % a.nsl;
-  const int h = (L / a.nsl) / a.B, b = (L / a.nsl) % a.B;
+  int rl, slice, nsl;  // row in launch order, this workgroup's slice of it, its slices
+  if (a.nfull == 0) {
+    rl = L / a.nsl;
+    slice = L % a.nsl;
+    nsl = a.nsl;
+  } else {
+    const int m = gridDim.x >> 3, fpx = a.nfull >> 3;
+    const int spx = (a.B * a.Hq - a.nfull) >> 3;
+    const int x = L / m, i = L % m;
+    const bool whole = i < fpx;
+    rl = whole ? x * fpx + i : a.nfull + x * spx + (i - fpx) / a.nsl;
+    slice = whole ? 0 : (i - fpx) % a.nsl;
+    nsl = whole ? 1 : a.nsl;
+  }
+  const bool coop = a.coop && nsl > 1;
+  const int h = rl / a.B, b = rl % a.B;
   const int G = a.Hq / a.Hkv;
   const int g = h / G;
   const int64_t row = static_cast<int64_t>(b) * a.Hq + h;
@@ -180,7 +209,11 @@ __global__ void __launch_bounds__(kFusedBlock, 6) fused_kernel(FusedArgs a) {
   }
   __syncthreads();
 
-  // 2. ranking scores of all S tokens -> LDS
+  // 2. ranking scores -> LDS: of all S tokens, or with coop of this slice's
+  //    share [j0s, j1s) (shares of cs tokens, a multiple of 4)
+  const int cs = coop ? ((S + nsl - 1) / nsl + 3) & ~3 : S;
+  const int j0s = coop ? min(S, slice * cs) : 0;
+  const int j1s = coop ? min(S, j0s + cs) : S;
   {
     const int part = threadIdx.x % LPS;
     float qf[1][VEC];
@@ -201,15 +234,79 @@ __global__ void __launch_bounds__(kFusedBlock, 6) fused_kernel(FusedArgs a) {
     }
     constexpr int US = 3;  // 16-byte slab loads in flight per lane (8 waves)
     Chunk c[US];
-    score_first<E, LPS, US, NT>(sl, d, 0, S, c);
+    score_first<E, LPS, US, NT>(sl, d, j0s, j1s, c);
     // the selection's first radix digit is counted here, under the stream
-    score_loop<E, LPS, 1, US, NT>(sl, d, 0, S, qf, [&](int, int j, float s) {
+    score_loop<E, LPS, 1, US, NT>(sl, d, j0s, j1s, qf, [&](int, int j, float s) {
       if (STEP && j == a.pos) s = snew;
       sb[j] = s;
       if (SMALL) atomicAdd(&hist0[first_digit(order_key(s))], 1u);
     }, c);
   }
   __syncthreads();
+
+  // coop: hand this slice's scores to the row's other slices and take theirs
+  // (device scope; each slice's flag carries the row's epoch + 1)
+  bool gave_up = false;
+  unsigned long long* rsync = nullptr;
+  unsigned long long ev = 0ull;
+  if (coop) {
+    rsync = a.sync + 1 + static_cast<int64_t>(rl - a.nfull) * kCoopStride;
+    ev = ld_dev(rsync) + 1ull;
+    float* xrow = a.xsc + row * S;
+    const bool vec = (S & 3) == 0 && (reinterpret_cast<uintptr_t>(a.xsc) & 15) == 0;
+    const Region xr = make_region(xrow, static_cast<uint32_t>(S) * 4u);
+    if (vec) {
+      for (int j = j0s + 4 * static_cast<int>(threadIdx.x); j < j1s; j += 4 * NT)
+        st16_dev(xr, static_cast<uint32_t>(j) * 4u, *reinterpret_cast<const uint4*>(&sb[j]));
+    } else {
+      for (int j = j0s + static_cast<int>(threadIdx.x); j < j1s; j += NT) st_dev(xrow + j, sb[j]);
+    }
+    publish(rsync + 1 + slice, ev);
+    if (wait_flags(rsync + 1, nsl, ev)) {
+      // every slice has read the epoch: the merging slice advances it
+      if (slice == nsl - 1 && threadIdx.x == 0) st_dev(rsync, ev);
+      auto take = [&](int j, float s) {
+        sb[j] = s;
+        if (SMALL) atomicAdd(&hist0[first_digit(order_key(s))], 1u);
+      };
+      // every score outside this slice's share, XU loads in flight per thread
+      constexpr int XU = 4;
+      auto other = [&](int j) { return j < S && (j < j0s || j >= j1s); };
+      if (vec) {
+        for (int base = 4 * static_cast<int>(threadIdx.x); base < S; base += 4 * NT * XU) {
+          uint4 v[XU];
+#pragma unroll
+          for (int u = 0; u < XU; ++u) {
+            const int j = base + 4 * NT * u;
+            v[u] = other(j) ? ld16_dev(xr, static_cast<uint32_t>(j) * 4u) : make_uint4(0u, 0u, 0u, 0u);
+          }
+#pragma unroll
+          for (int u = 0; u < XU; ++u) {
+            const int j = base + 4 * NT * u;
+            if (other(j)) {
+              take(j, __uint_as_float(v[u].x));
+              take(j + 1, __uint_as_float(v[u].y));
+              take(j + 2, __uint_as_float(v[u].z));
+              take(j + 3, __uint_as_float(v[u].w));
+            }
+          }
+        }
+      } else {
+        for (int base = static_cast<int>(threadIdx.x); base < S; base += NT * XU) {
+          float v[XU];
+#pragma unroll
+          for (int u = 0; u < XU; ++u) v[u] = other(base + NT * u) ? ld_dev(xrow + base + NT * u) : 0.f;
+#pragma unroll
+          for (int u = 0; u < XU; ++u)
+            if (other(base + NT * u)) take(base + NT * u, v[u]);
+        }
+      }
+    } else {
+      gave_up = true;
+      if (threadIdx.x == 0) atomicAdd(reinterpret_cast<unsigned*>(a.sync), 1u);
+    }
+    __syncthreads();
+  }
 
   // 3. top-k -> LDS (the idx output is written at the end: one in-order
   //    counter tracks loads and stores alike, so stores issued here would
@@ -225,7 +322,7 @@ __global__ void __launch_bounds__(kFusedBlock, 6) fused_kernel(FusedArgs a) {
   __syncthreads();
 
   // 4. gather + exact attention over this slice of the kept tokens
-  const int per = (kk + a.nsl - 1) / a.nsl;
+  const int per = (kk + nsl - 1) / nsl;
   const int t0 = min(kk, slice * per), t1 = min(kk, t0 + per);
   const int r = threadIdx.x % Gm::LPV;
   const int kd0 = r * VEC;
@@ -238,23 +335,80 @@ __global__ void __launch_bounds__(kFusedBlock, 6) fused_kernel(FusedArgs a) {
                                 [&](int, int, int j) { return sb[j]; }, t0, t1, sl, rs, vv, d,
                                 qf, a.scale_log2, st, STEP ? a.pos : -1, kslot, vslot);
   __syncthreads();  // the merge scratch aliases the selection scratch
+  const bool merger = coop && slice == nsl - 1;
   merge_groups<E, D, 1, NT>(st, sc.mrg, [&](int, int dim, float M, float Ls, float A) {
-    if (a.nsl == 1) {
+    if (nsl == 1) {
       a.out[row * D + dim] = A / Ls;
-    } else {
-      float* pp = a.part + (row * a.nsl + slice) * (D + 2);
-      pp[dim] = A;
+    } else if (merger) {
+      mown[dim] = A;
       if (dim == 0) {
-        pp[D] = M;
-        pp[D + 1] = Ls;
+        mown[D] = M;
+        mown[D + 1] = Ls;
+      }
+    } else {
+      // coop partials by sliced row, the combine launch's by output row
+      const int64_t prow = coop ? rl - a.nfull : row;
+      float* pp = a.part + (prow * nsl + slice) * (D + 2);
+      if (coop) {
+        st_dev(pp + dim, A);
+        if (dim == 0) {
+          st_dev(pp + D, M);
+          st_dev(pp + D + 1, Ls);
+        }
+      } else {
+        pp[dim] = A;
+        if (dim == 0) {
+          pp[D] = M;
+          pp[D + 1] = Ls;
+        }
       }
     }
   });
+  if (coop && !gave_up) {
+    if (!merger) {
+      publish(rsync + 1 + kCoopMaxSlices + slice, ev);
+    } else {
+      // the log-sum-exp merge of the slices in order, as the combine launch
+      // forms it, with this slice's own partial from LDS
+      const bool ok = wait_flags(rsync + 1 + kCoopMaxSlices, nsl - 1, ev);
+      if (!ok && threadIdx.x == 0) atomicAdd(reinterpret_cast<unsigned*>(a.sync), 1u);
+      // every partial value loaded at once: the slices' max and sum by the
+      // first threads, each output dim's accumulators by its own thread
+      const float* pr = a.part + static_cast<int64_t>(rl - a.nfull) * nsl * (D + 2);
+      __shared__ float mlx[2][kCoopMaxSlices];
+      if (threadIdx.x < 2 * kCoopMaxSlices) {
+        const int o = threadIdx.x % kCoopMaxSlices, w = threadIdx.x / kCoopMaxSlices;
+        if (o + 1 < nsl) mlx[w][o] = ld_dev(pr + o * (D + 2) + D + w);
+        else if (o + 1 == nsl) mlx[w][o] = mown[D + w];
+      }
+      float av[kCoopMaxSlices];
+      const int dim = threadIdx.x;
+#pragma unroll
+      for (int o = 0; o < kCoopMaxSlices; ++o)
+        av[o] = (dim < D && o + 1 < nsl) ? ld_dev(pr + o * (D + 2) + dim) : 0.f;
+      __syncthreads();
+      if (dim < D) {
+        float M = -INFINITY;
+        for (int o = 0; o < nsl; ++o) M = fmaxf(M, mlx[0][o]);
+        float Ls = 0.f, A = 0.f;
+#pragma unroll
+        for (int o = 0; o < kCoopMaxSlices; ++o) {
+          if (o < nsl) {
+            const float m = mlx[0][o];
+            const float w = (m == -INFINITY) ? 0.f : fast_exp2(m - M);
+            Ls = fmaf(mlx[1][o], w, Ls);
+            A = fmaf(o + 1 == nsl ? mown[dim] : av[o], w, A);
+          }
+        }
+        a.out[row * D + dim] = ok ? A / Ls : __builtin_nanf("");
+      }
+    }
+  }
   // The row's stores come last (see the selection above): this slice's part
   // of the idx output and, for STEP, the appended token's cache row (one
   // writer per KV head; this launch served that token from LDS).
   int* irow = a.idx + row * kk;
-  for (int p = t0 + threadIdx.x; p < t1; p += NT) irow[p] = ib[p];
+  for (int p = t0 + threadIdx.x; p < t1; p += NT) irow[p] = gave_up ? -1 : ib[p];
   if (STEP && h % G == 0 && slice == 0 && threadIdx.x < D) {
     const int col = threadIdx.x;
     const int64_t slot = bgo * a.S_max + a.pos;
@@ -306,7 +460,13 @@ hipError_t fused_lps(const FusedArgs& fa, size_t lds, hipStream_t stream, int gr
 template <bool STEP>
 hipError_t fused_dispatch(const FusedArgs& fa, int dtype, int D, hipStream_t stream) {
   const size_t lds = fused_lds_bytes(D, fa.S, fa.kk);
-  const int grid = fa.B * fa.Hq * fa.nsl;
+  const int rows = fa.B * fa.Hq;
+  const int grid = fa.nfull + (rows - fa.nfull) * fa.nsl;
+  if (fa.nsl < 1 || fa.nfull < 0 || fa.nfull > rows) return hipErrorInvalidValue;
+  if (fa.nfull > 0 && (!fa.coop || grid % 8 || fa.nfull % 8 || (rows - fa.nfull) % 8))
+    return hipErrorInvalidValue;
+  if (fa.coop && fa.nsl > 1 && (fa.nsl > kCoopMaxSlices || !fa.xsc || !fa.sync || !fa.part))
+    return hipErrorInvalidValue;
   if (dtype == kF32)
     return D == 64 ? fused_lps<F32, 64, STEP>(fa, lds, stream, grid)
                    : fused_lps<F32, 128, STEP>(fa, lds, stream, grid);
@@ -336,8 +496,21 @@ FusedArgs fused_args(const DecodeArgs& a, int kk) {
   fa.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(a.D)));
   fa.rope = a.rope;
   fa.nsl = 1;
+  fa.nfull = 0;
+  fa.coop = 0;
   fa.part = nullptr;
+  fa.xsc = nullptr;
+  fa.sync = nullptr;
   return fa;
+}
+
+void set_slices(FusedArgs& fa, const FusedSlices& fs) {
+  fa.nsl = fs.nsl;
+  fa.nfull = fs.nfull;
+  fa.coop = fs.coop ? 1 : 0;
+  fa.part = fs.part;
+  fa.xsc = fs.xsc;
+  fa.sync = fs.sync;
 }
 
 }  // namespace
@@ -346,25 +519,25 @@ size_t fused_lds_bytes(int D, int S, int kk) {
   return (static_cast<size_t>(D) + S + kk) * sizeof(float);
 }
 
-hipError_t launch_fused(const DecodeArgs& a, int kk, int nsl, float* part) {
+hipError_t launch_fused(const DecodeArgs& a, int kk, const FusedSlices& fs) {
   FusedArgs fa = fused_args(a, kk);
-  fa.nsl = nsl;
-  fa.part = part;
+  set_slices(fa, fs);
   hipError_t e = fused_dispatch<false>(fa, a.dtype, a.D, a.stream);
-  if (e == hipSuccess && nsl > 1) e = launch_combine(part, a.out, a.B * a.Hq, a.D, nsl, a.stream);
+  if (e == hipSuccess && fs.nsl > 1 && !fs.coop)
+    e = launch_combine(fs.part, a.out, a.B * a.Hq, a.D, fs.nsl, a.stream);
   return e;
 }
 
 hipError_t launch_fused_step(const DecodeArgs& a, const void* k_new, const void* v_new, int pos,
-                             int kk, int nsl, float* part) {
+                             int kk, const FusedSlices& fs) {
   FusedArgs fa = fused_args(a, kk);
   fa.k_new = k_new;
   fa.v_new = v_new;
   fa.pos = pos;
-  fa.nsl = nsl;
-  fa.part = part;
+  set_slices(fa, fs);
   hipError_t e = fused_dispatch<true>(fa, a.dtype, a.D, a.stream);
-  if (e == hipSuccess && nsl > 1) e = launch_combine(part, a.out, a.B * a.Hq, a.D, nsl, a.stream);
+  if (e == hipSuccess && fs.nsl > 1 && !fs.coop)
+    e = launch_combine(fs.part, a.out, a.B * a.Hq, a.D, fs.nsl, a.stream);
   return e;
 }
 

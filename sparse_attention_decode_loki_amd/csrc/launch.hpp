@@ -69,14 +69,33 @@ constexpr int kUnionMaxS = 1 << 17;
 hipError_t launch_attend_union(const DecodeArgs& a, const float* qrot, const float* scores,
                                const unsigned* bits, float* part, int nsplit);
 size_t fused_lds_bytes(int D, int S, int kk);
-// nsl > 1: each row's gather split over nsl workgroups (each ranks and
-// selects the whole row), partials in part [B*Hq][nsl][D + 2], then merged
-hipError_t launch_fused(const DecodeArgs& a, int kk, int nsl = 1, float* part = nullptr);
+// How the single-kernel path splits rows over workgroups.  Rows [0, nfull)
+// (in the kernel's head-major launch order) take one workgroup each; every
+// later row takes nsl (at most kCoopMaxSlices with coop), each gathering
+// 1/nsl of its kept tokens.  Without coop (nfull must be 0) every slice
+// ranks and selects the whole row, partials go to part [B*Hq][nsl][D + 2]
+// and a combine launch merges them.  With coop the slices of a row rank a
+// share of its tokens each and exchange the scores through xsc [B*Hq][S],
+// and the row's last slice merges the partials (part [sliced rows][nsl]
+// [D + 2]) itself; sync holds 1 + kCoopStride words per sliced row (any
+// contents are valid).  With nfull > 0 the grid, nfull and the sliced rows
+// are multiples of 8.
+constexpr int kCoopMaxSlices = 16;
+constexpr int kCoopStride = 1 + 2 * kCoopMaxSlices;
+struct FusedSlices {
+  int nsl = 1;
+  int nfull = 0;
+  bool coop = false;
+  float* part = nullptr;
+  float* xsc = nullptr;
+  unsigned long long* sync = nullptr;
+};
+hipError_t launch_fused(const DecodeArgs& a, int kk, const FusedSlices& fs = FusedSlices());
 // append (k_new, v_new [B, Hkv, D]) at pos and decode over a.S = pos + 1;
 // with a.rope.base > 0 the new key is embedded at pos (the query at
 // a.rope.pos)
 hipError_t launch_fused_step(const DecodeArgs& a, const void* k_new, const void* v_new, int pos,
-                             int kk, int nsl = 1, float* part = nullptr);
+                             int kk, const FusedSlices& fs = FusedSlices());
 // log-sum-exp merge of nsplit slice partials [rows][nsplit][D + 2] into out
 hipError_t launch_combine(const float* part, float* out, int rows, int D, int nsplit,
                           hipStream_t stream);

@@ -83,37 +83,48 @@ def test_decode_fused_rejects_when_lds_too_small(L):
     lib = L.load()
     assert lib.loki_decode_path(1, 4, 4, 128, 32, 20000, 5000, 1, 1) == -4
     assert lib.loki_decode_path(16, 40, 40, 128, 32, 3584, 896, 1, 0) == 1   # auto -> fused
-    assert lib.loki_decode_path(8, 32, 8, 128, 32, 8192, 2048, 1, 0) == 3    # GQA, k = S/4 -> union
-    assert lib.loki_decode_path(8, 32, 8, 128, 32, 8192, 2048, 0, 0) == 2    # ... float32 cache -> split
+    assert lib.loki_decode_path(8, 32, 8, 128, 32, 8192, 2048, 1, 0) == 1    # GQA that fits -> fused
+    assert lib.loki_decode_path(8, 32, 8, 128, 32, 8192, 2048, 0, 0) == 1    # ... float32 cache too
     assert lib.loki_decode_path(4, 32, 8, 128, 64, 32768, 4096, 1, 0) == 2   # GQA, k = S/8 -> split
-    assert lib.loki_decode_path(8, 32, 8, 128, 16, 8192, 2048, 1, 0) == 2    # d < D - 96 -> split
-    assert lib.loki_decode_path(1, 32, 32, 128, 32, 4096, 1024, 1, 0) == 2   # few heads -> split
+    assert lib.loki_decode_path(4, 32, 8, 128, 32, 32768, 8192, 1, 0) == 3   # GQA, k = S/4 -> union
+    assert lib.loki_decode_path(4, 32, 8, 128, 32, 32768, 8192, 0, 0) == 2   # ... float32 cache -> split
+    assert lib.loki_decode_path(4, 32, 8, 128, 16, 32768, 8192, 1, 0) == 2   # d < D - 96 -> split
+    assert lib.loki_decode_path(1, 32, 32, 128, 32, 4096, 1024, 1, 0) == 4   # few heads -> sliced
     assert lib.loki_decode_path(1, 4, 4, 128, 32, 100, 25, 1, 2) == 2
     assert lib.loki_decode_path(1, 4, 4, 128, 32, 100, 25, 1, 1) == 1
     assert lib.loki_decode_path(1, 4, 4, 128, 33, 100, 25, 1, 0) == -4
 
 
 def test_auto_takes_fused_by_rows_and_context(L):
-    # fused when rows * S + 420000 >= 190 * S (one query head per KV head)
+    # where the sliced path does not apply (k <= 64 leaves one slice per
+    # row): fused when rows * S + 420000 >= 190 * S
     lib = L.load()
-    assert lib.loki_decode_path(1, 1, 1, 128, 32, 2222, 555, 1, 0) == 1    # short rows: any count
-    assert lib.loki_decode_path(1, 1, 1, 128, 32, 2223, 555, 1, 0) == 2
-    assert lib.loki_decode_path(1, 87, 87, 128, 32, 4097, 1024, 1, 0) == 2
-    assert lib.loki_decode_path(1, 88, 88, 128, 32, 4097, 1024, 1, 0) == 1
-    assert lib.loki_decode_path(1, 138, 138, 128, 32, 8192, 2048, 1, 0) == 2
-    assert lib.loki_decode_path(1, 139, 139, 128, 32, 8192, 2048, 1, 0) == 1
-    assert lib.loki_decode_path(1, 190, 190, 128, 32, 11000, 2750, 1, 0) == 1
-    assert lib.loki_decode_path(2, 4, 2, 128, 32, 500, 125, 1, 0) != 1     # grouped heads: never
+    assert lib.loki_decode_path(1, 1, 1, 128, 32, 2222, 64, 1, 0) == 1     # short rows: any count
+    assert lib.loki_decode_path(1, 1, 1, 128, 32, 2223, 64, 1, 0) == 2
+    assert lib.loki_decode_path(1, 87, 87, 128, 32, 4097, 64, 1, 0) == 2
+    assert lib.loki_decode_path(1, 88, 88, 128, 32, 4097, 64, 1, 0) == 1
+    assert lib.loki_decode_path(1, 138, 138, 128, 32, 8192, 64, 1, 0) == 2
+    assert lib.loki_decode_path(1, 139, 139, 128, 32, 8192, 64, 1, 0) == 1
+    assert lib.loki_decode_path(2, 4, 2, 128, 32, 500, 125, 1, 0) == 1     # grouped heads too
+    assert lib.loki_decode_path(1, 4, 4, 128, 32, 12000, 3000, 1, 0) == 2  # LDS too small
+    assert lib.loki_decode_path(1, 224, 224, 128, 32, 4096, 1024, 1, 0) == 1  # slices gain nothing
 
 
-def test_auto_takes_sliced_for_48_to_128_rows_of_up_to_4096(L):
+def test_auto_takes_sliced_where_its_plan_slices(L):
     lib = L.load()
-    assert lib.loki_decode_path(1, 47, 47, 128, 32, 4096, 1024, 1, 0) == 2
-    assert lib.loki_decode_path(1, 48, 48, 128, 32, 4096, 1024, 1, 0) == 4
-    assert lib.loki_decode_path(2, 64, 64, 128, 32, 4096, 1024, 1, 0) == 4   # 128 rows
-    assert lib.loki_decode_path(1, 129, 129, 128, 32, 4096, 1024, 1, 0) == 1
-    assert lib.loki_decode_path(2, 32, 32, 128, 32, 4097, 1024, 1, 0) == 2
-    assert lib.loki_decode_path(2, 32, 8, 128, 32, 4096, 1024, 1, 0) != 4    # grouped heads
+    # fewer rows than compute units, rows of at least 2048 tokens
+    assert lib.loki_decode_path(1, 32, 32, 128, 32, 4096, 1024, 1, 0) == 4
+    assert lib.loki_decode_path(1, 1, 1, 128, 32, 2223, 555, 1, 0) == 4
+    assert lib.loki_decode_path(2, 32, 8, 128, 32, 4096, 1024, 1, 0) == 4    # grouped heads
+    assert lib.loki_decode_path(1, 190, 190, 128, 32, 11000, 2750, 1, 0) == 4
+    assert lib.loki_decode_path(1, 32, 32, 128, 32, 2048, 512, 1, 0) == 4
+    assert lib.loki_decode_path(1, 32, 32, 128, 32, 2047, 512, 1, 0) == 1    # shorter rows: fused
+    # whole rounds of the compute units plus a remainder of at most 64 rows
+    assert lib.loki_decode_path(9, 32, 32, 128, 32, 3584, 896, 1, 0) == 4    # 288 rows
+    assert lib.loki_decode_path(18, 32, 32, 128, 32, 3584, 896, 1, 0) == 4   # 576 rows
+    assert lib.loki_decode_path(16, 32, 32, 128, 32, 3584, 896, 1, 0) == 1   # 512: no remainder
+    assert lib.loki_decode_path(16, 40, 40, 128, 32, 3584, 896, 1, 0) == 1   # remainder 128
+    assert lib.loki_decode_path(1, 289, 289, 128, 32, 3584, 896, 1, 0) == 1  # rows not a multiple of 8
 
 
 def test_union_path_only_for_two_or_four_heads_per_kv_head(L):

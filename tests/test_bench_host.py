@@ -62,4 +62,17 @@ def test_design_bytes_per_path():
     assert bench.design_bytes(w, 10, 3, "split", idx) == slab + ids + scores + 4 * 3 * row
     # union: KV head 0 gathers {0,1,2,3}, KV head 1 gathers {5,6,7}
     assert bench.design_bytes(w, 10, 3, "union", idx) == slab + ids + scores + 7 * row
-    assert bench.design_bytes(w, 10, 3, "fused", idx) == slab + ids + 4 * 3 * row
+    # fused: the slab once per query head
+    assert bench.design_bytes(w, 10, 3, "fused", idx) == 2 * slab + ids + 4 * 3 * row
+    # sliced: 4 rows of k = 3 take one slice each (at least 64 kept tokens
+    # per slice), so there is nothing to exchange
+    assert bench.sliced_slices(4, 3) == 1
+    assert bench.design_bytes(w, 10, 3, "sliced", idx) == 2 * slab + ids + 4 * 3 * row
+    # with slices: each row's S scores written once and read by the other
+    # slices (S * nsl floats), and nsl - 1 partials written and read
+    assert bench.sliced_slices(32, 1024) == 8
+    assert bench.sliced_slices(640, 896) == 1 and bench.sliced_slices(576, 896) == 4
+    w2 = dataclasses.replace(w, B=1, Hq=32, Hkv=32)
+    idx2 = np.tile(np.arange(1024), (1, 32, 1))
+    base = bench.design_bytes(w2, 4096, 1024, "fused", idx2)
+    assert bench.design_bytes(w2, 4096, 1024, "sliced", idx2) == base + 32 * (4096 * 4 * 8 + 2 * 7 * 10 * 4)

@@ -37,6 +37,10 @@ SMALL = {
                               tau=8.0), 900, 960),
     # bf16 with d < 32 at D = 128: the union gather takes its VALU kernel
     "gqa4_d16": (synth.custom("gqa4_d16", 113, B=2, Hq=8, Hkv=2, d=16, S=700), 700, 720),
+    # more rows than compute units: on the sliced path 256 whole rows and a
+    # remainder of 32 (40) rows in slices that share the ranking
+    "tail_rows_288": (synth.custom("tail_rows_288", 114, B=2, Hq=144, Hkv=144, S=700), 700, 720),
+    "tail_gqa_296": (synth.custom("tail_gqa_296", 115, B=1, Hq=296, Hkv=74, S=2100), 2100, 2100),
 }
 
 
@@ -436,6 +440,8 @@ STEP_CASES = {
     "step_f32": synth.custom("step_f32", 303, B=1, Hq=2, Hkv=2, D=64, d=16, S=300, dtype="f32",
                              tau=8.0),
     "step_first": synth.custom("step_first", 304, B=2, Hq=2, Hkv=2, S=1),
+    # 288 rows: the sliced path's whole rows and sliced remainder in one step
+    "step_tail": synth.custom("step_tail", 306, B=2, Hq=144, Hkv=144, S=700),
     # the benchmark's step at full size (B=16, 40 heads, S=3584, k=896): every
     # (sequence, head) pair and every written slot against the oracle
     "step_l2_13b_full": synth.WORKLOADS["l2_13b_run"],

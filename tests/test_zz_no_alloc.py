@@ -16,10 +16,10 @@ pytestmark = pytest.mark.gpu
 import oracle  # noqa: E402
 
 CALLS = [  # (workload, paths): the first call is the larger one
-    (synth.custom("noalloc_big", 801, B=4, Hq=32, Hkv=8, S=8192, k_f=0.25), [0, 2, 3]),
-    (synth.custom("noalloc_small", 802, B=2, Hq=8, Hkv=2, S=1500, k_f=0.25), [0, 2, 3]),
+    (synth.custom("noalloc_big", 801, B=4, Hq=32, Hkv=8, S=8192, k_f=0.25), [0, 2, 3, 4]),
+    (synth.custom("noalloc_small", 802, B=2, Hq=8, Hkv=2, S=1500, k_f=0.25), [0, 2, 3, 4]),
     (synth.custom("noalloc_f32", 803, B=1, Hq=4, Hkv=2, D=64, d=16, S=700, k_f=0.2,
-                  dtype="f32"), [2, 3]),
+                  dtype="f32"), [2, 3, 4]),
 ]
 
 
