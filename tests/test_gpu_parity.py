@@ -381,7 +381,7 @@ LIMITS = {
                     [2, 3]),
     # q' + scores + kept ids just under the fused kernel's 56 KiB of LDS
     "fused_lds_max": (synth.custom("fused_lds_max", 702, B=1, Hq=2, Hkv=2, S=11000,
-                                   k_f=2999.5 / 11000), [1, 2]),
+                                   k_f=2999.5 / 11000), [1, 2, 4]),
 }
 
 
@@ -412,12 +412,13 @@ FULL = ["l2_7b", "l2_13b_run", "l3_8b_gqa", "mistral_32k"]
 
 
 @pytest.mark.parametrize("name,path", [(n, 0) for n in FULL] +
-                         [("l3_8b_gqa", 2), ("mistral_32k", 3)])
+                         [("l2_7b", 2), ("l3_8b_gqa", 2), ("l3_8b_gqa", 3), ("mistral_32k", 3)])
 def test_full_size_decode_sampled(lib, name, path):
     """Full benchmark shapes, launched exactly as the benchmark launches them
-    (AUTO path; also the gather AUTO does not take for the grouped-query
-    shapes); every (sequence, head) pair checked against the oracle, with at
-    most 1 in 100 near-tie swaps (at least one allowed)."""
+    (AUTO path: sliced, fused, fused and split), and on the split and union
+    paths where AUTO takes another; every (sequence, head) pair checked
+    against the oracle, with at most 1 in 100 near-tie swaps (at least one
+    allowed)."""
     w = synth.WORKLOADS[name]
     c = make_case(w)
     cache = device_cache(lib, c)
