@@ -508,9 +508,10 @@ PER_CONFIG = ["l2_7b", "l3_8b_gqa", "mistral_32k"]
 
 
 def measure_config(loki, torch, name, dev, steps, warmup, log) -> dict:
-    """Decode alone (AUTO path), the dense baseline and, for grouped-query
-    shapes, the other gather, for one workload at its full size, timed as
-    the headline's decode: back-to-back launches between two HIP events,
+    """Decode alone (AUTO path), the dense baseline and every other path the
+    shape supports, for one workload at its full size, timed as the
+    headline's decode: back-to-back launches between two HIP events after
+    untimed warmup launches (and 500 settle launches before the first),
     cache copies cycled so that no launch finds its bytes cached."""
     import synth
     w = synth.WORKLOADS[name]
@@ -551,14 +552,16 @@ def measure_config(loki, torch, name, dev, steps, warmup, log) -> dict:
     code = loki.decode_path(w.B, w.Hq, w.Hkv, w.D, w.d, S, k, w.dtype, loki.PATH_AUTO)
     path = PATH_NAMES[code]
 
-    def run(p):
+    def run(p, settle=0):
         plans = [loki.DecodePlan(qs[i % R], caches[i % L], Pd, k, S=S, out=out, idx=idx,
                                  workspace=ws, path=p) for i in range(n_plans)]
-        for i in range(warmup):
+        for i in range(warmup + settle):
             plans[i % n_plans]()
         return timed(torch, lambda i: plans[i % n_plans](), steps)[1]
 
-    dec_ms = run(loki.PATH_AUTO)
+    # the first path timed after the host-side set-up would otherwise run
+    # while the GPU leaves its idle clocks (about 1.5 us slower per launch)
+    dec_ms = run(loki.PATH_AUTO, settle=500)
     loki.DecodePlan(qs[0], caches[0], Pd, k, S=S, out=out, idx=idx, workspace=ws)()
     torch.cuda.synchronize()
     by = algorithmic_bytes(w, S, k)

@@ -66,7 +66,13 @@ typedef enum { LOKI_F32 = 0, LOKI_BF16 = 1 } loki_dtype;
 /* Execution path of loki_decode_ex.  AUTO picks one by shape and dtype
  * (loki_decode_path reports which).  FUSED runs one kernel per (sequence,
  * query head) that scores, selects and attends with the scores held in LDS
- * (requires (D + S + min(k, S)) * 4 bytes <= 56 KiB).  SLICED is FUSED with
+ * (requires (D + S + min(k, S)) * 4 bytes <= 56 KiB).  It needs no
+ * workspace; given one (at least loki_decode_workspace_size), with four
+ * query heads per KV head on a bf16 cache of D = 128, d <= 64 and S a
+ * multiple of 16, the four query heads' workgroups share the ranking of
+ * their KV head's slab (each scores a quarter of the tokens for all four
+ * and they exchange the scores through the workspace), with the same
+ * result.  SLICED is FUSED with
  * some rows split over several workgroups ("slices"): the slices of a row
  * each rank a share of its tokens and exchange the scores through the
  * workspace, each selects the whole row and gathers a share of the kept

@@ -295,6 +295,23 @@ int sliced_slices(int B, int Hq, int D, int S_max, int kk, void* workspace, size
   return LOKI_OK;
 }
 
+// The grouped ranking of the single-kernel decode, where it is built (four
+// query heads per KV head, bf16, D = 128, d <= 64, S a multiple of 16) and a
+// large enough workspace is given; it changes no result (the same scores
+// reach every selection), only where they are computed.
+void grouped_ranking(int B, int Hq, int Hkv, int D, int d, int S, int S_max, int dtype,
+                     void* workspace, size_t ws_bytes, loki::FusedSlices& fs) {
+  if (fs.nsl != 1 || Hq != loki::kGrpHeads * Hkv || dtype != LOKI_BF16 || D != 128 ||
+      d > loki::kGrpMaxD || S % (4 * loki::kGrpHeads) != 0)
+    return;
+  const Layout L = layout(B, Hq, D, S_max, 1);
+  if (!workspace || ws_bytes < L.total || !aligned16(workspace)) return;
+  char* ws = static_cast<char*>(workspace);
+  fs.grp = loki::kGrpHeads;
+  fs.xsc = reinterpret_cast<float*>(ws + L.scores);
+  fs.sync = reinterpret_cast<unsigned long long*>(ws + L.coop);
+}
+
 int decode_impl(const void* q, const void* k_slab, const void* k_rest, const void* v,
                 const float* P, int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t d,
                 int32_t S, int32_t S_max, int32_t k, int32_t dtype, float* out, int32_t* idx,
@@ -323,6 +340,7 @@ int decode_impl(const void* q, const void* k_slab, const void* k_rest, const voi
       st = sliced_slices(B, Hq, D, S_max, kk, workspace, ws_bytes, fs);
       if (st != LOKI_OK) return st;
     }
+    grouped_ranking(B, Hq, Hkv, D, d, S, S_max, dtype, workspace, ws_bytes, fs);
     return status_of(loki::launch_fused(a, kk, fs));
   }
   const int nsplit = uni ? union_nsplit(B, Hkv, S) : sparse_nsplit(rows, kk);

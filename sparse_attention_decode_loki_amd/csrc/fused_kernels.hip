@@ -13,6 +13,8 @@
 // from LDS, so it does not matter when the writing workgroup's stores land.
 // Only the workgroup of the first query head of each KV head writes the slot,
 // after its gather.
+#include <type_traits>
+
 #include "attend.hpp"
 #include "launch.hpp"
 #include "score.hpp"
@@ -46,6 +48,13 @@ struct FusedArgs {
   // through xsc [rows][S]; each then selects the whole row and gathers its
   // share, and the last slice merges the others' partials into out itself.
   int nsl, nfull, coop;
+  // grouped ranking (grp = Hq / Hkv > 1, one workgroup per row, rows in
+  // (KV head, sequence, query head) order): the grp workgroups of one KV
+  // head each score a 1/grp share of the tokens for all grp heads (one slab
+  // read, grp products) and exchange the other heads' scores through xsc
+  // and sync as the slices of a row do; each then selects and gathers its
+  // own row.  Same ranking scores as the single-head pass, so the same result.
+  int grp;
   float* part;
   float* xsc;
   // coop: [0] given-up waits, then kCoopStride words per sliced row: its
@@ -63,10 +72,15 @@ static_assert(kCoopStride == 1 + 2 * kCoopMaxSlices, "epoch + two flags per slic
 // register keys with a first-digit histogram counted during the stream.
 // At least six waves per SIMD (at most 80 VGPRs): three workgroups of eight
 // waves share a CU when the rows outnumber the CUs.
-template <class E, int D, int LPS, bool SMALL, bool STEP>
-__global__ void __launch_bounds__(kFusedBlock, 6) fused_kernel(FusedArgs a) {
+// GRP > 1: the grouped ranking for GRP query heads per KV head (four waves
+// per SIMD: its ranking holds GRP products per token).
+template <class E, int D, int LPS, bool SMALL, bool STEP, int GRP>
+__global__ void __launch_bounds__(kFusedBlock, GRP > 1 ? 4 : 6) fused_kernel(FusedArgs a) {
   using T = typename E::T;
   constexpr int NT = kFusedBlock;
+  constexpr bool GROUP = GRP > 1;
+  static_assert(!(GROUP && STEP), "the grouped ranking is built for decode");
+  constexpr int GD = GROUP ? kGrpMaxD : 1;
   using Gm = Geo<E, D, NT>;
   constexpr int VEC = E::VEC;
   // the rotation is formed by kBlock threads with the partition of
@@ -77,6 +91,7 @@ __global__ void __launch_bounds__(kFusedBlock, 6) fused_kernel(FusedArgs a) {
   struct Rot {
     float q[NRB][D];
     double k[STEP ? NRB : 1][D];
+    float g[GROUP ? NRB : 1][GRP][GD];  // GROUP: the group's heads, ranking columns
   };
   constexpr int CAP = 64;  // crossing bins up to this size are ranked directly
   struct Sel {
@@ -90,7 +105,8 @@ __global__ void __launch_bounds__(kFusedBlock, 6) fused_kernel(FusedArgs a) {
   };
   __shared__ Scratch sc;
   __shared__ unsigned hist0[SMALL ? kSelBins : 1];  // first-digit histogram of the scores
-  __shared__ float rin[D];                     // q as float (embedded)
+  __shared__ float rin[GRP][D];                // q as float (embedded); GROUP: the group's heads
+  __shared__ float qg[GRP][GD];                // GROUP: ranking q' of the group's heads
   __shared__ double kin[STEP ? D : 1];         // STEP: the new key, float64 (embedded)
   __shared__ __align__(16) T kslot[STEP ? D : VEC];  // new key row [slab | rest], stored values
   __shared__ __align__(16) T vslot[STEP ? D : VEC];  // new value row
@@ -119,8 +135,13 @@ __global__ void __launch_bounds__(kFusedBlock, 6) fused_kernel(FusedArgs a) {
     nsl = whole ? 1 : a.nsl;
   }
   const bool coop = a.coop && nsl > 1;
-  const int h = rl / a.B, b = rl % a.B;
   const int G = a.Hq / a.Hkv;
+  // GROUP: row rl is query head rl % GRP of unit rl / GRP = (KV head g,
+  // sequence b), units KV-head-major (as rows are otherwise head-major), so
+  // a unit's heads share its slab and an XCD's units share their basis in L2
+  const int jg = GROUP ? rl % GRP : 0;
+  const int h = GROUP ? (rl / GRP) / a.B * GRP + jg : rl / a.B;
+  const int b = GROUP ? (rl / GRP) % a.B : rl % a.B;
   const int g = h / G;
   const int64_t row = static_cast<int64_t>(b) * a.Hq + h;
   const int64_t bgo = static_cast<int64_t>(b) * a.Hkv + g;
@@ -137,12 +158,13 @@ __global__ void __launch_bounds__(kFusedBlock, 6) fused_kernel(FusedArgs a) {
   //    new value row is loaded together with the query.
   T vn{};
   if (STEP && threadIdx.x < D) vn = static_cast<const T*>(a.v_new)[bgo * D + threadIdx.x];
+  // the queries: this row's, or (GROUP) those of the KV head's GRP heads
+  const int64_t qrow0 = GROUP ? row - jg : row;
   if (a.rope.base == 0.0) {
-    if (threadIdx.x < D) {
-      rin[threadIdx.x] = ld_elem<E>(static_cast<const T*>(a.q), row * D + threadIdx.x);
-      if (STEP)
-        kin[threadIdx.x] = ld_elem<E>(static_cast<const T*>(a.k_new), bgo * D + threadIdx.x);
-    }
+    for (int e = threadIdx.x; e < GRP * D; e += NT)
+      rin[e / D][e % D] = ld_elem<E>(static_cast<const T*>(a.q), qrow0 * D + e);
+    if (STEP && threadIdx.x < D)
+      kin[threadIdx.x] = ld_elem<E>(static_cast<const T*>(a.k_new), bgo * D + threadIdx.x);
   } else {
     // RoPE: each pair's cosine and sine once, then the elements (a step
     // places the query and the new key both at pos: a.rope.pos == a.pos)
@@ -150,13 +172,18 @@ __global__ void __launch_bounds__(kFusedBlock, 6) fused_kernel(FusedArgs a) {
     if (threadIdx.x < D / 2)
       rope_cs(threadIdx.x, D, a.rope.base, a.rope.pos, rcs[0][threadIdx.x], rcs[1][threadIdx.x]);
     __syncthreads();
+    for (int e = threadIdx.x; e < GRP * D; e += NT) {
+      const int m = e % D, h = D / 2;
+      const bool first = m < h;
+      const int i = first ? m : m - h, mp = first ? m + h : m - h;
+      const T* qv = static_cast<const T*>(a.q) + (qrow0 + e / D) * D;
+      rin[e / D][m] = static_cast<float>(rope_apply(ld_elem<E>(qv, m), ld_elem<E>(qv, mp),
+                                                    rcs[0][i], rcs[1][i], first));
+    }
     if (threadIdx.x < D) {
       const int m = threadIdx.x, h = D / 2;
       const bool first = m < h;
       const int i = first ? m : m - h, mp = first ? m + h : m - h;
-      const T* qv = static_cast<const T*>(a.q) + row * D;
-      rin[m] = static_cast<float>(rope_apply(ld_elem<E>(qv, m), ld_elem<E>(qv, mp), rcs[0][i],
-                                             rcs[1][i], first));
       if (STEP) {
         const T* kv = static_cast<const T*>(a.k_new) + bgo * D;
         kin[m] = rope_apply(ld_elem<E>(kv, m), ld_elem<E>(kv, mp), rcs[0][i], rcs[1][i], first);
@@ -169,16 +196,39 @@ __global__ void __launch_bounds__(kFusedBlock, 6) fused_kernel(FusedArgs a) {
     const int cq = threadIdx.x % CQ, rb = threadIdx.x / CQ;
     const float* Pg = a.P + static_cast<int64_t>(g) * D * D;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    float4 accg[GRP];  // GROUP: every head of the group, ranking columns only
+#pragma unroll
+    for (int hh = 0; hh < GRP; ++hh) accg[hh] = make_float4(0.f, 0.f, 0.f, 0.f);
+    const bool gcol = GROUP && 4 * cq < d;
     double kacc[4] = {0.0, 0.0, 0.0, 0.0};
+    // GROUP: the block's basis rows are all loaded before any product, so
+    // that the group's extra products do not hold back the loads
+    float4 pre[GROUP ? RB : 1];
+    if constexpr (GROUP) {
+#pragma unroll
+      for (int rr = 0; rr < RB; ++rr)
+        pre[rr] = *reinterpret_cast<const float4*>(Pg + (rb * RB + rr) * D + 4 * cq);
+    }
 #pragma unroll
     for (int rr = 0; rr < RB; ++rr) {
       const int m = rb * RB + rr;
-      const float4 p = *reinterpret_cast<const float4*>(Pg + m * D + 4 * cq);
-      const float x = rin[m];
+      const float4 p = GROUP ? pre[GROUP ? rr : 0]
+                             : *reinterpret_cast<const float4*>(Pg + m * D + 4 * cq);
+      const float x = rin[jg][m];
       acc.x = fmaf(x, p.x, acc.x);
       acc.y = fmaf(x, p.y, acc.y);
       acc.z = fmaf(x, p.z, acc.z);
       acc.w = fmaf(x, p.w, acc.w);
+      if (gcol) {
+#pragma unroll
+        for (int hh = 0; hh < GRP; ++hh) {
+          const float xg = rin[hh][m];
+          accg[hh].x = fmaf(xg, p.x, accg[hh].x);
+          accg[hh].y = fmaf(xg, p.y, accg[hh].y);
+          accg[hh].z = fmaf(xg, p.z, accg[hh].z);
+          accg[hh].w = fmaf(xg, p.w, accg[hh].w);
+        }
+      }
       if (STEP) {
         const double xk = kin[STEP ? m : 0];
         kacc[0] = fma(xk, static_cast<double>(p.x), kacc[0]);
@@ -188,12 +238,25 @@ __global__ void __launch_bounds__(kFusedBlock, 6) fused_kernel(FusedArgs a) {
       }
     }
     *reinterpret_cast<float4*>(&sc.rot.q[rb][4 * cq]) = acc;
+    if (gcol) {
+#pragma unroll
+      for (int hh = 0; hh < GRP; ++hh)
+        *reinterpret_cast<float4*>(&sc.rot.g[GROUP ? rb : 0][hh][GROUP ? 4 * cq : 0]) = accg[hh];
+    }
     if (STEP) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) sc.rot.k[STEP ? rb : 0][4 * cq + i] = kacc[i];
     }
   }
   __syncthreads();
+  if (GROUP && threadIdx.x >= NT - GRP * d) {
+    // the group's ranking q', summed as the row's own columns are
+    const int e = threadIdx.x - (NT - GRP * d), hh = e / d, col = e % d;
+    float x = 0.f;
+#pragma unroll
+    for (int pp = 0; pp < NRB; ++pp) x += sc.rot.g[GROUP ? pp : 0][hh][GROUP ? col : 0];
+    qg[hh][GROUP ? col : 0] = x;
+  }
   if (threadIdx.x < D) {
     const int col = threadIdx.x;
     float s = 0.f;
@@ -210,43 +273,109 @@ __global__ void __launch_bounds__(kFusedBlock, 6) fused_kernel(FusedArgs a) {
   __syncthreads();
 
   // 2. ranking scores -> LDS: of all S tokens, or with coop of this slice's
-  //    share [j0s, j1s) (shares of cs tokens, a multiple of 4)
-  const int cs = coop ? ((S + nsl - 1) / nsl + 3) & ~3 : S;
-  const int j0s = coop ? min(S, slice * cs) : 0;
-  const int j1s = coop ? min(S, j0s + cs) : S;
+  //    share [j0s, j1s) (shares of cs tokens, a multiple of 4), or (GROUP)
+  //    of share jg (S / GRP tokens) for each head of the group: this row's
+  //    into place, head hh's staged in share hh's slots of sb (free until
+  //    the exchange below refills them)
+  const int cs = coop ? ((S + nsl - 1) / nsl + 3) & ~3 : (GROUP ? S / GRP : S);
+  const int j0s = coop ? min(S, slice * cs) : (GROUP ? jg * cs : 0);
+  const int j1s = coop ? min(S, j0s + cs) : (GROUP ? j0s + cs : S);
   {
+    constexpr int NH = GRP;
     const int part = threadIdx.x % LPS;
-    float qf[1][VEC];
+    float qf[NH][VEC];
 #pragma unroll
-    for (int v = 0; v < VEC; ++v) qf[0][v] = (part * VEC < d) ? qs[part * VEC + v] : 0.f;
+    for (int hh = 0; hh < NH; ++hh)
+#pragma unroll
+      for (int v = 0; v < VEC; ++v)
+        qf[hh][v] = (part * VEC < d) ? (GROUP ? qg[hh][GROUP ? part * VEC + v : 0]
+                                              : qs[part * VEC + v])
+                                     : 0.f;
     // STEP: the new token's score from its LDS row, with the streaming
     // pass's arithmetic, formed by every wave (each lane group ends with the
     // same sum), so the stream's value for that slot, read from the cache row
     // the launch has not written yet, is replaced without a barrier
-    float snew = 0.f;
+    float snew[NH];
+#pragma unroll
+    for (int hh = 0; hh < NH; ++hh) snew[hh] = 0.f;
     if (STEP) {
       float x[VEC];
       Chunk ch = (part * VEC < d) ? ld16(kslot + part * VEC) : zero_chunk();
       unpack<E>(ch, x);
 #pragma unroll
-      for (int v = 0; v < VEC; ++v) snew = fmaf(qf[0][v], x[v], snew);
-      snew = group_sum<LPS>(snew);
+      for (int hh = 0; hh < NH; ++hh) {
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) snew[hh] = fmaf(qf[hh][v], x[v], snew[hh]);
+        snew[hh] = group_sum<LPS>(snew[hh]);
+      }
     }
     constexpr int US = 3;  // 16-byte slab loads in flight per lane (8 waves)
     Chunk c[US];
     score_first<E, LPS, US, NT>(sl, d, j0s, j1s, c);
     // the selection's first radix digit is counted here, under the stream
-    score_loop<E, LPS, 1, US, NT>(sl, d, j0s, j1s, qf, [&](int, int j, float s) {
-      if (STEP && j == a.pos) s = snew;
-      sb[j] = s;
-      if (SMALL) atomicAdd(&hist0[first_digit(order_key(s))], 1u);
+    score_loop<E, LPS, NH, US, NT>(sl, d, j0s, j1s, qf, [&](int hh, int j, float s) {
+      if (STEP && j == a.pos) s = snew[hh];
+      if (hh == jg) {
+        sb[j] = s;
+        if (SMALL) atomicAdd(&hist0[first_digit(order_key(s))], 1u);
+      } else {
+        sb[hh * cs + (j - j0s)] = s;
+      }
     }, c);
   }
   __syncthreads();
 
+  // GROUP: hand the other heads' scores of share jg to their workgroups and
+  // take this row's other shares (device scope; flags carry the KV head's
+  // epoch + 1, advanced by its last head's workgroup once all have published)
+  bool gave_up = false;
+  if constexpr (GROUP) {
+    unsigned long long* gsync = a.sync + 1 + static_cast<int64_t>(rl / GRP) * kCoopStride;
+    const unsigned long long gev = ld_dev(gsync) + 1ull;
+    const Region xg = make_region(a.xsc + qrow0 * S, static_cast<uint32_t>(GRP * S) * 4u);
+#pragma unroll
+    for (int hh = 0; hh < GRP; ++hh) {
+      if (hh == jg) continue;
+      for (int i = 4 * static_cast<int>(threadIdx.x); i < cs; i += 4 * NT)
+        st16_dev(xg, static_cast<uint32_t>(hh * S + j0s + i) * 4u,
+                 *reinterpret_cast<const uint4*>(&sb[hh * cs + i]));
+    }
+    publish(gsync + 1 + jg, gev);
+    if (wait_flags(gsync + 1, GRP, gev)) {
+      if (jg == GRP - 1 && threadIdx.x == 0) st_dev(gsync, gev);
+      constexpr int XU = 4;
+      for (int base = 4 * static_cast<int>(threadIdx.x); base < S; base += 4 * NT * XU) {
+        uint4 v[XU];
+#pragma unroll
+        for (int u = 0; u < XU; ++u) {
+          const int j = base + 4 * NT * u;
+          v[u] = (j < S && (j < j0s || j >= j1s))
+                     ? ld16_dev(xg, static_cast<uint32_t>(jg * S + j) * 4u)
+                     : make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (int u = 0; u < XU; ++u) {
+          const int j = base + 4 * NT * u;
+          if (j < S && (j < j0s || j >= j1s)) {
+            const float f[4] = {__uint_as_float(v[u].x), __uint_as_float(v[u].y),
+                                __uint_as_float(v[u].z), __uint_as_float(v[u].w)};
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              sb[j + t] = f[t];
+              if (SMALL) atomicAdd(&hist0[first_digit(order_key(f[t]))], 1u);
+            }
+          }
+        }
+      }
+    } else {
+      gave_up = true;
+      if (threadIdx.x == 0) atomicAdd(reinterpret_cast<unsigned*>(a.sync), 1u);
+    }
+    __syncthreads();
+  }
+
   // coop: hand this slice's scores to the row's other slices and take theirs
   // (device scope; each slice's flag carries the row's epoch + 1)
-  bool gave_up = false;
   unsigned long long* rsync = nullptr;
   unsigned long long ev = 0ull;
   if (coop) {
@@ -424,14 +553,28 @@ __global__ void __launch_bounds__(kFusedBlock, 6) fused_kernel(FusedArgs a) {
 
 namespace {
 
+template <class E, int D, int LPS, bool STEP, int GRP>
+void fused_g(const FusedArgs& fa, size_t lds, hipStream_t stream, int grid) {
+  if (fa.S <= kFusedKeys * kFusedBlock)
+    hipLaunchKernelGGL((fused_kernel<E, D, LPS, true, STEP, GRP>), dim3(grid), dim3(kFusedBlock),
+                       lds, stream, fa);
+  else
+    hipLaunchKernelGGL((fused_kernel<E, D, LPS, false, STEP, GRP>), dim3(grid),
+                       dim3(kFusedBlock), lds, stream, fa);
+}
+
+// the grouped ranking is built for decode with four query heads per KV head
+// on bf16 caches of D = 128 (the host takes it only there)
 template <class E, int D, int LPS, bool STEP>
 hipError_t fused_t(const FusedArgs& fa, size_t lds, hipStream_t stream, int grid) {
-  if (fa.S <= kFusedKeys * kFusedBlock)
-    hipLaunchKernelGGL((fused_kernel<E, D, LPS, true, STEP>), dim3(grid), dim3(kFusedBlock), lds,
-                       stream, fa);
-  else
-    hipLaunchKernelGGL((fused_kernel<E, D, LPS, false, STEP>), dim3(grid), dim3(kFusedBlock), lds,
-                       stream, fa);
+  if constexpr (!STEP && std::is_same_v<E, BF16> && D == 128 && LPS * E::VEC <= kGrpMaxD) {
+    if (fa.grp == kGrpHeads) {
+      fused_g<E, D, LPS, STEP, kGrpHeads>(fa, lds, stream, grid);
+      return hipGetLastError();
+    }
+  }
+  if (fa.grp > 1) return hipErrorInvalidValue;
+  fused_g<E, D, LPS, STEP, 1>(fa, lds, stream, grid);
   return hipGetLastError();
 }
 
@@ -467,6 +610,9 @@ hipError_t fused_dispatch(const FusedArgs& fa, int dtype, int D, hipStream_t str
     return hipErrorInvalidValue;
   if (fa.coop && fa.nsl > 1 && (fa.nsl > kCoopMaxSlices || !fa.xsc || !fa.sync || !fa.part))
     return hipErrorInvalidValue;
+  if (fa.grp > 1 && (fa.nsl != 1 || fa.grp != fa.Hq / fa.Hkv || fa.S % (4 * fa.grp) ||
+                     fa.d > kGrpMaxD || !fa.xsc || !fa.sync))
+    return hipErrorInvalidValue;
   if (dtype == kF32)
     return D == 64 ? fused_lps<F32, 64, STEP>(fa, lds, stream, grid)
                    : fused_lps<F32, 128, STEP>(fa, lds, stream, grid);
@@ -498,6 +644,7 @@ FusedArgs fused_args(const DecodeArgs& a, int kk) {
   fa.nsl = 1;
   fa.nfull = 0;
   fa.coop = 0;
+  fa.grp = 1;
   fa.part = nullptr;
   fa.xsc = nullptr;
   fa.sync = nullptr;
@@ -508,6 +655,7 @@ void set_slices(FusedArgs& fa, const FusedSlices& fs) {
   fa.nsl = fs.nsl;
   fa.nfull = fs.nfull;
   fa.coop = fs.coop ? 1 : 0;
+  fa.grp = fs.grp;
   fa.part = fs.part;
   fa.xsc = fs.xsc;
   fa.sync = fs.sync;

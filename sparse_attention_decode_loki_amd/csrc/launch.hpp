@@ -82,10 +82,18 @@ size_t fused_lds_bytes(int D, int S, int kk);
 // are multiples of 8.
 constexpr int kCoopMaxSlices = 16;
 constexpr int kCoopStride = 1 + 2 * kCoopMaxSlices;
+// Grouped ranking on the single-kernel decode (one workgroup per row): the
+// kGrpHeads query heads of a KV head share the ranking of its slab, each
+// scoring a quarter of the tokens for all four and exchanging the scores
+// through xsc and sync (as coop slices do).  For bf16 caches with D = 128,
+// d <= kGrpMaxD and S a multiple of 4 * kGrpHeads.
+constexpr int kGrpHeads = 4;
+constexpr int kGrpMaxD = 64;
 struct FusedSlices {
   int nsl = 1;
   int nfull = 0;
   bool coop = false;
+  int grp = 1;  // kGrpHeads: grouped ranking (nsl == 1, nfull == 0)
   float* part = nullptr;
   float* xsc = nullptr;
   unsigned long long* sync = nullptr;

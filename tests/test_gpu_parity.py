@@ -578,7 +578,7 @@ def test_stream_read_probe_reads_every_element(lib):
         assert got == float((torch.arange(n, dtype=torch.float64) % 7).sum())
 
 
-@pytest.mark.parametrize("path", [2, 3, 4], ids=["split", "union", "sliced"])
+@pytest.mark.parametrize("path", [1, 2, 3, 4], ids=["fused", "split", "union", "sliced"])
 def test_split_paths_ignore_stale_workspace(lib, path):
     """The split and union paths read nothing from the workspace that the same
     call did not write: a workspace full of NaN bit patterns and a zeroed one
@@ -594,6 +594,38 @@ def test_split_paths_ignore_stale_workspace(lib, path):
         res.append((out.cpu().numpy(), idx.cpu().numpy()))
     assert np.array_equal(res[0][1], res[1][1])
     assert np.array_equal(res[0][0].view(np.uint32), res[1][0].view(np.uint32))
+
+
+GROUPED = {
+    # four query heads per KV head, bf16, D = 128, S a multiple of 16: given a
+    # workspace, the single-kernel decode shares each KV head's ranking among
+    # its four query heads' workgroups
+    "grp_d32": (synth.custom("grp_d32", 120, B=2, Hq=8, Hkv=2, S=1024), [1, 16, 256, 1024]),
+    "grp_d64": (synth.custom("grp_d64", 121, B=1, Hq=16, Hkv=4, d=64, S=4096, k_f=0.125), [512]),
+    "grp_d16": (synth.custom("grp_d16", 122, B=3, Hq=4, Hkv=1, d=16, S=512, sinks=4), [128]),
+    "grp_d8": (synth.custom("grp_d8", 123, B=2, Hq=8, Hkv=2, d=8, S=4992), [1248]),
+}
+
+
+@pytest.mark.parametrize("name", sorted(GROUPED))
+def test_grouped_ranking_matches_oracle_and_the_single_head_pass(lib, name):
+    """The fused decode with a workspace (grouped ranking) against the oracle,
+    and bit-identical to the fused decode without one (each workgroup ranks
+    its own row), at several budgets."""
+    import torch
+    w, ks = GROUPED[name]
+    c = make_case(w)
+    cache = device_cache(lib, c)
+    ws = lib.alloc_workspace(w.B, w.Hq, c.S_max, w.D, max(ks), torch.device("cuda"))
+    for k in ks:
+        print(f"grouped: {name} k={k}", flush=True)
+        out, idx = lib.decode(_q(c), cache, _P(c), k, workspace=ws, path=1)
+        one_out, one_idx = lib.decode(_q(c), cache, _P(c), k, path=1)
+        out, idx = out.cpu().numpy(), idx.cpu().numpy()
+        assert np.array_equal(idx, one_idx.cpu().numpy())
+        assert np.array_equal(out.view(np.uint32), one_out.cpu().numpy().view(np.uint32))
+        ref_out, ref_idx, ref_s = oracle.decode(c.q, c.slab, c.rest, c.v, c.P, k, w.dtype, S=c.S)
+        check_decode(w.dtype, k, out, idx, ref_out, ref_idx, ref_s, all_pairs(w), src_of(c))
 
 
 def test_per_layer_slab_width(lib):

@@ -8,7 +8,8 @@ GPU needed).
 - Every instantiation of the single-kernel decode fits six waves per SIMD
   (80 VGPRs or fewer), so three eight-wave workgroups share a compute unit;
   the 13B-shape decode runs 2.5 rows per CU and loses its third workgroup
-  otherwise."""
+  otherwise.  The grouped-ranking instantiations (four query heads' products
+  per token) fit four waves per SIMD (128 VGPRs), two workgroups per CU."""
 
 import os
 import re
@@ -67,10 +68,24 @@ def test_no_kernel_spills(resources):
     assert not bad, bad
 
 
+def _group_size(name):
+    """The last template argument of a fused_kernel instantiation (its
+    grouped-ranking head count; mangled as ...Lb?ELi<n>EE)."""
+    m = re.search(r"Lb[01]ELi(\d+)EE", name)
+    assert m, name
+    return int(m.group(1))
+
+
 def test_fused_kernel_fits_three_workgroups_per_cu(resources):
     fused = {k: v for k, v in resources.items() if "fused_kernel" in k and "VGPRs" in v}
     # {f32, bf16} x D {64, 128} x slab lane counts x {SMALL or not} x {decode, step}
-    assert len(fused) >= 40
-    bad = {k: v for k, v in fused.items()
+    single = {k: v for k, v in fused.items() if _group_size(k) == 1}
+    assert len(single) >= 40
+    bad = {k: v for k, v in single.items()
            if v["VGPRs"] > 80 or v.get("Occupancy [waves/SIMD]", 0) < 6}
+    assert not bad, bad
+    grouped = {k: v for k, v in fused.items() if _group_size(k) > 1}
+    assert len(grouped) >= 8  # bf16, D = 128: slab lane counts x {SMALL or not}
+    bad = {k: v for k, v in grouped.items()
+           if v["VGPRs"] > 128 or v.get("Occupancy [waves/SIMD]", 0) < 4}
     assert not bad, bad
