@@ -152,6 +152,13 @@ __global__ void __launch_bounds__(kFusedBlock, GRP > 1 ? 4 : 6) fused_kernel(Fus
   if (SMALL)
     for (int i = threadIdx.x; i < kSelBins; i += NT) hist0[i] = 0u;
 
+  // GROUP: the ranking stream is ALU-bound (four products per token), so its
+  // first batch of slab loads, four per lane, is issued here, ahead of the
+  // rotation, for the share this workgroup ranks
+  constexpr int US = GROUP ? 4 : 3;  // 16-byte slab loads in flight per lane
+  Chunk cg[GROUP ? US : 1];
+  if constexpr (GROUP) score_first<E, LPS, US, NT>(sl, d, jg * (S / GRP), (jg + 1) * (S / GRP), cg);
+
   // 1. q' = q . P[g] (and, for STEP, k' = k_new . P[g] in float64): thread
   //    (cq, rb) adds rows [rb*RB, rb*RB + RB) for columns 4*cq .. 4*cq + 3,
   //    read as 16-byte chunks; the NRB partials are added through LDS.  The
@@ -309,9 +316,13 @@ __global__ void __launch_bounds__(kFusedBlock, GRP > 1 ? 4 : 6) fused_kernel(Fus
         snew[hh] = group_sum<LPS>(snew[hh]);
       }
     }
-    constexpr int US = 3;  // 16-byte slab loads in flight per lane (8 waves)
     Chunk c[US];
-    score_first<E, LPS, US, NT>(sl, d, j0s, j1s, c);
+    if constexpr (GROUP) {
+#pragma unroll
+      for (int u = 0; u < US; ++u) c[u] = cg[GROUP ? u : 0];
+    } else {
+      score_first<E, LPS, US, NT>(sl, d, j0s, j1s, c);
+    }
     // the selection's first radix digit is counted here, under the stream
     score_loop<E, LPS, NH, US, NT>(sl, d, j0s, j1s, qf, [&](int hh, int j, float s) {
       if (STEP && j == a.pos) s = snew[hh];
