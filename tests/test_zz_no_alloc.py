@@ -1,8 +1,8 @@
 """The allocation-free decode (loki_decode_noalloc) against loki_decode_ex
 with a caller workspace: the same selections and bit-identical outputs,
 over two calls in a row whose second is smaller (it finds the first call's
-contents in the library's scratch), on every path that uses the scratch,
-and against the oracle.  A shape whose workspace exceeds the scratch is
+contents in the library's scratch), on every path that uses the scratch
+(the fused path for its grouped ranking), and against the oracle.  A shape whose workspace exceeds the scratch is
 refused before anything is launched."""
 
 import numpy as np
@@ -16,7 +16,7 @@ pytestmark = pytest.mark.gpu
 import oracle  # noqa: E402
 
 CALLS = [  # (workload, paths): the first call is the larger one
-    (synth.custom("noalloc_big", 801, B=4, Hq=32, Hkv=8, S=8192, k_f=0.25), [0, 2, 3, 4]),
+    (synth.custom("noalloc_big", 801, B=4, Hq=32, Hkv=8, S=8192, k_f=0.25), [0, 1, 2, 3, 4]),
     (synth.custom("noalloc_small", 802, B=2, Hq=8, Hkv=2, S=1500, k_f=0.25), [0, 2, 3, 4]),
     (synth.custom("noalloc_f32", 803, B=1, Hq=4, Hkv=2, D=64, d=16, S=700, k_f=0.2,
                   dtype="f32"), [2, 3, 4]),
