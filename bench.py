@@ -125,12 +125,13 @@ def main():
                     help="CPU oracle: seconds of work per worker process")
     ap.add_argument("--cpu-workers", type=int, default=0,
                     help="CPU oracle: worker processes (0: every host core, at most 16)")
+    ap.add_argument("--cpu-sequences", type=int, default=4, help=argparse.SUPPRESS)
     ap.add_argument("--cpu-baseline-child", action="store_true", help=argparse.SUPPRESS)
     args = ap.parse_args()
     if args.cpu_baseline_child:
         # the CPU oracle's timing, in a process that never touches the GPU
         print(json.dumps(cpu_baseline_child(args.config, args.rope_base, args.cpu_seconds,
-                                            args.cpu_workers)), flush=True)
+                                            args.cpu_workers, args.cpu_sequences)), flush=True)
         return
     if args.gpus != 1:
         print(f"bench.py: this implementation runs on a single GPU; --gpus {args.gpus} is not "
@@ -413,9 +414,15 @@ def main():
                                                         args.warmup, log)
             torch.cuda.empty_cache()
 
-    # ---- CPU oracle on a bounded sample (rank 0, one GPU), in a child process
+    # ---- CPU oracle on a bounded sample (rank 0, one GPU), in a child process;
+    # for the other workloads a shorter sample (every head of one sequence)
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(args, log)
+        for name, res in result.get("per_config", {}).items():
+            rec = cpu_baseline(args, log, config=name, seconds=min(args.cpu_seconds, 3.0),
+                               sequences=1)
+            res["cpu_oracle"] = {k_: rec[k_] for k_ in ("value", "unit", "cores", "sample")}
+            res["gpu_over_cpu_oracle"] = res["head_queries_per_s"] / rec["value"]
 
     print(json.dumps(result), flush=True)
 
@@ -599,20 +606,21 @@ def measure_config(loki, torch, name, dev, steps, warmup, log) -> dict:
     return res
 
 
-def cpu_baseline(args, log):
+def cpu_baseline(args, log, config=None, seconds=None, sequences=4):
     """Runs the CPU oracle's timing in a child process (which never touches
     the GPU, so it may fork its workers) and returns its record."""
     import subprocess
+    config = config or args.config
     cmd = [sys.executable, os.path.abspath(__file__), "--cpu-baseline-child", "--config",
-           args.config, "--cpu-seconds", str(args.cpu_seconds), "--cpu-workers",
-           str(args.cpu_workers)]
-    if args.rope_base is not None:
+           config, "--cpu-seconds", str(args.cpu_seconds if seconds is None else seconds),
+           "--cpu-workers", str(args.cpu_workers), "--cpu-sequences", str(sequences)]
+    if args.rope_base is not None and config == args.config:
         cmd += ["--rope-base", str(args.rope_base)]
     r = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
     if r.returncode != 0:
         raise RuntimeError("CPU oracle timing failed:\n" + r.stderr[-2000:])
     rec = json.loads(r.stdout.strip().splitlines()[-1])
-    log(f"cpu oracle: {rec['value']:.0f} head-queries/s on {rec['cores']} processes")
+    log(f"cpu oracle ({config}): {rec['value']:.0f} head-queries/s on {rec['cores']} processes")
     return rec
 
 
@@ -638,7 +646,7 @@ def _cpu_worker(job):
 _CPU_STATE = {}
 
 
-def cpu_baseline_child(config, rb, seconds, workers) -> dict:
+def cpu_baseline_child(config, rb, seconds, workers, sequences=4) -> dict:
     """The CPU oracle, as it stands, decoding a bounded sample of the same
     workload (every query head of the first sequences at S tokens) on the
     host's cores: the sampled head-queries are split into one contiguous
@@ -652,7 +660,7 @@ def cpu_baseline_child(config, rb, seconds, workers) -> dict:
     import synth
     w = synth.WORKLOADS[config]
     S, k = w.S, w.k
-    nb = min(4, w.B)
+    nb = max(1, min(sequences, w.B))
     workers = workers if workers > 0 else min(16, os.cpu_count() or 1)
     Qs = synth.bases(w)
     P = np.stack([oracle.calibrate(synth.calib_keys(w, g, Qs[g]))[0]
