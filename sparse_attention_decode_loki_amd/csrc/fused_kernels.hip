@@ -41,12 +41,13 @@ struct FusedArgs {
   // gather 1/nsl of the row's kept tokens.  With nfull > 0 (the grid, nfull
   // and the sliced rows all multiples of 8) each XCD takes an eighth of the
   // whole rows, then an eighth of the sliced rows, so every CU gets the same
-  // mix.  Without coop every slice ranks
-  // and selects the whole row and leaves its [accumulator, max, sum] partial
-  // in part [rows][nsl][D + 2] for the combine launch.  With coop slice s
-  // ranks only its share of the tokens and the slices exchange the scores
-  // through xsc [rows][S]; each then selects the whole row and gathers its
-  // share, and the last slice merges the others' partials into out itself.
+  // mix.  Without coop every slice ranks and selects the whole row and
+  // leaves its [accumulator, max, sum] partial in part [rows][nsl][D + 2]
+  // for the combine launch.  With coop slice s ranks only its share of the
+  // tokens and the slices exchange the scores through xsc [rows][S]; each
+  // then selects the whole row and gathers its share, and the last slice
+  // merges the others' partials (part [sliced rows][nsl][D + 2]) into out
+  // itself.
   int nsl, nfull, coop;
   // grouped ranking (grp = Hq / Hkv > 1, one workgroup per row, rows in
   // (KV head, sequence, query head) order): the grp workgroups of one KV
@@ -57,8 +58,9 @@ struct FusedArgs {
   int grp;
   float* part;
   float* xsc;
-  // coop: [0] given-up waits, then kCoopStride words per sliced row: its
-  // epoch, then the flags of the slices' scores and of their partials
+  // coop or grouped: [0] given-up waits, then kCoopStride words per sliced
+  // row (per KV head unit when grouped): its epoch, then the flags of the
+  // members' scores and (coop) of their partials
   unsigned long long* sync;
 };
 
@@ -478,7 +480,7 @@ __global__ void __launch_bounds__(kFusedBlock, GRP > 1 ? 4 : 6) fused_kernel(Fus
   const bool merger = coop && slice == nsl - 1;
   merge_groups<E, D, 1, NT>(st, sc.mrg, [&](int, int dim, float M, float Ls, float A) {
     if (nsl == 1) {
-      a.out[row * D + dim] = A / Ls;
+      a.out[row * D + dim] = gave_up ? __builtin_nanf("") : A / Ls;
     } else if (merger) {
       mown[dim] = A;
       if (dim == 0) {
@@ -504,6 +506,8 @@ __global__ void __launch_bounds__(kFusedBlock, GRP > 1 ? 4 : 6) fused_kernel(Fus
       }
     }
   });
+  if (coop && gave_up && merger && threadIdx.x < D)
+    a.out[row * D + threadIdx.x] = __builtin_nanf("");
   if (coop && !gave_up) {
     if (!merger) {
       publish(rsync + 1 + kCoopMaxSlices + slice, ev);
