@@ -165,6 +165,20 @@ __global__ void __launch_bounds__(kFusedBlock, GRP > 1 ? 4 : 6) fused_kernel(Fus
   //    (cq, rb) adds rows [rb*RB, rb*RB + RB) for columns 4*cq .. 4*cq + 3,
   //    read as 16-byte chunks; the NRB partials are added through LDS.  The
   //    new value row is loaded together with the query.
+  // GROUP: the block's basis rows, loaded before the queries so that both
+  // arrive in one round trip (the rotation waits for the queries behind a
+  // barrier); the single-head kernel has no registers to hold them there
+  constexpr bool PEARLY = GROUP;
+  float4 pre[PEARLY ? RB : 1];
+  if constexpr (PEARLY) {
+    if (threadIdx.x < kBlock) {
+      const int cq = threadIdx.x % CQ, rb = threadIdx.x / CQ;
+      const float* Pg = a.P + static_cast<int64_t>(g) * D * D;
+#pragma unroll
+      for (int rr = 0; rr < RB; ++rr)
+        pre[rr] = *reinterpret_cast<const float4*>(Pg + (rb * RB + rr) * D + 4 * cq);
+    }
+  }
   T vn{};
   if (STEP && threadIdx.x < D) vn = static_cast<const T*>(a.v_new)[bgo * D + threadIdx.x];
   // the queries: this row's, or (GROUP) those of the KV head's GRP heads
@@ -210,19 +224,11 @@ __global__ void __launch_bounds__(kFusedBlock, GRP > 1 ? 4 : 6) fused_kernel(Fus
     for (int hh = 0; hh < GRP; ++hh) accg[hh] = make_float4(0.f, 0.f, 0.f, 0.f);
     const bool gcol = GROUP && 4 * cq < d;
     double kacc[4] = {0.0, 0.0, 0.0, 0.0};
-    // GROUP: the block's basis rows are all loaded before any product, so
-    // that the group's extra products do not hold back the loads
-    float4 pre[GROUP ? RB : 1];
-    if constexpr (GROUP) {
-#pragma unroll
-      for (int rr = 0; rr < RB; ++rr)
-        pre[rr] = *reinterpret_cast<const float4*>(Pg + (rb * RB + rr) * D + 4 * cq);
-    }
 #pragma unroll
     for (int rr = 0; rr < RB; ++rr) {
       const int m = rb * RB + rr;
-      const float4 p = GROUP ? pre[GROUP ? rr : 0]
-                             : *reinterpret_cast<const float4*>(Pg + m * D + 4 * cq);
+      const float4 p = PEARLY ? pre[PEARLY ? rr : 0]
+                              : *reinterpret_cast<const float4*>(Pg + m * D + 4 * cq);
       const float x = rin[jg][m];
       acc.x = fmaf(x, p.x, acc.x);
       acc.y = fmaf(x, p.y, acc.y);
