@@ -295,10 +295,10 @@ int sliced_slices(int B, int Hq, int D, int S_max, int kk, void* workspace, size
   return LOKI_OK;
 }
 
-// The grouped ranking of the single-kernel decode, where it is built (four
-// query heads per KV head, bf16, D = 128, d <= 64, S a multiple of 16) and a
-// large enough workspace is given; it changes no result (the same scores
-// reach every selection), only where they are computed.
+// The grouped ranking of the single-kernel decode and step, where it is
+// built (four query heads per KV head, bf16, D = 128, d <= 64, S a multiple
+// of 16) and a large enough workspace is given; it changes no result (the
+// same scores reach every selection), only where they are computed.
 void grouped_ranking(int B, int Hq, int Hkv, int D, int d, int S, int S_max, int dtype,
                      void* workspace, size_t ws_bytes, loki::FusedSlices& fs) {
   if (fs.nsl != 1 || Hq != loki::kGrpHeads * Hkv || dtype != LOKI_BF16 || D != 128 ||
@@ -399,6 +399,7 @@ int step_impl(const void* q, const void* k_new, const void* v_new, const float* 
       st = sliced_slices(B, Hq, D, S_max, kk, workspace, ws_bytes, fs);
       if (st != LOKI_OK) return st;
     }
+    grouped_ranking(B, Hq, Hkv, D, d, S, S_max, dtype, workspace, ws_bytes, fs);
     return status_of(loki::launch_fused_step(a, k_new, v_new, pos, kk, fs));
   }
   const Layout L = split_layout(B, Hq, Hkv, D, S, S_max, kk, uni);

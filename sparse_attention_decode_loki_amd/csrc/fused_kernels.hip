@@ -81,7 +81,6 @@ __global__ void __launch_bounds__(kFusedBlock, GRP > 1 ? 4 : 6) fused_kernel(Fus
   using T = typename E::T;
   constexpr int NT = kFusedBlock;
   constexpr bool GROUP = GRP > 1;
-  static_assert(!(GROUP && STEP), "the grouped ranking is built for decode");
   constexpr int GD = GROUP ? kGrpMaxD : 1;
   using Gm = Geo<E, D, NT>;
   constexpr int VEC = E::VEC;
@@ -157,9 +156,11 @@ __global__ void __launch_bounds__(kFusedBlock, GRP > 1 ? 4 : 6) fused_kernel(Fus
   // GROUP: the ranking stream is ALU-bound (four products per token), so its
   // first batch of slab loads, four per lane, is issued here, ahead of the
   // rotation, for the share this workgroup ranks
-  constexpr int US = GROUP ? 4 : 3;  // 16-byte slab loads in flight per lane
-  Chunk cg[GROUP ? US : 1];
-  if constexpr (GROUP) score_first<E, LPS, US, NT>(sl, d, jg * (S / GRP), (jg + 1) * (S / GRP), cg);
+  // (not for a step: its float64 key rotation needs those registers)
+  constexpr bool GEARLY = GROUP && !STEP;
+  constexpr int US = GEARLY ? 4 : 3;  // 16-byte slab loads in flight per lane
+  Chunk cg[GEARLY ? US : 1];
+  if constexpr (GEARLY) score_first<E, LPS, US, NT>(sl, d, jg * (S / GRP), (jg + 1) * (S / GRP), cg);
 
   // 1. q' = q . P[g] (and, for STEP, k' = k_new . P[g] in float64): thread
   //    (cq, rb) adds rows [rb*RB, rb*RB + RB) for columns 4*cq .. 4*cq + 3,
@@ -168,7 +169,7 @@ __global__ void __launch_bounds__(kFusedBlock, GRP > 1 ? 4 : 6) fused_kernel(Fus
   // GROUP: the block's basis rows, loaded before the queries so that both
   // arrive in one round trip (the rotation waits for the queries behind a
   // barrier); the single-head kernel has no registers to hold them there
-  constexpr bool PEARLY = GROUP;
+  constexpr bool PEARLY = GEARLY;
   float4 pre[PEARLY ? RB : 1];
   if constexpr (PEARLY) {
     if (threadIdx.x < kBlock) {
@@ -222,7 +223,7 @@ __global__ void __launch_bounds__(kFusedBlock, GRP > 1 ? 4 : 6) fused_kernel(Fus
     float4 accg[GRP];  // GROUP: every head of the group, ranking columns only
 #pragma unroll
     for (int hh = 0; hh < GRP; ++hh) accg[hh] = make_float4(0.f, 0.f, 0.f, 0.f);
-    const bool gcol = GROUP && 4 * cq < d;
+    const bool gcol = GROUP && !STEP && 4 * cq < d;  // (a step: in a pass of its own)
     double kacc[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
     for (int rr = 0; rr < RB; ++rr) {
@@ -264,6 +265,37 @@ __global__ void __launch_bounds__(kFusedBlock, GRP > 1 ? 4 : 6) fused_kernel(Fus
     }
   }
   __syncthreads();
+  if constexpr (GROUP && STEP) {
+    // the group's ranking columns in a pass of their own, so that their sums
+    // are not live beside the new key's float64 ones (the basis rows come
+    // again from cache)
+    if (threadIdx.x < kBlock) {
+      const int cq = threadIdx.x % CQ, rb = threadIdx.x / CQ;
+      if (4 * cq < d) {
+        const float* Pg = a.P + static_cast<int64_t>(g) * D * D;
+        float4 ag[GRP];
+#pragma unroll
+        for (int hh = 0; hh < GRP; ++hh) ag[hh] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int rr = 0; rr < RB; ++rr) {
+          const int m = rb * RB + rr;
+          const float4 p = *reinterpret_cast<const float4*>(Pg + m * D + 4 * cq);
+#pragma unroll
+          for (int hh = 0; hh < GRP; ++hh) {
+            const float xg = rin[hh][m];
+            ag[hh].x = fmaf(xg, p.x, ag[hh].x);
+            ag[hh].y = fmaf(xg, p.y, ag[hh].y);
+            ag[hh].z = fmaf(xg, p.z, ag[hh].z);
+            ag[hh].w = fmaf(xg, p.w, ag[hh].w);
+          }
+        }
+#pragma unroll
+        for (int hh = 0; hh < GRP; ++hh)
+          *reinterpret_cast<float4*>(&sc.rot.g[GROUP ? rb : 0][hh][GROUP ? 4 * cq : 0]) = ag[hh];
+      }
+    }
+    __syncthreads();
+  }
   if (GROUP && threadIdx.x >= NT - GRP * d) {
     // the group's ranking q', summed as the row's own columns are
     const int e = threadIdx.x - (NT - GRP * d), hh = e / d, col = e % d;
@@ -310,10 +342,11 @@ __global__ void __launch_bounds__(kFusedBlock, GRP > 1 ? 4 : 6) fused_kernel(Fus
     // pass's arithmetic, formed by every wave (each lane group ends with the
     // same sum), so the stream's value for that slot, read from the cache row
     // the launch has not written yet, is replaced without a barrier
+    // (GROUP: after the stream instead, below; the registers are short)
     float snew[NH];
 #pragma unroll
     for (int hh = 0; hh < NH; ++hh) snew[hh] = 0.f;
-    if (STEP) {
+    if (STEP && !GROUP) {
       float x[VEC];
       Chunk ch = (part * VEC < d) ? ld16(kslot + part * VEC) : zero_chunk();
       unpack<E>(ch, x);
@@ -325,15 +358,15 @@ __global__ void __launch_bounds__(kFusedBlock, GRP > 1 ? 4 : 6) fused_kernel(Fus
       }
     }
     Chunk c[US];
-    if constexpr (GROUP) {
+    if constexpr (GEARLY) {
 #pragma unroll
-      for (int u = 0; u < US; ++u) c[u] = cg[GROUP ? u : 0];
+      for (int u = 0; u < US; ++u) c[u] = cg[GEARLY ? u : 0];
     } else {
       score_first<E, LPS, US, NT>(sl, d, j0s, j1s, c);
     }
     // the selection's first radix digit is counted here, under the stream
     score_loop<E, LPS, NH, US, NT>(sl, d, j0s, j1s, qf, [&](int hh, int j, float s) {
-      if (STEP && j == a.pos) s = snew[hh];
+      if (STEP && !GROUP && j == a.pos) s = snew[hh];
       if (hh == jg) {
         sb[j] = s;
         if (SMALL) atomicAdd(&hist0[first_digit(order_key(s))], 1u);
@@ -343,6 +376,35 @@ __global__ void __launch_bounds__(kFusedBlock, GRP > 1 ? 4 : 6) fused_kernel(Fus
     }, c);
   }
   __syncthreads();
+  if constexpr (STEP && GROUP) {
+    // the appended token's scores, if it lies in this share: formed from its
+    // LDS row with the stream's arithmetic (one lane group per head) and put
+    // in place of what the stream read from its slot, the first-digit count
+    // moved with it
+    const int part = threadIdx.x % LPS, hh = threadIdx.x / LPS;
+    if (a.pos >= j0s && a.pos < j1s && hh < GRP) {
+      float x[VEC];
+      Chunk ch = (part * VEC < d) ? ld16(kslot + part * VEC) : zero_chunk();
+      unpack<E>(ch, x);
+      float sn = 0.f;
+#pragma unroll
+      for (int v = 0; v < VEC; ++v)
+        sn = fmaf((part * VEC < d) ? qg[hh][GROUP ? part * VEC + v : 0] : 0.f, x[v], sn);
+      sn = group_sum<LPS>(sn);
+      if (part == 0) {
+        if (hh == jg) {
+          if (SMALL) {
+            atomicSub(&hist0[first_digit(order_key(sb[a.pos]))], 1u);
+            atomicAdd(&hist0[first_digit(order_key(sn))], 1u);
+          }
+          sb[a.pos] = sn;
+        } else {
+          sb[hh * cs + (a.pos - j0s)] = sn;
+        }
+      }
+    }
+    __syncthreads();
+  }
 
   // GROUP: hand the other heads' scores of share jg to their workgroups and
   // take this row's other shares (device scope; flags carry the KV head's
@@ -584,11 +646,11 @@ void fused_g(const FusedArgs& fa, size_t lds, hipStream_t stream, int grid) {
                        dim3(kFusedBlock), lds, stream, fa);
 }
 
-// the grouped ranking is built for decode with four query heads per KV head
-// on bf16 caches of D = 128 (the host takes it only there)
+// the grouped ranking is built for four query heads per KV head on bf16
+// caches of D = 128 (the host takes it only there)
 template <class E, int D, int LPS, bool STEP>
 hipError_t fused_t(const FusedArgs& fa, size_t lds, hipStream_t stream, int grid) {
-  if constexpr (!STEP && std::is_same_v<E, BF16> && D == 128 && LPS * E::VEC <= kGrpMaxD) {
+  if constexpr (std::is_same_v<E, BF16> && D == 128 && LPS * E::VEC <= kGrpMaxD) {
     if (fa.grp == kGrpHeads) {
       fused_g<E, D, LPS, STEP, kGrpHeads>(fa, lds, stream, grid);
       return hipGetLastError();

@@ -82,7 +82,7 @@ size_t fused_lds_bytes(int D, int S, int kk);
 // are multiples of 8.
 constexpr int kCoopMaxSlices = 16;
 constexpr int kCoopStride = 1 + 2 * kCoopMaxSlices;
-// Grouped ranking on the single-kernel decode (one workgroup per row): the
+// Grouped ranking on the single-kernel decode and step (one workgroup per row): the
 // kGrpHeads query heads of a KV head share the ranking of its slab, each
 // scoring a quarter of the tokens for all four and exchanging the scores
 // through xsc and sync (as coop slices do).  For bf16 caches with D = 128,

@@ -628,6 +628,46 @@ def test_grouped_ranking_matches_oracle_and_the_single_head_pass(lib, name):
         check_decode(w.dtype, k, out, idx, ref_out, ref_idx, ref_s, all_pairs(w), src_of(c))
 
 
+def test_grouped_ranking_steps_match_the_single_head_step(lib):
+    """Decode steps (append + decode in one launch) with a workspace, so the
+    four query heads of a KV head share the ranking, from the same starting
+    cache as steps without one: identical selections, bit-identical outputs
+    and cache contents after each step, at lengths that take the grouped
+    ranking (a multiple of 16) and one that does not, and the first step's
+    decode against the oracle."""
+    import torch
+    w = synth.custom("grp_step", 124, B=2, Hq=8, Hkv=2, S=1023)
+    c = make_case(w, 1023, 1040)
+    caches = [device_cache(lib, c), device_cache(lib, c)]
+    P = to_dev(c.P, "f32")
+    ws = lib.alloc_workspace(w.B, w.Hq, c.S_max, w.D, 300, torch.device("cuda"))
+    for step in range(3):  # S = 1024, 1025, 1026
+        kn, vn = synth.new_tokens(w, 200 + step)
+        q = synth.queries(w, step=200 + step)
+        S = 1024 + step
+        k = w.k_at(S)
+        print(f"grouped step: S={S} k={k}", flush=True)
+        res = [lib.decode_step(to_dev(q, w.dtype), to_dev(kn[:, :, 0], w.dtype),
+                               to_dev(vn[:, :, 0], w.dtype), caches[i], P, k, path=1,
+                               workspace=wsi)
+               for i, wsi in ((0, ws), (1, None))]
+        torch.cuda.synchronize()
+        assert np.array_equal(res[0][1].cpu().numpy(), res[1][1].cpu().numpy()), S
+        assert np.array_equal(res[0][0].cpu().numpy().view(np.uint32),
+                              res[1][0].cpu().numpy().view(np.uint32)), S
+        for a, b in ((caches[0].k_slab, caches[1].k_slab), (caches[0].k_rest, caches[1].k_rest),
+                     (caches[0].v, caches[1].v)):
+            assert torch.equal(a, b), S
+        if step == 0:
+            full = {nm: to_host(t, w.dtype)[:, :, :S] for nm, t in
+                    (("slab", caches[0].k_slab), ("rest", caches[0].k_rest), ("v", caches[0].v))}
+            ref_out, ref_idx, ref_s = oracle.decode(q, full["slab"], full["rest"], full["v"], c.P,
+                                                    k, w.dtype, S=S)
+            check_decode(w.dtype, k, res[0][0].cpu().numpy(), res[0][1].cpu().numpy(), ref_out,
+                         ref_idx, ref_s, all_pairs(w),
+                         OracleSrc(q, full["slab"], full["rest"], full["v"], c.P))
+
+
 def test_per_layer_slab_width(lib):
     """Per-layer d (the pages' ablation over d): one cache per layer, each
     with its own slab width, decoded one after another with the same query
