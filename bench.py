@@ -519,8 +519,13 @@ def measure_config(loki, torch, name, dev, steps, warmup, log) -> dict:
     shape supports, for one workload at its full size, timed as the
     headline's decode: back-to-back launches between two HIP events after
     untimed warmup launches (and 500 settle launches before the first),
-    cache copies cycled so that no launch finds its bytes cached."""
+    cache copies cycled so that no launch finds its bytes cached.  At least
+    200 launches are timed per path: the events open while the GPU is idle,
+    so the host's latency to the first launch (tens of microseconds) is
+    inside the span, and over 20 launches of a 20 us kernel it would add
+    about a quarter to each."""
     import synth
+    steps = max(steps, 200)
     w = synth.WORKLOADS[name]
     S, k = w.S, w.k
     Qs = synth.bases(w)
@@ -582,7 +587,7 @@ def measure_config(loki, torch, name, dev, steps, warmup, log) -> dict:
            "frac": by["total"] / (dec_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
            "path_design_bytes": moved,
            "path_design_GBs": moved / (dec_ms * 1e-3) / 1e9,
-           "layers_cycled": L}
+           "layers_cycled": L, "launches_timed": steps}
     # the other paths this shape supports, on the same caches
     for other in ("fused", "sliced", "split", "union"):
         if other == path:
