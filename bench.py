@@ -18,6 +18,7 @@ bounded sample.
 from __future__ import annotations
 
 import argparse
+import csv
 import hashlib
 import json
 import os
@@ -61,6 +62,64 @@ def algorithmic_bytes(w, S, k) -> dict:
     rows = w.B * w.Hq * k * 2 * w.D * e
     dense = w.B * w.Hkv * S * 2 * w.D * e
     return {"slab": slab, "rows": rows, "total": slab + rows, "dense": dense}
+
+
+def live_traffic(args, log):
+    """HBM bytes per launch of the fused step kernel, measured now: two child
+    runs of this script's step (20 + 5 launches, no other measurement) under
+    rocprofv3, one counter each (FETCH_SIZE, then WRITE_SIZE, KiB per
+    dispatch), each scaled by what the same counter reads for a plain 1 GiB
+    device copy in the same child.  Returns (bytes, detail) or (None, reason).
+    The children start after every timed measurement of this process."""
+    import glob
+    import shutil
+    import signal
+    import subprocess
+    import tempfile
+    prof = shutil.which("rocprofv3")
+    if prof is None:
+        return None, "rocprofv3 not found"
+    base = [sys.executable, os.path.abspath(__file__), "--config", args.config,
+            "--no-per-config", "--no-cpu", "--no-jaccard", "--no-run", "--no-dense",
+            "--no-read-probe", "--no-live-traffic", "--steps", "20", "--warmup", "5",
+            "--settle", "0", "--copy-probe-mib", "1024"]
+    if args.rope_base is not None:
+        base += ["--rope-base", str(args.rope_base)]
+    env = dict(os.environ, TMPDIR="/tmp")
+    per = {}
+    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+        out = tempfile.mkdtemp(prefix="loki_pmc_", dir="/tmp")
+        cmd = [prof, "--pmc", counter, "-f", "csv", "-d", out, "-o", "p", "--"] + base
+        log(f"counter run: {counter}")
+        p = subprocess.Popen(cmd, stdout=subprocess.DEVNULL, stderr=subprocess.DEVNULL, env=env,
+                             start_new_session=True)
+        try:
+            p.wait(timeout=240)
+        except subprocess.TimeoutExpired:
+            os.killpg(p.pid, signal.SIGKILL)
+            p.wait()
+            return None, f"{counter} run timed out"
+        # (the profiler can exit non-zero after the program ended with its
+        # results complete; the files decide)
+        vals = {}
+        for f in glob.glob(os.path.join(out, "**", "*counter_collection.csv"), recursive=True):
+            with open(f) as fh:
+                for r in csv.DictReader(fh):
+                    if r.get("Counter_Name") == counter:
+                        vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        shutil.rmtree(out, ignore_errors=True)
+        copy = [max(v) for k, v in vals.items() if "copyBuffer" in k]
+        step = [v for k, v in vals.items()
+                if re.search(r"fused_kernel<[^>]*, (true|false), true, \d+>", k)]
+        if not copy or len(step) != 1:
+            return None, f"{counter}: no copy or step dispatches in the counter output"
+        scale = 1048576.0 / max(copy)
+        per[counter] = (float(np.median(step[0])) * 1024.0 * scale, scale, len(step[0]))
+    total = per["FETCH_SIZE"][0] + per["WRITE_SIZE"][0]
+    detail = {"fetch_bytes": per["FETCH_SIZE"][0], "write_bytes": per["WRITE_SIZE"][0],
+              "fetch_scale": per["FETCH_SIZE"][1], "write_scale": per["WRITE_SIZE"][1],
+              "dispatches": per["FETCH_SIZE"][2]}
+    return total, detail
 
 
 def measured_traffic(kernel_hash: str, workload: str):
@@ -155,6 +214,9 @@ def main():
                     help="RoPE variant: keys embedded at their positions, the query at S-1")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="first run a plain device copy of this size (counter calibration)")
+    ap.add_argument("--no-live-traffic", action="store_true",
+                    help="skip the two rocprofv3 counter runs (FETCH_SIZE, WRITE_SIZE) of the "
+                         "step that give roofline.traffic for this run")
     ap.add_argument("--no-per-config", action="store_true",
                     help="skip the decode measurements of the other workloads")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -307,8 +369,9 @@ def main():
     path_name = PATH_NAMES[
         loki.decode_path(w.B, w.Hq, w.Hkv, w.D, w.d, S, k, w.dtype, args.path)]
     overridden = args.kf is not None or args.df is not None
-    traffic = (measured_traffic(khash, args.config)
-               if "fused" in path_name and not overridden else None)
+    traffic_recorded = (measured_traffic(khash, args.config)
+                        if "fused" in path_name and not overridden else None)
+    traffic = traffic_recorded
 
     result = {
         "metric": METRIC,
@@ -338,6 +401,7 @@ def main():
                          "recorded, not measured in this run: rocprofv3 --pmc FETCH_SIZE and "
                          f"WRITE_SIZE in profiles/traffic_fused_decode_step_{args.config}.txt, "
                          "taken on this kernel source hash" if traffic is not None else None),
+                     "traffic_recorded": traffic_recorded,
                      "kernel": ("fused decode step (append + decode, one launch)" if "fused" in path_name
                                 else "decode step (split kernels)"),
                      "algorithmic_bytes_per_launch": step_bytes,
@@ -459,6 +523,25 @@ def main():
                                sequences=1)
             res["cpu_oracle"] = {k_: rec[k_] for k_ in ("value", "unit", "cores", "sample")}
             res["gpu_over_cpu_oracle"] = res["head_queries_per_s"] / rec["value"]
+
+    # ---- HBM traffic of the step kernel, measured in this run (after every
+    # timed measurement): the counters' bytes per launch replace the recorded
+    # figure in roofline.traffic
+    if not args.no_live_traffic and "fused" in path_name and not overridden:
+        tb, det = live_traffic(args, log)
+        if tb is not None:
+            result["roofline"]["traffic"] = tb
+            result["roofline"]["traffic_source"] = (
+                "measured in this run: two child runs of the step (20 + 5 launches) under "
+                "rocprofv3 --pmc, FETCH_SIZE then WRITE_SIZE (KiB per dispatch, median over the "
+                "step kernel's dispatches), each scaled by the same counter's reading for a "
+                "plain 1 GiB device copy in that child")
+            result["roofline"]["traffic_detail"] = det
+            log(f"HBM traffic per step launch: {tb / 1e6:.1f} MB (recorded: "
+                f"{(traffic_recorded or 0) / 1e6:.1f} MB)")
+        else:
+            result["roofline"]["traffic_live_error"] = det
+            log(f"live traffic not measured: {det}")
 
     print(json.dumps(result), flush=True)
 
