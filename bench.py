@@ -154,7 +154,10 @@ def timed(torch, fn, n):
     return (t1 - t0) * 1e3 / n, e0.elapsed_time(e1) / n
 
 
-def timed_queued(torch, fn, n, state={}):
+_QUEUE = {}  # the spin kernel's ms per cycle and the host's last submission time
+
+
+def timed_queued(torch, fn, n):
     """Per-launch GPU time of fn(i), i < n, launched back to back: the
     launches are queued behind a GPU-side delay (torch's spin kernel) that
     outlasts their host-side submission, so the two events around them see
@@ -162,6 +165,7 @@ def timed_queued(torch, fn, n, state={}):
     (event ms per call, host submission us per call, queue_kept): the last is
     False if the host took longer to submit than the delay and the launches
     lasted (the figure then includes gaps)."""
+    state = _QUEUE
     if "ms_per_cycle" not in state:
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
