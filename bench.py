@@ -94,7 +94,7 @@ def live_traffic(args, log):
         p = subprocess.Popen(cmd, stdout=subprocess.DEVNULL, stderr=subprocess.DEVNULL, env=env,
                              start_new_session=True)
         try:
-            p.wait(timeout=240)
+            p.wait(timeout=120)
         except subprocess.TimeoutExpired:
             os.killpg(p.pid, signal.SIGKILL)
             p.wait()
