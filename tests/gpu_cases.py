@@ -186,5 +186,22 @@ def ulp_diff_f32(a: np.ndarray, b: np.ndarray) -> np.ndarray:
     return np.abs(ordered(np.ascontiguousarray(a)) - ordered(np.ascontiguousarray(b)))
 
 
+def check_rounded_rotation(got, want, x, mag, dtype):
+    """got (the library's) and want (the oracle's) are storage-dtype roundings
+    of the same rotated values, whose exact float64 sums are x, each a sum of
+    terms whose magnitudes add up to mag.  Both sides sum in float64 in
+    different orders, so they may round to neighbouring values where x lies
+    within float64 summation error (here 64 units of 2^-53 times mag) of the
+    boundary between them; everywhere else they must be equal."""
+    ud = ulp_diff_bf16(got, want) if dtype == "bf16" else ulp_diff_f32(got, want)
+    assert ud.max() <= 1, f"{int(ud.max())} units apart"
+    off = ud == 1
+    if off.any():
+        mid = (oracle.to_f64(got[off], dtype) + oracle.to_f64(want[off], dtype)) / 2.0
+        slack = np.abs(x[off] - mid) / mag[off]
+        assert np.all(slack <= 64 * 2.0 ** -53), f"a neighbour {slack.max():.3g} (of the terms) away"
+    return int(off.sum())
+
+
 def scale(D):
     return 1.0 / math.sqrt(D)
