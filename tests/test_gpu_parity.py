@@ -386,19 +386,21 @@ def test_append_matches_oracle(lib, w, pos, T):
     torch.cuda.synchronize()
     slab = to_host(cache.k_slab, w.dtype)[:, :, pos:pos + T]
     vv = to_host(cache.v, w.dtype)[:, :, pos:pos + T]
+    off = n = 0
     for g in range(w.Hkv):
-        rs, rr, rv = oracle.append(oracle.to_f64(K[:, g], w.dtype), oracle.to_f64(V[:, g], w.dtype),
+        kg = oracle.to_f64(K[:, g], w.dtype)
+        rs, rr, rv = oracle.append(kg, oracle.to_f64(V[:, g], w.dtype),
                                    P[g].astype(np.float64), w.d, w.dtype)
-        got = [slab[:, g]]
-        want = [rs]
+        x = kg @ P[g].astype(np.float64)
+        mag = np.abs(kg) @ np.abs(P[g].astype(np.float64))
+        off += check_rounded_rotation(slab[:, g], rs, x[..., :w.d], mag[..., :w.d], w.dtype)
+        n += rs.size
         if w.d < w.D:
-            got.append(to_host(cache.k_rest, w.dtype)[:, g, pos:pos + T])
-            want.append(rr)
-        for a, e in zip(got, want):
-            ud = ulp_diff_bf16(a, e) if w.dtype == "bf16" else ulp_diff_f32(a, e)
-            assert ud.max() <= 1
-            assert (ud == 0).mean() >= 0.999
+            off += check_rounded_rotation(to_host(cache.k_rest, w.dtype)[:, g, pos:pos + T], rr,
+                                          x[..., w.d:], mag[..., w.d:], w.dtype)
+            n += rr.size
         assert np.array_equal(vv[:, g], rv)
+    assert off <= max(1, n // 1000)  # neighbours at rounding boundaries are rare
     # untouched slots stay zero
     full = to_host(cache.v, w.dtype)
     assert not np.any(full[:, :, :pos]) and not np.any(full[:, :, pos + T:])
