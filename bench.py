@@ -157,6 +157,19 @@ def timed(torch, fn, n):
 _QUEUE = {}  # the spin kernel's ms per cycle and the host's last submission time
 
 
+# (bytes, workgroups, threads, loads in flight per lane, which launch it mirrors)
+FLOOR_SHAPES = [
+    (440_401_920, 640, 512, 4, "13B step: one 512-thread workgroup per row"),
+    (440_401_920, 640, 512, 8, "13B step grid, deeper loads"),
+    (440_401_920, 2048, 256, 4, "13B step bytes, many workgroups"),
+    (33_554_432, 256, 512, 4, "Llama3-8B grouped ranking: one workgroup per CU"),
+    (33_554_432, 256, 512, 16, "Llama3-8B grouped ranking, deeper loads"),
+    (134_217_728, 1024, 256, 4, "Mistral ranking pass grid"),
+    (268_435_456, 2048, 256, 4, "Llama3-8B dense bytes"),
+    (536_870_912, 2048, 256, 4, "Mistral dense bytes"),
+]
+
+
 def timed_queued(torch, fn, n):
     """Per-launch GPU time of fn(i), i < n, launched back to back: the
     launches are queued behind a GPU-side delay (torch's spin kernel) that
@@ -428,10 +441,33 @@ def main():
                 loki.stream_read(buf, sink, wg)
             _, rms = timed_(lambda i: loki.stream_read(buf, sink, wg), 10)
             best = max(best, buf.numel() / (rms * 1e-3) / 1e9)
-        del buf
         result["roofline"]["measured_stream_read_GBs"] = best
         result["roofline"]["frac_of_measured_stream_read"] = achieved / best
         log(f"streaming-read probe {best:.0f} GB/s; step at {achieved / best:.3f} of it")
+        # floors of the launch shapes the decode kernels use: each workgroup
+        # streams its own contiguous share, regions of the 4 GiB buffer cycled
+        floors = []
+        for nbytes, wg, nt, loads, what in FLOOR_SHAPES:
+            nbytes -= nbytes % (16 * wg)
+            regions = buf.numel() // nbytes
+            views = [buf[r * nbytes:(r + 1) * nbytes] for r in range(regions)]
+            sink = torch.empty(wg * nt, dtype=torch.float32, device=dev)
+            for i in range(3):
+                loki.stream_read_shares(views[i % regions], sink, wg, nt, loads)
+            ms, _, _ = timed_queued(
+                torch, lambda i: loki.stream_read_shares(views[i % regions], sink, wg, nt, loads), 40)
+            floors.append({"bytes": nbytes, "workgroups": wg, "threads": nt, "loads_per_lane": loads,
+                           "us": ms * 1e3, "GBs": nbytes / (ms * 1e-3) / 1e9, "shape_of": what})
+            log(f"share-read floor: {nbytes / 1e6:.1f} MB, {wg} x {nt} threads, {loads} loads/lane: "
+                f"{ms * 1e3:.2f} us ({what})")
+        result["streaming_floors"] = floors
+        if w.name == "l2_13b_run" and "fused" in path_name and not overridden:
+            # the step against a plain stream of its bytes by its own grid
+            same = min(f["us"] for f in floors if f["workgroups"] == 640 and f["threads"] == 512)
+            result["roofline"]["same_grid_stream_us"] = same
+            result["roofline"]["frac_of_same_grid_stream"] = same / (step_avg_ms * 1e3)
+            log(f"step at {same / (step_avg_ms * 1e3):.3f} of a plain stream of its bytes by its grid")
+        del buf
 
     # ---- grouped-query shapes: the other gather (union / per-head) on the
     # same caches

@@ -315,6 +315,18 @@ int loki_decode_noalloc(const void* q, const void* k_slab, const void* k_rest, c
  * published peak.  1 <= workgroups <= 65536. */
 int loki_stream_read(const void* buf, size_t bytes, float* sink, int32_t workgroups, void* stream);
 
+/* Measurement helper, not part of the method: the read pattern of a kernel
+ * that gives each workgroup one row.  Each of `workgroups` workgroups of
+ * `threads` threads (256, 512 or 1024) reads its own contiguous share of
+ * bytes / workgroups bytes at buf with nontemporal 16-byte loads, `loads`
+ * (1, 2, 4, 8 or 16) in flight per lane, and writes one float per thread (the
+ * sum of what it read) to sink (device, workgroups * threads floats).  Timing
+ * it at a decode launch's grid and bytes gives the floor a plain stream of
+ * that shape reaches.  buf 16-byte aligned; bytes a multiple of
+ * 16 * workgroups; 1 <= workgroups <= 65536; otherwise LOKI_EINVAL. */
+int loki_stream_read_shares(const void* buf, size_t bytes, float* sink, int32_t workgroups,
+                            int32_t threads, int32_t loads, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

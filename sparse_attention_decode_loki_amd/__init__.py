@@ -45,6 +45,7 @@ _SIGS = {
     "loki_dense_decode": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P,
                                          _P, ctypes.c_size_t, _P]),
     "loki_stream_read": (ctypes.c_int, [_P, ctypes.c_size_t, _P, _I, _P]),
+    "loki_stream_read_shares": (ctypes.c_int, [_P, ctypes.c_size_t, _P, _I, _I, _I, _P]),
     "loki_decode_noalloc": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I,
                                            _P, _P, _I, _P]),
     "loki_kv_append_rope": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I,
@@ -482,6 +483,23 @@ def stream_read(buf, sink, workgroups: int):
     st = load().loki_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
                                  workgroups, _stream(buf))
     _check(st, "loki_stream_read")
+
+
+def stream_read_shares(buf, sink, workgroups: int, threads: int = 256, loads: int = 4):
+    """Measurement helper: each of `workgroups` workgroups of `threads`
+    threads reads its own contiguous share of `buf` (a contiguous device
+    tensor whose byte size is a multiple of 16 * workgroups) with `loads`
+    16-byte loads in flight per lane; `sink` is a float32 device tensor of at
+    least workgroups * threads entries."""
+    torch = _torch()
+    _need(buf, "buf")
+    _need(sink, "sink", torch.float32, device=buf.device)
+    _on_gpu(buf, "buf")
+    if sink.numel() < workgroups * threads:
+        raise ValueError("sink needs workgroups * threads floats")
+    st = load().loki_stream_read_shares(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
+                                        workgroups, threads, loads, _stream(buf))
+    _check(st, "loki_stream_read_shares")
 
 
 # ------------------------------------------------- pre-marshalled calls --

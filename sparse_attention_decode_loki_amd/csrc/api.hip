@@ -671,4 +671,17 @@ int loki_stream_read(const void* buf, size_t bytes, float* sink, int32_t workgro
                                             static_cast<hipStream_t>(stream)));
 }
 
+int loki_stream_read_shares(const void* buf, size_t bytes, float* sink, int32_t workgroups,
+                            int32_t threads, int32_t loads, void* stream) {
+  if (workgroups < 1 || workgroups > 65536) return LOKI_EINVAL;
+  if (threads != 256 && threads != 512 && threads != 1024) return LOKI_EINVAL;
+  if (loads != 1 && loads != 2 && loads != 4 && loads != 8 && loads != 16) return LOKI_EINVAL;
+  if (bytes % (16ull * static_cast<size_t>(workgroups)) != 0) return LOKI_EINVAL;
+  if (bytes == 0) return LOKI_OK;
+  if (!buf || !sink || !aligned16(buf) || (reinterpret_cast<uintptr_t>(sink) & 3u))
+    return LOKI_EINVAL;
+  return status_of(loki::launch_share_read(buf, bytes, sink, workgroups, threads, loads,
+                                           static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

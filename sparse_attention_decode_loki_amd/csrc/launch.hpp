@@ -118,4 +118,11 @@ hipError_t launch_append(const void* k_new, const void* v_new, const float* P, v
 hipError_t launch_stream_read(const void* buf, size_t bytes, float* sink, int workgroups,
                               hipStream_t stream);
 
+// each of `workgroups` workgroups of `threads` threads (256, 512 or 1024)
+// reads its own contiguous share, bytes / workgroups (a multiple of 16),
+// with `loads` (1, 2, 4, 8 or 16) 16-byte loads in flight per lane; sink
+// receives workgroups * threads floats
+hipError_t launch_share_read(const void* buf, size_t bytes, float* sink, int workgroups,
+                             int threads, int loads, hipStream_t stream);
+
 }  // namespace loki

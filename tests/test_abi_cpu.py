@@ -283,6 +283,19 @@ def test_stream_read_rejects_bad_arguments(L):
     assert lib.loki_stream_read(FAKE, 0, FAKE, 4, None) == 0
 
 
+def test_stream_read_shares_rejects_bad_arguments(L):
+    lib = L.load()
+    f = lib.loki_stream_read_shares
+    assert f(FAKE, 4096, FAKE, 0, 256, 4, None) == -1       # no workgroups
+    assert f(FAKE, 4096, FAKE, 65537, 256, 4, None) == -1
+    assert f(FAKE, 4096, FAKE, 4, 128, 4, None) == -1       # block size
+    assert f(FAKE, 4096, FAKE, 4, 256, 3, None) == -1       # loads in flight
+    assert f(FAKE, 4096, FAKE, 3, 256, 4, None) == -1       # shares not whole chunks
+    assert f(None, 4096, FAKE, 4, 256, 4, None) == -1
+    assert f(FAKE_MIS, 4096, FAKE, 4, 256, 4, None) == -1
+    assert f(FAKE, 0, FAKE, 4, 1024, 16, None) == 0
+
+
 def test_decode_noalloc_rejects_before_touching_a_device(L):
     lib = L.load()
     a = [FAKE, FAKE, FAKE, FAKE, FAKE, 2, 4, 2, 128, 32, 100, 128, 25, 1, FAKE, FAKE, 2, None]

@@ -654,6 +654,21 @@ def test_stream_read_probe_reads_every_element(lib):
         assert got == float((torch.arange(n, dtype=torch.float64) % 7).sum())
 
 
+@pytest.mark.parametrize("threads,loads", [(256, 1), (512, 4), (1024, 16), (256, 8)])
+def test_share_read_probe_reads_every_element(lib, threads, loads):
+    """Each workgroup of the per-share probe reads exactly its share: the
+    per-thread sums add up to the sum of the buffer, also when a share is not
+    a multiple of the workgroup's loads."""
+    import torch
+    for wg in (1, 5, 256):
+        n = wg * 4 * (3 * threads * loads + 7)  # float32 elements: ragged shares
+        buf = (torch.arange(n, dtype=torch.int64, device="cuda") % 7).to(torch.float32)
+        sink = torch.full((wg * threads,), float("nan"), dtype=torch.float32, device="cuda")
+        lib.stream_read_shares(buf, sink, wg, threads, loads)
+        got = sink.double().sum().item()
+        assert got == float((n // 7) * 21 + sum(range(n % 7))), (wg, threads, loads)
+
+
 @pytest.mark.parametrize("path", [1, 2, 3, 4], ids=["fused", "split", "union", "sliced"])
 def test_split_paths_ignore_stale_workspace(lib, path):
     """The split and union paths read nothing from the workspace that the same
