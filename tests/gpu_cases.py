@@ -186,6 +186,27 @@ def ulp_diff_f32(a: np.ndarray, b: np.ndarray) -> np.ndarray:
     return np.abs(ordered(np.ascontiguousarray(a)) - ordered(np.ascontiguousarray(b)))
 
 
+def random_workload(i):
+    """A seeded random shape: dtype, head dim, slab width, query heads per KV
+    head (1, 2, 4 or 8), batch, length (log-uniform up to 20000, ragged
+    capacity), budget (sometimes past S) and key spectrum, with or without
+    sink tokens."""
+    r = np.random.default_rng(91000 + i)
+    dtype = "bf16" if r.random() < 0.7 else "f32"
+    D = 128 if r.random() < 0.7 else 64
+    unit = 8 if dtype == "bf16" else 4
+    d = int(r.choice([x for x in (4, 8, 16, 24, 32, 48, 64, 128) if x % unit == 0 and x <= D]))
+    G = int(r.choice([1, 2, 4, 8]))
+    Hkv = int(r.integers(1, 4))
+    B = int(r.integers(1, 4))
+    S = max(1, int(np.exp(r.uniform(0.0, np.log(20000.0)))))
+    k_f = float(r.choice([0.01, 0.1, 0.25, 0.5, 0.9, 1.5]))
+    w = synth.custom(f"random_{i}", 950 + i, B=B, Hq=G * Hkv, Hkv=Hkv, D=D, d=d, S=S, k_f=k_f,
+                     dtype=dtype, tau=float(r.choice([8.0, 24.0, 48.0])),
+                     sinks=min(S, 4) if r.random() < 0.3 else 0)
+    return w, S, S + int(r.integers(0, 40))
+
+
 def check_rounded_rotation(got, want, x, mag, dtype):
     """got (the library's) and want (the oracle's) are storage-dtype roundings
     of the same rotated values, whose exact float64 sums are x, each a sum of

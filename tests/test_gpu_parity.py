@@ -13,8 +13,8 @@ import pytest
 import oracle
 import synth
 from gpu_cases import (TOL, OracleSrc, all_pairs, check_decode, check_rounded_rotation,
-                       device_cache, make_case, out_error, src_of, to_dev, to_host, ulp_diff_bf16,
-                       ulp_diff_f32)
+                       device_cache, make_case, out_error, random_workload, src_of, to_dev,
+                       to_host, ulp_diff_bf16, ulp_diff_f32)
 
 pytestmark = pytest.mark.gpu
 
@@ -275,31 +275,10 @@ def test_decode_matches_oracle(lib, name, path):
     check_decode(c.w.dtype, c.k, out, idx, ref_out, ref_idx, ref_s, all_pairs(c.w), src_of(c))
 
 
-def _random_decode_workload(i):
-    """A seeded random shape: dtype, head dim, slab width, query heads per KV
-    head (1, 2, 4 or 8), batch, length (log-uniform up to 20000, ragged
-    capacity), budget (sometimes past S) and key spectrum, with or without
-    sink tokens."""
-    r = np.random.default_rng(91000 + i)
-    dtype = "bf16" if r.random() < 0.7 else "f32"
-    D = 128 if r.random() < 0.7 else 64
-    unit = 8 if dtype == "bf16" else 4
-    d = int(r.choice([x for x in (4, 8, 16, 24, 32, 48, 64, 128) if x % unit == 0 and x <= D]))
-    G = int(r.choice([1, 2, 4, 8]))
-    Hkv = int(r.integers(1, 4))
-    B = int(r.integers(1, 4))
-    S = max(1, int(np.exp(r.uniform(0.0, np.log(20000.0)))))
-    k_f = float(r.choice([0.01, 0.1, 0.25, 0.5, 0.9, 1.5]))
-    w = synth.custom(f"random_{i}", 950 + i, B=B, Hq=G * Hkv, Hkv=Hkv, D=D, d=d, S=S, k_f=k_f,
-                     dtype=dtype, tau=float(r.choice([8.0, 24.0, 48.0])),
-                     sinks=min(S, 4) if r.random() < 0.3 else 0)
-    return w, S, S + int(r.integers(0, 40))
-
-
 @pytest.mark.parametrize("i", range(24))
 def test_decode_random_family(lib, i):
     # every path the library takes for the shape (AUTO included) against the oracle
-    w, S, S_max = _random_decode_workload(i)
+    w, S, S_max = random_workload(i)
     c = make_case(w, S, S_max)
     k = max(1, min(int(w.k_f * S), S + 3))
     print(f"random decode case {i}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} D={w.D} d={w.d} S={S} "
@@ -524,7 +503,7 @@ def test_decode_step_matches_oracle(lib, name, path):
 @pytest.mark.parametrize("i", range(12))
 def test_decode_step_random_family(lib, i):
     # the random decode shapes as one generation step, on every applicable path
-    w, _, _ = _random_decode_workload(100 + i)
+    w, _, _ = random_workload(100 + i)
     print(f"random step case {i}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} D={w.D} d={w.d} S={w.S} "
           f"k={w.k_at(w.S)} {w.dtype} sinks={w.sinks}", flush=True)
     ran = 0

@@ -10,7 +10,8 @@ import pytest
 import oracle
 import synth
 from gpu_cases import (TOL, OracleSrc, all_pairs, basis, check_decode, device_cache, make_case,
-                       out_error, src_of, to_dev, to_host, ulp_diff_bf16, ulp_diff_f32)
+                       out_error, random_workload, src_of, to_dev, to_host, ulp_diff_bf16,
+                       ulp_diff_f32)
 
 pytestmark = pytest.mark.gpu
 
@@ -56,6 +57,33 @@ def test_rope_decode_matches_oracle(lib, name):
             out, idx = lib.decode(q, cache, P, c.k, path=path, rope_base=base, q_pos=q_pos)
             check_decode(c.w.dtype, c.k, out.cpu().numpy(), idx.cpu().numpy(), ref_out, ref_idx,
                          ref_s, all_pairs(c.w), src_of(c, (base, q_pos)))
+
+
+@pytest.mark.parametrize("i", range(8))
+def test_rope_decode_random_family(lib, i):
+    # random shapes with embedded keys, the query at the last position, on AUTO
+    # and every path that applies
+    w, S, S_max = random_workload(200 + i)
+    base = (10000.0, 500000.0)[i % 2]
+    c = make_case(w, S, S_max, rope_base=base)
+    k = max(1, min(int(w.k_f * S), S + 3))
+    print(f"random rope case {i}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} D={w.D} d={w.d} S={S} k={k} "
+          f"{w.dtype} base={base}", flush=True)
+    cache = device_cache(lib, c)
+    q, P = to_dev(c.q, w.dtype), to_dev(c.P, "f32")
+    ref_out, ref_idx, ref_s = oracle.decode(c.q, c.slab, c.rest, c.v, c.P, k, w.dtype, S=S,
+                                            rope=(base, S - 1))
+    ran = 0
+    for path in (0, 1, 2, 3, 4):
+        try:
+            lib.decode_path(w.B, w.Hq, w.Hkv, w.D, w.d, S, k, w.dtype, path)
+        except lib.LokiError:
+            continue
+        out, idx = lib.decode(q, cache, P, k, path=path, rope_base=base)
+        check_decode(w.dtype, k, out.cpu().numpy(), idx.cpu().numpy(), ref_out, ref_idx, ref_s,
+                     all_pairs(w), src_of(c, (base, S - 1)))
+        ran += 1
+    assert ran >= 2
 
 
 @pytest.mark.parametrize("name", sorted(CASES))
