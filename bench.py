@@ -154,7 +154,7 @@ def timed(torch, fn, n):
     return (t1 - t0) * 1e3 / n, e0.elapsed_time(e1) / n
 
 
-_QUEUE = {}  # the spin kernel's ms per cycle and the host's last submission time
+_QUEUE = {}  # the delay reads' buffer and time, and the host's last submission time
 
 
 # (bytes, workgroups, threads, loads in flight per lane, which launch it mirrors)
@@ -172,27 +172,35 @@ FLOOR_SHAPES = [
 
 def timed_queued(torch, fn, n):
     """Per-launch GPU time of fn(i), i < n, launched back to back: the
-    launches are queued behind a GPU-side delay (torch's spin kernel) that
-    outlasts their host-side submission, so the two events around them see
-    the kernels run back to back and not the host's launch rate.  Returns
+    launches are queued behind a GPU-side delay that outlasts their host-side
+    submission, so the two events around them see the kernels run back to
+    back and not the host's launch rate.  The delay is a run of the library's
+    streaming reads over 1 GiB, which keep every CU and the HBM busy (a spin
+    kernel on one CU let the clocks drop before short kernels).  Returns
     (event ms per call, host submission us per call, queue_kept): the last is
     False if the host took longer to submit than the delay and the launches
     lasted (the figure then includes gaps)."""
+    import sparse_attention_decode_loki_amd as loki
     state = _QUEUE
-    if "ms_per_cycle" not in state:
+    if "buf" not in state:
+        state["buf"] = torch.zeros(1 << 30, dtype=torch.uint8, device="cuda")
+        state["sink"] = torch.empty(2048 * 256, dtype=torch.float32, device="cuda")
+        for _ in range(3):
+            loki.stream_read(state["buf"], state["sink"], 2048)
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
         a.record()
-        torch.cuda._sleep(1 << 22)
+        for _ in range(10):
+            loki.stream_read(state["buf"], state["sink"], 2048)
         b.record()
         torch.cuda.synchronize()
-        state["ms_per_cycle"] = max(a.elapsed_time(b), 1e-3) / (1 << 22)
+        state["read_ms"] = max(a.elapsed_time(b) / 10, 1e-3)
         state["host_us"] = 100.0
     # room for the host to submit every launch at its last measured rate, x3
     delay_ms = max(2.0, 3.0 * n * state["host_us"] * 1e-3)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    torch.cuda._sleep(int(delay_ms / state["ms_per_cycle"]))
+    for _ in range(int(delay_ms / state["read_ms"]) + 1):
+        loki.stream_read(state["buf"], state["sink"], 2048)
     e0.record()
     t0 = time.perf_counter()
     for i in range(n):
